@@ -1,0 +1,356 @@
+"""CPU oracle of the single-GPU MoE-layer forward pass.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check in
+``__graft_entry__`` and the benchmark's CPU-baseline leg may import or run
+this module.  The product library never imports, links or calls it, and it
+shares no code with the HIP path (only the seeded input generator in
+``moe_synth`` feeds both sides).
+
+What it computes, step by step, in the order and notation of the pages:
+
+* Router: a bias-free linear layer ``logits = W_gate x`` of shape (N, E)
+  ["MoE 推理完整机制" (zoe.im), 第一层: Router 与 Top-K 的算法细节; the
+  ``gate = nn.Linear(hidden_dim, num_experts, bias=False)`` of
+  "MoE 大规模分布式推理工程实战" (ybb.press), 4.1 Router 辅助损失的工程化实现].
+* Optional per-expert bias added to the logits before top-K
+  [ybb.press 4.1, ``logits + self.dynamic_bias``].
+* Top-K per token, then either softmax over the K selected values (weights
+  sum to 1) [zoe.im 第一层] or the sigmoid variant where the selected
+  sigmoid scores are divided by their sum [zoe.im 第一层, "DeepSeek 的
+  sigmoid + norm 变体"].
+* Contiguous permutation: tokens regrouped into one buffer with one segment
+  per expert, plus ``expert_offsets`` [zoe.im 第二层, 范式 A Step 1]; counts
+  by histogram and offsets by exclusive prefix sum [ybb.press 2.2,
+  ``moe_alltoall_start`` steps 1-2].
+* Capacity-padded variant: a fixed capacity per expert, filled in token
+  order, overflow dropped [zoe.im 第二层, 范式 B; capacity formula of
+  "MoE工程实战" (jsqmd.com) 3.2].
+* Per-expert FFN, two GEMMs (m_e, D) -> (m_e, F) -> (m_e, D), empty experts
+  skipped [zoe.im 范式 A Step 2; jsqmd.com 4.2 ``numel() > 0``].  The FFN
+  is SwiGLU: ``h = silu(x Wg^T) * (x Wu^T)``, ``out = h Wd^T``.
+* Un-permutation: results put back in token order, multiplied by the router
+  weights and summed [zoe.im 范式 A Step 3 and the opening dataflow].
+
+Precision: every sum is taken in float64.  Values are rounded only where the
+layer stores them: logits and router weights to fp32, and the bf16 tensors
+``h`` (FFN intermediate), ``out_perm`` (FFN output rows) and ``y`` (layer
+output) to bf16 with round-to-nearest-even.  Top-K is decided on fp32 keys.
+
+Readings where the pages are silent (each also listed in the design doc):
+ties in top-K go to the lower expert id, -0.0 equals +0.0 and NaN keys sort
+last; the K outputs are in descending key order; selection in sigmoid mode is
+done on the key itself (sigmoid is strictly increasing); the bias is one fp32
+add and also feeds the weights; a sigmoid sum of zero gives weights 1/K;
+within a segment rows are in ascending slot order n*K+k; capacity is
+``ceil(num*N*K/(den*E))`` and the first ``cap`` slots (slot order) of each
+expert are kept, dropped slots contribute nothing and the kept weights are not
+renormalised; padding rows are zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GATING_SOFTMAX = "softmax"
+GATING_SIGMOID = "sigmoid"
+
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Decode raw bf16 bit patterns (uint16) to float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(v) -> np.ndarray:
+    """Round float64 values to bf16 (8 significant bits), nearest-even.
+
+    frexp gives v = m * 2**ex with 0.5 <= |m| < 1, so m * 2**8 has 8 integer
+    bits; np.rint rounds half to even.  Normal range only (the layer's values
+    stay far from bf16 overflow and underflow).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, ex = np.frexp(v)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), ex - 8)
+
+
+def f64_to_bf16_bits(v) -> np.ndarray:
+    r = round_bf16(v).astype(np.float32)          # exact: 8 significant bits
+    return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def round_f32(v) -> np.ndarray:
+    return np.asarray(v, dtype=np.float64).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# router and gating
+# --------------------------------------------------------------------------
+
+def router_logits(x_bits, w_router) -> np.ndarray:
+    """logits[n, e] = sum_d x[n, d] * W_gate[e, d], float64 sum, rounded to fp32.
+
+    zoe.im 第一层 (``logits = W_gate @ x``); W_gate in nn.Linear [E, D] layout
+    (ybb.press 4.1).  Each product bf16*fp32 is exact in float64.
+    """
+    x = bf16_to_f64(x_bits)
+    w = np.asarray(w_router, dtype=np.float32).astype(np.float64)
+    return round_f32(x @ w.T)
+
+
+def gating_keys(logits, bias=None) -> np.ndarray:
+    """Selection keys: logits plus the per-expert bias (one fp32 add), as fp32.
+
+    ybb.press 4.1 adds the dynamic bias to the logits before ``torch.topk``.
+    -0.0 becomes +0.0 and NaN becomes -inf, so equal values compare equal and
+    a NaN is never selected ahead of a number.
+    """
+    key = np.asarray(logits, dtype=np.float32)
+    if bias is not None:
+        key = key + np.asarray(bias, dtype=np.float32)[None, :]   # float32 + float32
+    key = key.astype(np.float32, copy=True)
+    key[key == 0] = np.float32(0.0)
+    key[np.isnan(key)] = np.float32(-np.inf)
+    return key
+
+
+def select_topk(keys, K: int) -> np.ndarray:
+    """Ids of the K largest keys per row, largest first, equal keys by lower id.
+
+    zoe.im 第一层 (``torch.topk(logits, k=K)``, sorted output).
+    """
+    keys = np.asarray(keys, dtype=np.float32)
+    N, E = keys.shape
+    ids = np.arange(E)
+    out = np.empty((N, K), dtype=np.int32)
+    for n in range(N):
+        order = np.lexsort((ids, -keys[n].astype(np.float64)))   # key desc, then id asc
+        out[n] = order[:K]
+    return out
+
+
+def topk_weights(sel_keys, gating: str) -> np.ndarray:
+    """Router weights of the K selected experts (float64 math, fp32 result).
+
+    softmax: w_j = exp(k_j - max) / sum_i exp(k_i - max)     (zoe.im 第一层)
+    sigmoid: s_j = 1/(1+exp(-k_j)), w_j = s_j / sum_i s_i     (zoe.im sigmoid + norm)
+    A row whose selected keys give a zero denominator gets w = 1/K.
+    """
+    k = np.asarray(sel_keys, dtype=np.float32).astype(np.float64)
+    K = k.shape[1]
+    if gating == GATING_SOFTMAX:
+        kmax = k.max(axis=1, keepdims=True)
+        finite = np.isfinite(kmax[:, 0])
+        z = np.zeros_like(k)
+        z[finite] = np.exp(k[finite] - kmax[finite])
+    elif gating == GATING_SIGMOID:
+        z = 1.0 / (1.0 + np.exp(-k))
+    else:
+        raise ValueError(gating)
+    tot = z.sum(axis=1, keepdims=True)
+    w = np.where(tot > 0, z / np.where(tot > 0, tot, 1.0), 1.0 / K)
+    return round_f32(w)
+
+
+def route_from_logits(logits, bias, K: int, gating: str):
+    """(topk_ids [N,K] int32, topk_weights [N,K] fp32) from fp32 logits."""
+    keys = gating_keys(logits, bias)
+    ids = select_topk(keys, K)
+    sel = np.take_along_axis(keys, ids.astype(np.int64), axis=1)
+    return ids, topk_weights(sel, gating)
+
+
+def route(x_bits, w_router, bias, K: int, gating: str):
+    logits = router_logits(x_bits, w_router)
+    ids, w = route_from_logits(logits, bias, K, gating)
+    return logits, ids, w
+
+
+# --------------------------------------------------------------------------
+# permutation
+# --------------------------------------------------------------------------
+
+def capacity(N: int, K: int, E: int, num: int, den: int) -> int:
+    """Per-expert capacity ceil((num/den) * N*K / E) in exact integer arithmetic.
+
+    zoe.im 范式 B (``ceil(1.5 * N * K / num_experts)``) with the factor as a
+    parameter; jsqmd.com 3.2 gives the same product tokens*k/E*factor.
+    """
+    return -((-num * N * K) // (den * E))
+
+
+def permute(topk_ids, E: int, cap: int | None = None):
+    """Group the N*K slots by expert.
+
+    Slots are numbered i = n*K + k.  Histogram then exclusive prefix sum give
+    ``expert_offsets`` (ybb.press 2.2; zoe.im 范式 A, offsets [0,3,5,8] for
+    its 8-token example).  Walking the slots in ascending order, each takes
+    the next free row of its expert's segment, so every segment lists its
+    tokens in token order, as in the example.
+
+    cap None : contiguous segments, offsets[e+1] = offsets[e] + counts[e].
+    cap int  : padded segments [e*cap, (e+1)*cap); slots past the capacity
+               are dropped (slot_row = -1); unused rows have row_token = -1.
+
+    Returns counts [E] (raw, before any drop), offsets [E+1], row_token [R],
+    slot_row [N*K].
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    N, K = ids.shape
+    flat = ids.reshape(-1)
+    S = N * K
+    counts = np.zeros(E, dtype=np.int64)
+    for i in range(S):
+        counts[flat[i]] += 1
+    if cap is None:
+        offsets = np.zeros(E + 1, dtype=np.int64)
+        for e in range(E):
+            offsets[e + 1] = offsets[e] + counts[e]
+        R = S
+    else:
+        offsets = np.arange(E + 1, dtype=np.int64) * cap
+        R = E * cap
+    run = np.zeros(E, dtype=np.int64)
+    row_token = np.full(R, -1, dtype=np.int64)
+    slot_row = np.full(S, -1, dtype=np.int64)
+    for i in range(S):
+        e = flat[i]
+        if cap is None or run[e] < cap:
+            row = offsets[e] + run[e]
+            row_token[row] = i // K
+            slot_row[i] = row
+        run[e] += 1
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            row_token.astype(np.int32), slot_row.astype(np.int32))
+
+
+def gather_rows(x_bits, row_token) -> np.ndarray:
+    """x_perm[row] = x[row_token[row]] (bit copy); padding rows are zero."""
+    x = np.asarray(x_bits, dtype=np.uint16)
+    rt = np.asarray(row_token, dtype=np.int64)
+    out = np.zeros((rt.shape[0], x.shape[1]), dtype=np.uint16)
+    valid = rt >= 0
+    out[valid] = x[rt[valid]]
+    return out
+
+
+# --------------------------------------------------------------------------
+# expert FFN and combine
+# --------------------------------------------------------------------------
+
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_rows(a, wg_bits, wu_bits, wd_bits):
+    """One expert's FFN on rows a [m, D] (float64 values).
+
+    g = a Wg^T, u = a Wu^T (float64); h = bf16(silu(g) * u);
+    out = bf16(h Wd^T).  Wg, Wu are [F, D] and Wd is [D, F] (nn.Linear layout).
+    Returns (h, out) as float64 arrays holding bf16 values.
+    """
+    wg = bf16_to_f64(wg_bits)
+    wu = bf16_to_f64(wu_bits)
+    wd = bf16_to_f64(wd_bits)
+    g = a @ wg.T
+    u = a @ wu.T
+    h = round_bf16(silu(g) * u)
+    out = round_bf16(h @ wd.T)
+    return h, out
+
+
+def expert_ffn(x_perm_bits, offsets, w_gate_bits, w_up_bits, w_down_bits):
+    """Run each expert's FFN over its own segment of the permuted buffer.
+
+    zoe.im 范式 A Step 2: expert e maps its (m_e, D) rows to (m_e, F) and back
+    to (m_e, D).  Experts with an empty segment are skipped (jsqmd.com 4.2).
+    Returns (h [R, F], out_perm [R, D]) as float64 arrays of bf16 values.
+    """
+    xp = bf16_to_f64(x_perm_bits)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = offsets.shape[0] - 1
+    R, D = xp.shape
+    F = np.asarray(w_gate_bits).shape[1]
+    h_all = np.zeros((R, F))
+    out = np.zeros((R, D))
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi == lo:
+            continue
+        h, o = swiglu_rows(xp[lo:hi], w_gate_bits[e], w_up_bits[e], w_down_bits[e])
+        h_all[lo:hi] = h
+        out[lo:hi] = o
+    return h_all, out
+
+
+def combine(out_perm, slot_row, topk_w) -> np.ndarray:
+    """y[n] = bf16( sum_k w[n,k] * out_perm[slot_row[n*K+k]] ), k ascending, kept slots only.
+
+    zoe.im 范式 A Step 3: restore token order and multiply by the router
+    weights; the opening dataflow then sums the K weighted results.
+    """
+    op = np.asarray(out_perm, dtype=np.float64)
+    w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+    N, K = w.shape
+    sr = np.asarray(slot_row, dtype=np.int64).reshape(N, K)
+    y = np.zeros((N, op.shape[1]))
+    for k in range(K):
+        rows = sr[:, k]
+        kept = rows >= 0
+        y[kept] += w[kept, k][:, None] * op[rows[kept]]
+    return round_bf16(y)
+
+
+# --------------------------------------------------------------------------
+# whole layer
+# --------------------------------------------------------------------------
+
+def forward(x_bits, w_router, bias, w_gate_bits, w_up_bits, w_down_bits,
+            K: int, gating: str, cap: int | None = None, logits=None) -> dict:
+    """The whole layer.  If ``logits`` is given it replaces the router GEMM
+    (used to check selection on exactly the fp32 logits another side produced).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    E = np.asarray(w_router).shape[0]
+    if logits is None:
+        logits = router_logits(x_bits, w_router)
+    ids, w = route_from_logits(logits, bias, K, gating)
+    counts, offsets, row_token, slot_row = permute(ids, E, cap)
+    x_perm = gather_rows(x_bits, row_token)
+    h, out_perm = expert_ffn(x_perm, offsets, w_gate_bits, w_up_bits, w_down_bits)
+    y = combine(out_perm, slot_row, w)
+    return dict(logits=logits, topk_ids=ids, topk_weights=w, expert_counts=counts,
+                expert_offsets=offsets, row_token=row_token, slot_row=slot_row,
+                x_perm=x_perm, h=h, out_perm=out_perm, y=y)
+
+
+def token_outputs(x_bits, topk_ids, topk_w, kept_mask, expert_weights):
+    """y for a subset of tokens, one token at a time (for large layers).
+
+    x_bits [n, D]; topk_ids / topk_w / kept_mask [n, K]; ``expert_weights(e)``
+    returns (Wg, Wu, Wd) bf16 bit arrays of expert e.  Per token:
+    y = bf16(sum_k w_k * out_k) with out_k the expert FFN of that token's row.
+    Returns (y [n, D], out [n, K, D]) as float64 arrays of bf16 values.
+    """
+    xs = bf16_to_f64(x_bits)
+    n, K = np.asarray(topk_ids).shape
+    D = xs.shape[1]
+    outs = np.zeros((n, K, D))
+    need = {}
+    for t in range(n):
+        for k in range(K):
+            if kept_mask[t, k]:
+                need.setdefault(int(topk_ids[t, k]), []).append((t, k))
+    for e, pairs in sorted(need.items()):
+        wg, wu, wd = expert_weights(e)
+        rows = np.stack([xs[t] for t, _ in pairs])
+        _, o = swiglu_rows(rows, wg, wu, wd)
+        for j, (t, k) in enumerate(pairs):
+            outs[t, k] = o[j]
+    w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+    y = np.zeros((n, D))
+    for k in range(K):
+        y += np.where(np.asarray(kept_mask)[:, k:k + 1], w[:, k:k + 1] * outs[:, k], 0.0)
+    return round_bf16(y), outs

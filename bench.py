@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Throughput of the single-GPU MoE-layer forward pass on MI355X.
+
+One step = the whole layer on one batch: router GEMM + top-K gating, permute
+into expert segments, grouped gate/up GEMM with SwiGLU, grouped down GEMM,
+unpermute + weighted combine -- the five libmoe calls moe_forward is made of,
+issued separately so the dominant kernel (the gate/up grouped GEMM) can be
+bracketed with HIP events on the stream it runs on.  Inputs are synthetic,
+seeded and already resident in HBM when timing starts.
+
+Prints one JSON line.  ``value`` is tokens/s of the layer on this GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral",
+                    help="tiny | mixtral | deepseek_v3 | qwen3_decode | hot_skew")
+    ap.add_argument("--padded", action="store_true", help="capacity-padded layout (hot_skew)")
+    ap.add_argument("--cpu-tokens", type=int, default=192,
+                    help="tokens of the CPU-oracle sample (0 = skip the CPU baseline)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_level_amd as moe
+    import moe_synth as ms
+
+    cfg = ms.CONFIGS[args.config]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    cap = cfg.capacity if args.padded else None
+    if args.padded and cap is None:
+        raise SystemExit(f"{cfg.name} has no capacity factor")
+    t0 = time.time()
+    inp = ms.make_inputs(cfg, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    p = moe.problem(cfg.N, cfg.D, cfg.F, cfg.E, cfg.K, cfg.gating, cap)
+    R, capv = moe.permuted_rows(p)
+    N, D, E, K, F = cfg.N, cfg.D, cfg.E, cfg.K, cfg.F
+    e = lambda *s, dt=torch.float32: torch.empty(*s, dtype=dt, device=dev)
+    logits, ids, w = e(N, E), e(N, K, dt=torch.int32), e(N, K)
+    counts, offsets = e(E, dt=torch.int32), e(E + 1, dt=torch.int32)
+    row_token, slot_row = e(R, dt=torch.int32), e(N * K, dt=torch.int32)
+    x_perm, h = e(R, D, dt=torch.bfloat16), e(R, F, dt=torch.bfloat16)
+    out_perm, y = e(R, D, dt=torch.bfloat16), e(N, D, dt=torch.bfloat16)
+    ws = torch.empty(moe.workspace_size(p), dtype=torch.uint8, device=dev)
+    x, wr, bias = inp["x"], inp["w_router"], inp["bias"]
+    wg, wu, wd = inp["w_gate"], inp["w_up"], inp["w_down"]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
+        moe.permute(p, x, ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        moe.expert_gateup(p, x_perm, offsets, wg, wu, h, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.expert_down(p, h, offsets, wd, out_perm, stream=stream)
+        moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    gateup_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    counts_h = counts.cpu().numpy().astype(np.int64)
+    kept = int(np.minimum(counts_h, capv).sum()) if capv else cfg.S
+    flops = 2.0 * N * D * E + 6.0 * D * F * kept        # router + SwiGLU FFN, kept slots
+    gateup_flops = 4.0 * D * F * kept
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gateup_tflops = gateup_flops / (gateup_ms * 1e-3) / 1e12
+    touched = int((counts_h > 0).sum())
+    weight_bytes = 3.0 * touched * F * D * 2
+    line = {
+        "metric": "MoE-layer tokens/sec + TFLOPS (% bf16 MFMA peak) / HBM GB/s (% peak), 1 GPU",
+        "value": N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based draws, random-init weights)",
+        "config": {"workload": cfg.note + (" [capacity-padded]" if capv else ""),
+                   "tokens": N, "hidden": D, "experts": E, "top_k": K, "ffn": F,
+                   "gating": cfg.gating, "capacity": capv or None},
+        "tflops": tflops,
+        "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "weight_stream_gbps": weight_bytes / (ms_step * 1e-3) / 1e9,
+        "max_expert_rows": int(counts_h.max()),
+        "dropped_slots": int(cfg.S - kept),
+        "roofline": {
+            "kernel": "grouped_gemm_kernel (gate/up + SwiGLU)",
+            "bound": "mfma",
+            "achieved": gateup_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gateup_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "avg_ms": gateup_ms,
+        },
+        "cpu_baseline": None,
+    }
+    print(f"[bench] {ms_step:.3f} ms/step, gate/up {gateup_ms:.3f} ms", file=sys.stderr,
+          flush=True)
+
+    if args.cpu_tokens > 0:
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, N), capv)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, inp, n, capv):
+    """The CPU oracle, as it stands, on the first n tokens of the same layer."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+
+    wbytes = 3 * cfg.E * cfg.F * cfg.D * 2
+    if wbytes > 8e9:
+        return {"value": None, "unit": "tokens/s", "cores": None, "kind": "oracle",
+                "sample": f"skipped: {wbytes / 1e9:.1f} GB of expert weights do not fit "
+                          f"the host-side oracle run"}
+
+    def b(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    x = b(inp["x"][:n])
+    wr = inp["w_router"].cpu().numpy()
+    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    wg, wu, wd = b(inp["w_gate"]), b(inp["w_up"]), b(inp["w_down"])
+    cap = None
+    if capv:
+        cap = O.capacity(n, cfg.K, cfg.E, *cfg.capacity)
+    t0 = time.perf_counter()
+    O.forward(x, wr, bias, wg, wu, wd, cfg.K, cfg.gating, cap=cap)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.N} tokens, same weights, float64 numpy oracle "
+                      f"({dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * libmoe -- forward pass of one Mixture-of-Experts layer on one AMD Instinct
+ * MI355X (gfx950) GPU, as a C ABI over hand-written HIP kernels.
+ *
+ * The layer (from "MoE 推理完整机制：从 Router 到 Expert Parallelism 的一切",
+ * zoe.im, opening dataflow and sections 第一层 / 第二层):
+ *   N x D tokens -> router logits (N x E) -> top-K experts per token and
+ *   their weights -> tokens regrouped into one expert-contiguous buffer with
+ *   expert_offsets -> per-expert FFN (two GEMMs) -> rows put back in token
+ *   order, scaled by the router weights and summed -> N x D output.
+ *
+ * Conventions for every call below
+ *   - Pointers are DEVICE pointers unless marked "host".  bf16 tensors are
+ *     passed as raw bit patterns (uint16_t).  All tensors are dense and
+ *     row-major; weights use the nn.Linear [out, in] layout.
+ *   - The caller owns every buffer.  No call allocates or frees device
+ *     memory; scratch comes from the caller's workspace `ws` of `ws_bytes`
+ *     bytes (size from moe_workspace_size; 256-byte alignment).
+ *   - Every call enqueues work on `stream` (a hipStream_t, NULL = default
+ *     stream) and returns without waiting; results are ready when the
+ *     stream reaches that point.  No call reads device memory on the host.
+ *   - Arguments are checked on the host before any HIP call:
+ *     MOE_ERR_INVALID_ARG for a null required pointer or an inconsistent
+ *     problem, MOE_ERR_UNSUPPORTED for shapes or alignments the kernels do
+ *     not handle, MOE_ERR_WORKSPACE for a missing or too small workspace.
+ *     A failed launch returns MOE_ERR_HIP.  Nothing aborts, throws or prints.
+ *   - num_tokens == 0 is valid: the call returns MOE_OK and launches nothing.
+ *   - Calls are re-entrant (no mutable global state besides a per-device
+ *     cache of the compute-unit count and a thread-local last HIP error);
+ *     concurrent calls on different streams must use different workspaces
+ *     and outputs.
+ *   - Results are deterministic: routing, counts, offsets and the
+ *     permutation are exact integer results; floating-point outputs do not
+ *     depend on scheduling (no floating-point atomics).
+ */
+#ifndef LIBMOE_MOE_H_
+#define LIBMOE_MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+/* Gating functions, zoe.im section 第一层 (Router 与 Top-K):
+ *  SOFTMAX_TOPK   : top-K of the keys, then softmax over the K selected keys.
+ *  SIGMOID_RENORM : top-K, weights sigmoid(key) divided by their sum over the
+ *                   K selected (the "DeepSeek sigmoid + norm" variant).
+ * The key of expert e is logit[e] + bias[e] (one fp32 add; bias optional), as
+ * in the dynamic-bias router of "MoE 大规模分布式推理工程实战" (ybb.press)
+ * section 4.1.  Selection: largest key first, equal keys by lower expert id,
+ * -0.0 == +0.0, NaN keys rank below every number.  In sigmoid mode selection
+ * is made on the key itself (sigmoid is increasing), so no rounding of
+ * sigmoid can change the chosen set. */
+typedef enum { MOE_GATING_SOFTMAX_TOPK = 0, MOE_GATING_SIGMOID_RENORM = 1 } moe_gating;
+
+typedef struct {
+  int64_t num_tokens;   /* N >= 0                                               */
+  int32_t hidden;       /* D: multiple of 64, >= 64                             */
+  int32_t ffn;          /* F: expert FFN width, multiple of 64, >= 64            */
+  int32_t num_experts;  /* E: 1 <= E <= 1024                                     */
+  int32_t top_k;        /* K: 1 <= K <= min(E, 64)                               */
+  int32_t gating;       /* moe_gating                                            */
+  /* Capacity factor num/den.  num == 0: contiguous layout (范式 A), no token
+   * is dropped, R = N*K rows.  num > 0: capacity-padded layout (范式 B),
+   * cap = ceil(num*N*K / (den*E)), expert e owns rows [e*cap, (e+1)*cap),
+   * the first cap slots of each expert in slot order are kept and the rest
+   * dropped, R = E*cap rows.  (zoe.im 范式 B; capacity = tokens*k/E*factor in
+   * "MoE工程实战" (jsqmd.com) 3.2.) */
+  int32_t capacity_num;
+  int32_t capacity_den;
+} moe_problem;
+
+/* ---------------------------------------------------------------- host only */
+
+int moe_abi_version(void);
+const char* moe_status_str(moe_status s);
+
+/* Text of the HIP error behind this thread's last MOE_ERR_HIP ("no error"
+ * before any).  Thread-local; the string is static. */
+const char* moe_last_hip_error(void);
+
+/* Rows R of the permuted buffers (x_perm, out_perm, row_token): N*K in the
+ * contiguous layout, E*cap in the padded one.  `rows` and `cap` are host
+ * pointers; `cap` may be NULL (it receives 0 in the contiguous layout). */
+moe_status moe_permuted_rows(const moe_problem* p, int64_t* rows, int64_t* cap);
+
+/* Workspace bytes (host pointer `bytes`) that moe_forward needs for this
+ * problem.  Every staged call below needs at most this much. */
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* ---------------------------------------------------------------- the path */
+
+/* Router GEMM and top-K gating (zoe.im 第一层; ybb.press 4.1).
+ *   x            [N, D] bf16, or NULL: then `logits` is an INPUT and the
+ *                router GEMM is skipped (selection on given fp32 logits).
+ *   w_router     [E, D] fp32 (the gate Linear, no bias); ignored if x NULL.
+ *   expert_bias  [E] fp32 or NULL (added to the logits before selection and
+ *                used for the weights).
+ *   logits       [N, E] fp32: written when x != NULL (pre-bias), read else.
+ *   topk_ids     [N, K] int32, out: selected experts, largest key first.
+ *   topk_weights [N, K] fp32, out: router weights, sum to 1 per row.
+ * Needs no workspace (ws may be NULL). */
+moe_status moe_route(const moe_problem* p, const uint16_t* x, const float* w_router,
+                     const float* expert_bias, float* logits, int32_t* topk_ids,
+                     float* topk_weights, void* ws, size_t ws_bytes, void* stream);
+
+/* Permutation into expert segments (zoe.im 范式 A Step 1 / 范式 B).
+ * Slot i = n*K + k.  Histogram + exclusive prefix sum give the offsets; each
+ * slot takes the next row of its expert's segment in ascending slot order, so
+ * a segment lists its tokens in token order.
+ *   x              [N, D] bf16 input rows.
+ *   topk_ids       [N, K] int32; a value outside [0, E) marks its slot as
+ *                  dropped (slot_row -1, not counted).
+ *   expert_counts  [E] int32 out: slots routed to each expert (before drops).
+ *   expert_offsets [E+1] int32 out: segment starts; contiguous: prefix sums
+ *                  of the counts, offsets[E] = N*K; padded: e*cap.
+ *   row_token      [R] int32 out: token of each row, -1 for padding rows.
+ *   slot_row       [N*K] int32 out: row of each slot, -1 if dropped.
+ *   x_perm         [R, D] bf16 out: x_perm[r] = x[row_token[r]], padding
+ *                  rows zero.
+ * Workspace: moe_workspace_size bytes suffice. */
+moe_status moe_permute(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
+                       int32_t* slot_row, uint16_t* x_perm, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Grouped SwiGLU expert FFN over the permuted rows (zoe.im 范式 A Step 2,
+ * "Grouped GEMM": one launch for all experts' GEMMs of different sizes).
+ * For expert e and each row r in [offsets[e], offsets[e+1]):
+ *   h[r]        = bf16( silu(x_perm[r] . Wg[e]^T) * (x_perm[r] . Wu[e]^T) )
+ *   out_perm[r] = bf16( h[r] . Wd[e]^T ),          silu(g) = g / (1 + e^-g)
+ * with fp32 accumulation.  Rows outside every segment are not written.
+ *   x_perm         [R, D] bf16;  expert_offsets [E+1] int32 (non-decreasing,
+ *                  offsets[E] <= R; not checked on the device).
+ *   w_gate, w_up   [E, F, D] bf16;  w_down [E, D, F] bf16.
+ *   out_perm       [R, D] bf16 out.
+ *   h              [R, F] bf16 out, or NULL to keep it in the workspace.
+ * Workspace: needed only when h is NULL; moe_workspace_size bytes suffice. */
+moe_status moe_grouped_ffn(const moe_problem* p, const uint16_t* x_perm,
+                           const int32_t* expert_offsets, const uint16_t* w_gate,
+                           const uint16_t* w_up, const uint16_t* w_down, uint16_t* out_perm,
+                           uint16_t* h, void* ws, size_t ws_bytes, void* stream);
+
+/* The two GEMMs of the expert FFN as separate launches (moe_grouped_ffn is
+ * moe_expert_gateup followed by moe_expert_down).  Same arguments, layouts
+ * and row coverage as moe_grouped_ffn; neither needs a workspace.
+ *   moe_expert_gateup: h [R, F] bf16 out from x_perm, w_gate, w_up.
+ *   moe_expert_down  : out_perm [R, D] bf16 out from h, w_down. */
+moe_status moe_expert_gateup(const moe_problem* p, const uint16_t* x_perm,
+                             const int32_t* expert_offsets, const uint16_t* w_gate,
+                             const uint16_t* w_up, uint16_t* h, void* stream);
+moe_status moe_expert_down(const moe_problem* p, const uint16_t* h,
+                           const int32_t* expert_offsets, const uint16_t* w_down,
+                           uint16_t* out_perm, void* stream);
+
+/* Un-permutation and weighted combine (zoe.im 范式 A Step 3):
+ *   y[n] = bf16( sum_{k=0..K-1, slot_row[n*K+k] >= 0} w[n,k] * out_perm[slot_row[n*K+k]] )
+ * summed in k order in fp32.  Dropped slots contribute nothing and the kept
+ * weights are not renormalised.
+ *   out_perm [R, D] bf16; slot_row [N*K] int32 (values < R; not checked on
+ *   the device); topk_weights [N, K] fp32; y [N, D] bf16 out.
+ * Needs no workspace. */
+moe_status moe_unpermute_combine(const moe_problem* p, const uint16_t* out_perm,
+                                 const int32_t* slot_row, const float* topk_weights,
+                                 uint16_t* y, void* stream);
+
+/* The whole layer: moe_route, moe_permute, moe_grouped_ffn and
+ * moe_unpermute_combine in sequence on one stream.
+ *   x [N, D] bf16; w_router [E, D] fp32; expert_bias [E] fp32 or NULL;
+ *   w_gate, w_up [E, F, D] bf16; w_down [E, D, F] bf16; y [N, D] bf16 out.
+ *   logits [N, E], topk_ids [N, K], topk_weights [N, K], expert_counts [E],
+ *   expert_offsets [E+1]: optional outputs (NULL = kept in the workspace).
+ * Workspace: moe_workspace_size(p) bytes. */
+moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_router,
+                       const float* expert_bias, const uint16_t* w_gate, const uint16_t* w_up,
+                       const uint16_t* w_down, uint16_t* y, float* logits, int32_t* topk_ids,
+                       float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_MOE_H_ */

@@ -1,0 +1,29 @@
+"""Single-GPU MoE-layer forward pass for AMD Instinct MI355X (gfx950).
+
+The compute path is the C-ABI library ``libmoe.so`` (hand-written HIP
+kernels, declared in ``include/moe.h``).  This package only marshals
+arguments: it turns torch tensors into device pointers and the current HIP
+stream into a handle, calls the library and raises on a non-OK status.
+PyTorch supplies device memory and streams and nothing else; there is no
+fallback path, and a missing library is an error.
+"""
+from ._lib import (  # noqa: F401
+    GATING_SIGMOID_RENORM,
+    GATING_SOFTMAX_TOPK,
+    MoEError,
+    MoEProblem,
+    abi_version,
+    expert_down,
+    expert_gateup,
+    forward,
+    grouped_ffn,
+    lib,
+    library_path,
+    permute,
+    permuted_rows,
+    problem,
+    route,
+    status_str,
+    unpermute_combine,
+    workspace_size,
+)

@@ -1,0 +1,176 @@
+"""ctypes binding of libmoe (include/moe.h): argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(HERE, "libmoe.so")
+
+MOE_OK = 0
+GATING_SOFTMAX_TOPK = 0
+GATING_SIGMOID_RENORM = 1
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or alignment",
+           3: "workspace missing or too small", 4: "HIP launch failed"}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str = ""):
+        msg = f"{fn}: status {status} ({_STATUS.get(status, 'unknown')})"
+        super().__init__(msg + (f": {detail}" if detail else ""))
+        self.status = status
+
+
+class MoEProblem(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int64), ("hidden", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("gating", ctypes.c_int32),
+                ("capacity_num", ctypes.c_int32), ("capacity_den", ctypes.c_int32)]
+
+
+def _load():
+    # torch first: its bundled HIP runtime (soname libamdhip64.so.7) is then the
+    # one libmoe binds to, so both share one runtime, one device context and
+    # the same streams.  Loading libmoe first would pull in a second runtime.
+    import torch  # noqa: F401
+    if not os.path.exists(library_path):
+        raise ImportError(f"{library_path} is not built; run __graft_entry__.build() "
+                          f"(hipcc for gfx950) first")
+    L = ctypes.CDLL(library_path)
+    P = ctypes.POINTER(MoEProblem)
+    vp = ctypes.c_void_p
+    sz = ctypes.c_size_t
+    L.moe_abi_version.restype = ctypes.c_int
+    L.moe_abi_version.argtypes = []
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_status_str.argtypes = [ctypes.c_int]
+    L.moe_last_hip_error.restype = ctypes.c_char_p
+    L.moe_last_hip_error.argtypes = []
+    L.moe_permuted_rows.restype = ctypes.c_int
+    L.moe_permuted_rows.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    L.moe_workspace_size.restype = ctypes.c_int
+    L.moe_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_permute.restype = ctypes.c_int
+    L.moe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_grouped_ffn.restype = ctypes.c_int
+    L.moe_grouped_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_gateup.restype = ctypes.c_int
+    L.moe_expert_gateup.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_down.restype = ctypes.c_int
+    L.moe_expert_down.argtypes = [P, vp, vp, vp, vp, vp]
+    L.moe_unpermute_combine.restype = ctypes.c_int
+    L.moe_unpermute_combine.argtypes = [P, vp, vp, vp, vp, vp]
+    L.moe_forward.restype = ctypes.c_int
+    L.moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    return L
+
+
+lib = _load()
+
+
+def abi_version() -> int:
+    return lib.moe_abi_version()
+
+
+def status_str(s: int) -> str:
+    return lib.moe_status_str(s).decode()
+
+
+def problem(N: int, D: int, F: int, E: int, K: int, gating="softmax",
+            capacity: Optional[tuple] = None) -> MoEProblem:
+    g = {"softmax": GATING_SOFTMAX_TOPK, "sigmoid": GATING_SIGMOID_RENORM}.get(gating, gating)
+    num, den = capacity if capacity else (0, 1)
+    return MoEProblem(N, D, F, E, K, g, num, den)
+
+
+def _ptr(t):
+    """Device address of a tensor (or an int address, or None for NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    if t is None or isinstance(t, int):
+        return 0
+    return t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, st: int):
+    if st != MOE_OK:
+        detail = lib.moe_last_hip_error().decode() if st == 4 else ""
+        raise MoEError(fn, st, detail)
+
+
+def permuted_rows(p: MoEProblem):
+    rows = ctypes.c_int64()
+    cap = ctypes.c_int64()
+    _check("moe_permuted_rows", lib.moe_permuted_rows(ctypes.byref(p), ctypes.byref(rows),
+                                                      ctypes.byref(cap)))
+    return rows.value, cap.value
+
+
+def workspace_size(p: MoEProblem) -> int:
+    n = ctypes.c_size_t()
+    _check("moe_workspace_size", lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def route(p, x, w_router, bias, logits, topk_ids, topk_weights, ws=None, stream=None):
+    _check("moe_route", lib.moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
+                                      _ptr(logits), _ptr(topk_ids), _ptr(topk_weights),
+                                      _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def permute(p, x, topk_ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=None):
+    _check("moe_permute", lib.moe_permute(ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(counts),
+                                          _ptr(offsets), _ptr(row_token), _ptr(slot_row),
+                                          _ptr(x_perm), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def grouped_ffn(p, x_perm, offsets, w_gate, w_up, w_down, out_perm, h, ws, stream=None):
+    _check("moe_grouped_ffn", lib.moe_grouped_ffn(ctypes.byref(p), _ptr(x_perm), _ptr(offsets),
+                                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                                  _ptr(out_perm), _ptr(h), _ptr(ws), _nbytes(ws),
+                                                  _stream(stream)))
+
+
+def expert_gateup(p, x_perm, offsets, w_gate, w_up, h, stream=None):
+    _check("moe_expert_gateup", lib.moe_expert_gateup(ctypes.byref(p), _ptr(x_perm), _ptr(offsets),
+                                                      _ptr(w_gate), _ptr(w_up), _ptr(h),
+                                                      _stream(stream)))
+
+
+def expert_down(p, h, offsets, w_down, out_perm, stream=None):
+    _check("moe_expert_down", lib.moe_expert_down(ctypes.byref(p), _ptr(h), _ptr(offsets),
+                                                  _ptr(w_down), _ptr(out_perm), _stream(stream)))
+
+
+def unpermute_combine(p, out_perm, slot_row, topk_weights, y, stream=None):
+    _check("moe_unpermute_combine",
+           lib.moe_unpermute_combine(ctypes.byref(p), _ptr(out_perm), _ptr(slot_row),
+                                     _ptr(topk_weights), _ptr(y), _stream(stream)))
+
+
+def forward(p, x, w_router, bias, w_gate, w_up, w_down, y, ws, logits=None, topk_ids=None,
+            topk_weights=None, counts=None, offsets=None, stream=None):
+    _check("moe_forward", lib.moe_forward(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
+                                          _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
+                                          _ptr(logits), _ptr(topk_ids), _ptr(topk_weights),
+                                          _ptr(counts), _ptr(offsets), _ptr(ws), _nbytes(ws),
+                                          _stream(stream)))

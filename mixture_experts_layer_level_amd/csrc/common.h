@@ -1,0 +1,82 @@
+// Internal definitions shared by the libmoe HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Validated problem shape, derived sizes included.
+struct Dims {
+  int64_t N;     // tokens
+  int64_t S;     // slots N*K
+  int64_t R;     // permuted rows: S (contiguous) or E*cap (padded)
+  int64_t cap;   // capacity per expert, 0 when contiguous
+  int D, F, E, K, gating;
+  bool padded;
+};
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Permutation kernels: slots handled per workgroup.
+constexpr int kPermChunk = 1024;
+
+// ---------------------------------------------------------------- device helpers
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- launchers
+
+// route.hip
+hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, float* logits,
+                              hipStream_t s);
+hipError_t launch_topk(const Dims& d, const float* logits, const float* bias, int32_t* ids,
+                       float* weights, hipStream_t s);
+
+// permute.hip
+size_t permute_ws_bytes(const Dims& d);
+hipError_t launch_permute(const Dims& d, const uint16_t* x, const int32_t* ids, int32_t* counts,
+                          int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                          uint16_t* x_perm, void* ws, hipStream_t s);
+
+// grouped_gemm.hip
+size_t ffn_ws_bytes(const Dims& d);  // h when the caller gives none
+hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                                const uint16_t* wg, const uint16_t* wu, uint16_t* h,
+                                hipStream_t s);
+hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
+                              const uint16_t* wd, uint16_t* out_perm, hipStream_t s);
+hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                              const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                              uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const Dims& d, const uint16_t* out_perm, const int32_t* slot_row,
+                          const float* weights, uint16_t* y, hipStream_t s);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace moe

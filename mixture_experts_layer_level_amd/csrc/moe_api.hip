@@ -1,0 +1,287 @@
+// C ABI of libmoe: argument checks, workspace layout and launch sequencing.
+// Every check runs on the host before the first HIP call of an entry point.
+#include <atomic>
+
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+moe_status check_problem(const moe_problem* p, Dims* d) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->num_tokens < 0 || p->hidden <= 0 || p->ffn <= 0 || p->num_experts < 1 ||
+      p->top_k < 1 || p->top_k > p->num_experts)
+    return MOE_ERR_INVALID_ARG;
+  if (p->gating != MOE_GATING_SOFTMAX_TOPK && p->gating != MOE_GATING_SIGMOID_RENORM)
+    return MOE_ERR_INVALID_ARG;
+  if (p->capacity_num < 0 || (p->capacity_num > 0 && p->capacity_den <= 0))
+    return MOE_ERR_INVALID_ARG;
+  if (p->hidden % 64 != 0 || p->ffn % 64 != 0 || p->num_experts > 1024 || p->top_k > 64)
+    return MOE_ERR_UNSUPPORTED;
+  d->N = p->num_tokens;
+  d->D = p->hidden;
+  d->F = p->ffn;
+  d->E = p->num_experts;
+  d->K = p->top_k;
+  d->gating = p->gating;
+  d->S = d->N * d->K;
+  d->padded = p->capacity_num > 0;
+  if (d->padded) {
+    // cap = ceil(num * S / (den * E)) in exact 128-bit integer arithmetic
+    const __int128 num = (__int128)p->capacity_num * d->S;
+    const __int128 den = (__int128)p->capacity_den * d->E;
+    const __int128 cap = (num + den - 1) / den;
+    if (cap > (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+    d->cap = (int64_t)cap;
+    d->R = d->cap * d->E;
+  } else {
+    d->cap = 0;
+    d->R = d->S;
+  }
+  // row and slot indices are int32 on the device, as are element offsets
+  // inside one expert's weight matrix
+  if (d->S >= (1ll << 31) || d->R >= (1ll << 31) || (int64_t)d->D * d->F >= (1ll << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct ForwardWs {
+  size_t logits, ids, weights, counts, offsets, row_token, slot_row, x_perm, out_perm, perm,
+      ffn, total;
+};
+
+ForwardWs forward_layout(const Dims& d) {
+  ForwardWs w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  w.logits = take((size_t)d.N * d.E * 4);
+  w.ids = take((size_t)d.S * 4);
+  w.weights = take((size_t)d.S * 4);
+  w.counts = take((size_t)d.E * 4);
+  w.offsets = take((size_t)(d.E + 1) * 4);
+  w.row_token = take((size_t)d.R * 4);
+  w.slot_row = take((size_t)d.S * 4);
+  w.x_perm = take((size_t)d.R * d.D * 2);
+  w.out_perm = take((size_t)d.R * d.D * 2);
+  w.perm = take(permute_ws_bytes(d));
+  w.ffn = take(ffn_ws_bytes(d));
+  w.total = o;
+  return w;
+}
+
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+inline moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  t_last_hip_error = e;
+  return MOE_ERR_HIP;
+}
+
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  g_cu_count[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or alignment";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_hip_error(void) { return hipGetErrorString(t_last_hip_error); }
+
+moe_status moe_permuted_rows(const moe_problem* p, int64_t* rows, int64_t* cap) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!rows) return MOE_ERR_INVALID_ARG;
+  *rows = d.R;
+  if (cap) *cap = d.cap;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = forward_layout(d).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_problem* p, const uint16_t* x, const float* w_router,
+                     const float* expert_bias, float* logits, int32_t* topk_ids,
+                     float* topk_weights, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_ids || !topk_weights || (x && !w_router)) return MOE_ERR_INVALID_ARG;
+  if (x && (!aligned16(x) || !aligned16(w_router))) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (x) {
+    st = hip_status(launch_router_gemm(d, x, w_router, logits, s));
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(launch_topk(d, logits, expert_bias, topk_ids, topk_weights, s));
+}
+
+moe_status moe_permute(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
+                       int32_t* slot_row, uint16_t* x_perm, void* ws, size_t ws_bytes,
+                       void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !topk_ids || !expert_counts || !expert_offsets || !row_token || !slot_row || !x_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = permute_ws_bytes(d);
+  if (d.N > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_permute(d, x, topk_ids, expert_counts, expert_offsets, row_token,
+                                   slot_row, x_perm, ws, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_ffn(const moe_problem* p, const uint16_t* x_perm,
+                           const int32_t* expert_offsets, const uint16_t* w_gate,
+                           const uint16_t* w_up, const uint16_t* w_down, uint16_t* out_perm,
+                           uint16_t* h, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !w_gate || !w_up || !w_down || !out_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(out_perm) || (h && !aligned16(h)))
+    return MOE_ERR_UNSUPPORTED;
+  const size_t need = h ? 0 : ffn_ws_bytes(d);
+  if (d.N > 0 && need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_grouped_ffn(d, x_perm, expert_offsets, w_gate, w_up, w_down, out_perm,
+                                       h, ws, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_gateup(const moe_problem* p, const uint16_t* x_perm,
+                             const int32_t* expert_offsets, const uint16_t* w_gate,
+                             const uint16_t* w_up, uint16_t* h, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !w_gate || !w_up || !h) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(h))
+    return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_gateup(d, x_perm, expert_offsets, w_gate, w_up, h,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_down(const moe_problem* p, const uint16_t* h,
+                           const int32_t* expert_offsets, const uint16_t* w_down,
+                           uint16_t* out_perm, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!h || !expert_offsets || !w_down || !out_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w_down) || !aligned16(out_perm)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_down(d, h, expert_offsets, w_down, out_perm,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_unpermute_combine(const moe_problem* p, const uint16_t* out_perm,
+                                 const int32_t* slot_row, const float* topk_weights,
+                                 uint16_t* y, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!out_perm || !slot_row || !topk_weights || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(out_perm) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_combine(d, out_perm, slot_row, topk_weights, y,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_router,
+                       const float* expert_bias, const uint16_t* w_gate, const uint16_t* w_up,
+                       const uint16_t* w_down, uint16_t* y, float* logits, int32_t* topk_ids,
+                       float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
+                       void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(y))
+    return MOE_ERR_UNSUPPORTED;
+  const ForwardWs L = forward_layout(d);
+  if (d.N > 0 && (!ws || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  char* base = static_cast<char*>(ws);
+  if (!logits) logits = reinterpret_cast<float*>(base + L.logits);
+  if (!topk_ids) topk_ids = reinterpret_cast<int32_t*>(base + L.ids);
+  if (!topk_weights) topk_weights = reinterpret_cast<float*>(base + L.weights);
+  if (!expert_counts) expert_counts = reinterpret_cast<int32_t*>(base + L.counts);
+  if (!expert_offsets) expert_offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* row_token = reinterpret_cast<int32_t*>(base + L.row_token);
+  int32_t* slot_row = reinterpret_cast<int32_t*>(base + L.slot_row);
+  uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);
+  uint16_t* out_perm = reinterpret_cast<uint16_t*>(base + L.out_perm);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(launch_router_gemm(d, x, w_router, logits, s));
+  if (st != MOE_OK) return st;
+  st = hip_status(launch_topk(d, logits, expert_bias, topk_ids, topk_weights, s));
+  if (st != MOE_OK) return st;
+  st = hip_status(launch_permute(d, x, topk_ids, expert_counts, expert_offsets, row_token,
+                                 slot_row, x_perm, base + L.perm, s));
+  if (st != MOE_OK) return st;
+  st = hip_status(launch_grouped_ffn(d, x_perm, expert_offsets, w_gate, w_up, w_down, out_perm,
+                                     nullptr, base + L.ffn, s));
+  if (st != MOE_OK) return st;
+  return hip_status(launch_combine(d, out_perm, slot_row, topk_weights, y, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+"""GPU parity: every ABI call against the CPU oracle on seeded inputs.
+
+Bars: routing ids, counts, offsets and the permutation bit-exact (selection
+compared on identical fp32 logits); x_perm bit-exact; logits within the fp32
+dot-product error bound; router weights within 1e-6; h, out_perm and y within
+max|d| <= 1e-2 * max|ref| and per-element rtol 2e-2 (bf16 storage, fp32
+accumulation against the oracle's float64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+from gpu_layer import (DEV, Layer, assert_fp_close, bits, check_permutation,  # noqa: E402
+                       check_routing, np_, sample_tokens, check_sampled_outputs)
+import mixture_experts_layer_level_amd as moe  # noqa: E402
+
+C = ms.MoEConfig
+SMALL = {
+    "tiny": ms.CONFIGS["tiny"],
+    # ragged: N not a tile multiple, F = 192 leaves a half-empty column tile
+    "ragged": C("ragged", N=333, D=320, E=6, K=2, F=192, gating="softmax", seed=101),
+    # small-row tiles (about 6 rows per expert), sigmoid gating
+    "decode_like": C("decode_like", N=50, D=128, E=32, K=4, F=256, gating="sigmoid", seed=102),
+    # two experts of about 350 rows: two row tiles each, the second ragged
+    "two_big_experts": C("two_big_experts", N=700, D=256, E=2, K=1, F=128, gating="softmax",
+                         seed=103),
+    "single_expert": C("single_expert", N=300, D=192, E=1, K=1, F=128, gating="softmax", seed=104),
+    "k_equals_e": C("k_equals_e", N=40, D=128, E=4, K=4, F=64, gating="sigmoid", seed=105),
+    # strong Zipf bias: several experts receive no token at all
+    "empty_experts": C("empty_experts", N=90, D=128, E=16, K=2, F=128, gating="softmax",
+                       seed=106, zipf_s=1.2, zipf_alpha=4.0),
+    "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
+                zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
+    "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,
+                           gating="softmax", seed=108, zipf_s=1.2, zipf_alpha=1.0,
+                           capacity=(1, 2)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_staged_path_small(name):
+    cfg = SMALL[name]
+    padded = cfg.capacity is not None
+    print(f"[staged] {name} N={cfg.N} D={cfg.D} E={cfg.E} K={cfg.K} F={cfg.F}", flush=True)
+    L = Layer(cfg, padded=padded)
+    L.staged()
+    check_routing(L)
+    offsets, row_token, slot_row = check_permutation(L)
+    if name == "empty_experts":
+        assert (np_(L.counts) == 0).any()
+    xg = bits(L.x)
+    assert np.array_equal(bits(L.x_perm), O.gather_rows(xg, row_token)), "x_perm"
+    # FFN on the GPU's own (bit-exact) x_perm and offsets
+    wg, wu, wd = bits(L.w_gate), bits(L.w_up), bits(L.w_down)
+    h_ref, out_ref = O.expert_ffn(bits(L.x_perm), offsets, wg, wu, wd)
+    covered = np.zeros(L.R, dtype=bool)
+    for e in range(cfg.E):
+        covered[offsets[e]:offsets[e + 1]] = True
+    assert_fp_close(O.bf16_to_f64(bits(L.h))[covered], h_ref[covered], "h")
+    out_gpu = O.bf16_to_f64(bits(L.out_perm))
+    assert_fp_close(out_gpu[covered], out_ref[covered], "out_perm")
+    if padded:
+        assert np.all(out_gpu[row_token < 0] == 0), "padding rows of out_perm must be zero"
+    # combine on the GPU's own out_perm
+    y_ref = O.combine(out_gpu, slot_row, np_(L.w))
+    y = O.bf16_to_f64(bits(L.y))
+    assert_fp_close(y, y_ref, "y (combine)")
+    assert np.mean(y == y_ref) > 0.97
+    # whole layer against the oracle (selection on the same fp32 logits)
+    x_bits, wr, bias = L.host_inputs()
+    ref = O.forward(x_bits, wr, bias, wg, wu, wd, cfg.K, cfg.gating,
+                    cap=(L.cap if padded else None), logits=np_(L.logits))
+    assert_fp_close(y, ref["y"], "y (layer)")
+    # moe_forward runs the same kernels: bit-identical to the staged calls
+    y2 = torch.empty_like(L.y)
+    L.forward(y2)
+    assert torch.equal(y2.view(torch.int16), L.y.view(torch.int16))
+
+
+@pytest.mark.parametrize("E,K,kind", [(3, 1, "ties"), (8, 2, "ties"), (64, 8, "zeros_nan"),
+                                      (256, 8, "random"), (1000, 5, "ties"), (128, 64, "random")])
+@pytest.mark.parametrize("gating", ["softmax", "sigmoid"])
+def test_route_on_given_logits(E, K, kind, gating):
+    """moe_route with x = NULL: selection and weights on caller-given logits."""
+    rng = np.random.default_rng(E * 131 + K)
+    N = 777
+    lg = rng.standard_normal((N, E)).astype(np.float32)
+    if kind == "ties":
+        lg = (np.round(lg * 2) / 2).astype(np.float32)
+    elif kind == "zeros_nan":
+        lg = np.round(lg).astype(np.float32)
+        lg[rng.random((N, E)) < 0.2] = -0.0
+        lg[rng.random((N, E)) < 0.05] = np.nan
+    bias = (np.round(rng.standard_normal(E) * 4) / 8).astype(np.float32)
+    p = moe.problem(N, 64, 64, E, K, gating)
+    logits = torch.from_numpy(lg).to(DEV)
+    ids = torch.empty(N, K, dtype=torch.int32, device=DEV)
+    w = torch.empty(N, K, dtype=torch.float32, device=DEV)
+    moe.route(p, None, None, torch.from_numpy(bias).to(DEV), logits, ids, w)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = O.route_from_logits(lg, bias, K, gating)
+    assert np.array_equal(np_(ids), ids_ref)
+    assert np.abs(np_(w).astype(np.float64) - w_ref).max() <= 1e-6
+
+
+@pytest.mark.parametrize("N,E,K,cap", [(1, 1, 1, None), (1000, 3, 2, None), (4097, 256, 8, None),
+                                       (333, 1024, 6, None), (2500, 64, 2, (5, 4)),
+                                       (999, 8, 3, (1, 3)), (64, 128, 8, (1, 1))])
+def test_permute_random_routing(N, E, K, cap):
+    rng = np.random.default_rng(N + E)
+    # skewed, distinct experts per token
+    p_e = rng.dirichlet(np.full(E, 0.3))
+    ids = np.stack([rng.choice(E, size=K, replace=False, p=p_e) for _ in range(N)]).astype(np.int32)
+    D = 64
+    x = torch.randn(N, D, device=DEV).to(torch.bfloat16)
+    p = moe.problem(N, D, 64, E, K, "softmax", cap)
+    R, c = moe.permuted_rows(p)
+    g = lambda *s: torch.empty(*s, dtype=torch.int32, device=DEV)
+    counts, offsets, row_token, slot_row = g(E), g(E + 1), g(R), g(N * K)
+    x_perm = torch.empty(R, D, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(moe.workspace_size(p), dtype=torch.uint8, device=DEV)
+    moe.permute(p, x, torch.from_numpy(ids).to(DEV), counts, offsets, row_token, slot_row,
+                x_perm, ws)
+    torch.cuda.synchronize()
+    ref = O.permute(ids, E, c if cap else None)
+    for got, exp, nm in zip((counts, offsets, row_token, slot_row), ref,
+                            ("counts", "offsets", "row_token", "slot_row")):
+        assert np.array_equal(np_(got), exp), nm
+    assert np.array_equal(bits(x_perm), O.gather_rows(bits(x), ref[2]))
+
+
+def test_deterministic_reruns():
+    L = Layer(SMALL["ragged"])
+    L.staged()
+    first = [t.clone() for t in (L.ids, L.slot_row, L.row_token, L.y)]
+    for _ in range(2):
+        L.staged()
+        for a, b in zip(first, (L.ids, L.slot_row, L.row_token, L.y)):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_generator_is_device_independent():
+    a = ms.normal_bf16(100003, 0.7, 99, 3, offset=12345, device=DEV).cpu()
+    b = ms.normal_bf16(100003, 0.7, 99, 3, offset=12345, device="cpu")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+FULL = [("mixtral", False), ("deepseek_v3", False), ("qwen3_decode", False),
+        ("hot_skew", False), ("hot_skew", True)]
+
+
+@pytest.mark.parametrize("name,padded", FULL, ids=[f"{n}{'_padded' if p else ''}" for n, p in FULL])
+def test_full_size(name, padded):
+    """The workloads at full size, in the launch configuration the benchmark
+    times: routing and permutation checked exhaustively, y on sampled tokens."""
+    cfg = ms.CONFIGS[name]
+    print(f"[full] {name} padded={padded}", flush=True)
+    L = Layer(cfg, padded=padded)
+    L.staged()
+    rows = sample_tokens(cfg.N, 64)
+    check_routing(L, sample_rows=rows)
+    check_permutation(L)
+    assert int(np_(L.counts).sum()) == cfg.S
+    tokens = sample_tokens(cfg.N, 12)
+    check_sampled_outputs(L, L.y, tokens)
+    y2 = torch.empty_like(L.y)
+    L.forward(y2)
+    assert torch.equal(y2.view(torch.int16), L.y.view(torch.int16))
+    if name == "hot_skew":
+        share = np_(L.counts).max() / cfg.S
+        assert 0.2 <= share <= 0.3
+    del L
+    torch.cuda.empty_cache()

@@ -20,6 +20,26 @@ import time
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_level_amd", "csrc", "grouped_gemm.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate/up launch from the committed rocprofv3 --pmc summary of
+    this workload, or None when there is none or the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path, encoding="utf-8"):
+        if line.startswith("traffic: "):
+            rec = json.loads(line[len("traffic: "):])
+    if rec is None:
+        return None
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    return rec["bytes"] if rec.get("source_sha256") == sha else None
 
 
 def main():
@@ -32,7 +52,13 @@ def main():
     ap.add_argument("--padded", action="store_true", help="capacity-padded layout (hot_skew)")
     ap.add_argument("--cpu-tokens", type=int, default=192,
                     help="tokens of the CPU-oracle sample (0 = skip the CPU baseline)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, three "
+                         "times (the reference kernel for HBM byte counters), then exit")
     args = ap.parse_args()
+    if args.calib_copy_mib > 0:
+        calib_copy(args.calib_copy_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(this build has no multi-GPU path)", file=sys.stderr)
@@ -134,7 +160,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gateup_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(args.config) if not capv else None,
             "avg_ms": gateup_ms,
         },
         "cpu_baseline": None,
@@ -145,6 +171,19 @@ def main():
     if args.cpu_tokens > 0:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, N), capv)
     print(json.dumps(line), flush=True)
+
+
+def calib_copy(mib: int):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+    factor between what those counters report and the bytes actually moved."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[calib] copied {n} bytes three times", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(cfg, inp, n, capv):

@@ -21,8 +21,7 @@
 // share a weight panel hit the same L2.
 //
 // Tile: BM x BN x 64 (bf16), operands double-buffered in LDS with a 16-byte
-// XOR swizzle (chunk c of row r stored at c ^ (r & 7)) so the MFMA operand
-// reads of 32 rows at one k-offset spread over all banks.
+// XOR swizzle (see swz) so the MFMA operand reads spread over all banks.
 #include "common.h"
 
 namespace moe {
@@ -30,6 +29,13 @@ namespace {
 
 constexpr int BK = 64;           // k depth of one LDS stage (bf16)
 constexpr int CHUNKS = BK / 8;   // 16-byte chunks per tile row
+
+// LDS swizzle: chunk c of tile row r is stored at position c ^ swz(r).  A
+// 128-byte tile row covers half of gfx950's 64 four-byte banks, so two
+// consecutive rows share one 16-chunk bank window; swz(r) = (r >> 1) & 7 gives
+// the 16 rows that one MFMA operand read touches per LDS cycle 16 distinct
+// (row parity, chunk position) pairs, i.e. all 64 banks once.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 struct GemmArgs {
   const uint16_t* A;        // [rows, Kd]
@@ -64,12 +70,12 @@ __device__ __forceinline__ void stage_lstore(uint4* st, const uint4 (&ra)[NA],
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int r = lrow + i * RPP;
-    st[r * CHUNKS + (lchunk ^ (r & 7))] = ra[i];
+    st[r * CHUNKS + (lchunk ^ swz(r))] = ra[i];
   }
 #pragma unroll
   for (int i = 0; i < NB_; ++i) {
     const int r = lrow + i * RPP;
-    st[(BM + r) * CHUNKS + (lchunk ^ (r & 7))] = rb[i];
+    st[(BM + r) * CHUNKS + (lchunk ^ swz(r))] = rb[i];
   }
 }
 
@@ -84,12 +90,12 @@ __device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[MB][NB], const uint4*
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int r = wm * TM + mb * 32 + (lane & 31);
-      af[mb] = __builtin_bit_cast(bf16x8_t, st[r * CHUNKS + (kc ^ (r & 7))]);
+      af[mb] = __builtin_bit_cast(bf16x8_t, st[r * CHUNKS + (kc ^ swz(r))]);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int r = wn * TN + nb * 32 + (lane & 31);
-      bfr[nb] = __builtin_bit_cast(bf16x8_t, st[(BM + r) * CHUNKS + (kc ^ (r & 7))]);
+      bfr[nb] = __builtin_bit_cast(bf16x8_t, st[(BM + r) * CHUNKS + (kc ^ swz(r))]);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)

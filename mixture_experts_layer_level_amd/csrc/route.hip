@@ -11,77 +11,169 @@ namespace moe {
 namespace {
 
 // ------------------------------------------------------------------ router GEMM
-// fp32 FMA tiles of 64 tokens x 64 experts, 32-deep K steps staged through LDS.
-// Thread (ty, tx) owns tokens ty + 16*i and experts tx + 16*j (i, j < 4), so a
-// wave reads 4 broadcast token values and 16 consecutive expert values per k.
-constexpr int RT_TM = 64, RT_TE = 64, RT_BK = 32;
+// bf16 MFMA with an exact three-way split of the fp32 router weights.
+//
+// Every fp32 weight w is split as w = hi + mid + lo with hi = bf16(w),
+// mid = bf16(w - hi), lo = w - hi - mid; all three are exact bf16 values (a
+// 24-bit significand cut into three 8-bit pieces), so the layer's x.w is
+// the sum of 3*D exact bf16 x bf16 products, accumulated in fp32 by
+// v_mfma_f32_32x32x16_bf16.  hi products go to one accumulator and the much
+// smaller mid + lo products to another; the two are added once.  The result
+// is an fp32 sum of exact products, so it obeys the usual fp32 dot-product
+// error bound (relative to sum |x.w|), at bf16 MFMA speed instead of fp32
+// vector-FMA speed.
+//
+// Workgroup = S waves on one tile of WT tokens x WT experts; wave s takes the
+// 64-deep k blocks s, s+S, s+2S, ...  Operands go straight from global memory
+// into MFMA registers (lane l reads a contiguous run of row l % 32), so there
+// is no LDS staging; the S partial tiles are summed through LDS in
+// wave order, so the result does not depend on scheduling.
 
-__global__ void __launch_bounds__(256)
-router_gemm_kernel(int64_t N, int D, int E, const uint16_t* __restrict__ x,
-                   const float* __restrict__ w, float* __restrict__ logits) {
-  __shared__ float xs[RT_BK][RT_TM + 4];
-  __shared__ float ws[RT_BK][RT_TE + 4];
-  const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
-  const int64_t n0 = (int64_t)blockIdx.y * RT_TM;
-  const int e0 = blockIdx.x * RT_TE;
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t rne_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
 
-  // loader mapping: 64 rows x 4 chunks of 8 elements
-  const int lrow = tid >> 2, lchunk = tid & 3;
-  const int64_t xrow = min<int64_t>(n0 + lrow, N - 1);
-  const int wrow = min(e0 + lrow, E - 1);
-  const uint16_t* xp = x + xrow * D + lchunk * 8;
-  const float* wp = w + (int64_t)wrow * D + lchunk * 8;
-
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-
-  for (int k0 = 0; k0 < D; k0 += RT_BK) {
-    uint4 xv = *reinterpret_cast<const uint4*>(xp + k0);
-    float4 w0 = *reinterpret_cast<const float4*>(wp + k0);
-    float4 w1 = *reinterpret_cast<const float4*>(wp + k0 + 4);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xs[lchunk * 8 + 2 * i][lrow] = bf16_bits_to_f32(xw[i] & 0xffffu);
-      xs[lchunk * 8 + 2 * i + 1][lrow] = bf16_bits_to_f32(xw[i] >> 16);
-    }
-    ws[lchunk * 8 + 0][lrow] = w0.x;
-    ws[lchunk * 8 + 1][lrow] = w0.y;
-    ws[lchunk * 8 + 2][lrow] = w0.z;
-    ws[lchunk * 8 + 3][lrow] = w0.w;
-    ws[lchunk * 8 + 4][lrow] = w1.x;
-    ws[lchunk * 8 + 5][lrow] = w1.y;
-    ws[lchunk * 8 + 6][lrow] = w1.z;
-    ws[lchunk * 8 + 7][lrow] = w1.w;
-    __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < RT_BK; ++k) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[k][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[k][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
+// Split 8 fp32 weights into the hi / mid / lo bf16 vectors.
+__device__ __forceinline__ void split3(const float4& a, const float4& b, bf16x8_t& hi,
+                                       bf16x8_t& mid, bf16x8_t& lo) {
+  const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], m[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t n = n0 + ty + 16 * i;
-    if (n >= N) continue;
+    uint32_t hb[2], mb[2], lb[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx + 16 * j;
-      if (e < E) logits[n * E + e] = acc[i][j];
+    for (int j = 0; j < 2; ++j) {
+      const float v = w[2 * i + j];
+      hb[j] = rne_bf16(v);
+      const float r1 = v - __uint_as_float(hb[j] << 16);      // exact
+      mb[j] = rne_bf16(r1);
+      const float r2 = r1 - __uint_as_float(mb[j] << 16);     // exact, fits bf16
+      lb[j] = __float_as_uint(r2) >> 16;
+    }
+    h[i] = hb[0] | (hb[1] << 16);
+    m[i] = mb[0] | (mb[1] << 16);
+    l[i] = lb[0] | (lb[1] << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+  mid = __builtin_bit_cast(bf16x8_t, make_uint4(m[0], m[1], m[2], m[3]));
+  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// Launch bounds follow the largest workgroup the launcher uses for each tile
+// size (4 waves at 64x64, 8 at 32x32), which sets the register budget.
+template <int WT>
+__global__ void __launch_bounds__(WT == 64 ? 256 : 512)
+router_mfma_kernel(int64_t N, int D, int E, int vec4, const uint16_t* __restrict__ x,
+                   const float* __restrict__ w, float* __restrict__ logits) {
+  constexpr int TB = WT / 32;                   // 32-row blocks per tile side
+  constexpr int LD = WT + 4;                    // LDS row stride (floats)
+  extern __shared__ float red[];                // [S-1][WT][LD] partial tiles
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int S = blockDim.x >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * WT;
+  const int e0 = blockIdx.y * WT;
+  const int r = lane & 31, kh = lane >> 5;
+
+  // k order inside a 64-deep block: MFMA step ks takes, in lane half kh,
+  // k = 32*kh + 8*ks .. +7.  Both operands use the same order, so the MFMA
+  // still pairs equal k; a lane then reads one contiguous 32-element run of
+  // its row per block (64 bytes of x, one 128-byte line of w).
+  const uint16_t* xr[TB];
+  const float* wr[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    xr[b] = x + min<int64_t>(n0 + b * 32 + r, N - 1) * D + kh * 32;
+    wr[b] = w + (int64_t)min(e0 + b * 32 + r, E - 1) * D + kh * 32;
+  }
+  f32x16_t acc_hi[TB][TB], acc_lo[TB][TB];      // [expert block][token block]
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < TB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc_hi[i][j][v] = acc_lo[i][j][v] = 0.f;
+
+  const int nkb = D / 64;
+  for (int kb = wave; kb < nkb; kb += S) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k = kb * 64 + ks * 8;
+      bf16x8_t xa[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+        xa[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr[b] + k));
+#pragma unroll
+      for (int i = 0; i < TB; ++i) {
+        const float4 wa = *reinterpret_cast<const float4*>(wr[i] + k);
+        const float4 wb = *reinterpret_cast<const float4*>(wr[i] + k + 4);
+        bf16x8_t hi, mid, lo;
+        split3(wa, wb, hi, mid, lo);
+#pragma unroll
+        for (int j = 0; j < TB; ++j) {
+          acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, xa[j], acc_hi[i][j], 0, 0, 0);
+          acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, xa[j], acc_lo[i][j], 0, 0, 0);
+          acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, xa[j], acc_lo[i][j], 0, 0, 0);
+        }
+      }
     }
   }
+  // Block (i, j): lane l, register v holds expert 8*(v/4) + 4*(l/32) + v%4 of
+  // expert block i and token l%32 of token block j; four consecutive
+  // registers are four consecutive experts.  Waves 1..S-1 leave their partial
+  // tiles in LDS; wave 0 adds them to its own in wave order and stores.
+  if (wave > 0) {
+    float* mine = red + (size_t)(wave - 1) * WT * LD;
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int j = 0; j < TB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float4 v;
+          v.x = acc_hi[i][j][4 * g + 0] + acc_lo[i][j][4 * g + 0];
+          v.y = acc_hi[i][j][4 * g + 1] + acc_lo[i][j][4 * g + 1];
+          v.z = acc_hi[i][j][4 * g + 2] + acc_lo[i][j][4 * g + 2];
+          v.w = acc_hi[i][j][4 * g + 3] + acc_lo[i][j][4 * g + 3];
+          *reinterpret_cast<float4*>(mine + (j * 32 + r) * LD + i * 32 + 8 * g + 4 * kh) = v;
+        }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int64_t n = n0 + j * 32 + r;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int el = i * 32 + 8 * g + 4 * kh;
+        float4 v;
+        v.x = acc_hi[i][j][4 * g + 0] + acc_lo[i][j][4 * g + 0];
+        v.y = acc_hi[i][j][4 * g + 1] + acc_lo[i][j][4 * g + 1];
+        v.z = acc_hi[i][j][4 * g + 2] + acc_lo[i][j][4 * g + 2];
+        v.w = acc_hi[i][j][4 * g + 3] + acc_lo[i][j][4 * g + 3];
+        for (int q = 0; q + 1 < S; ++q) {
+          const float4 o = *reinterpret_cast<const float4*>(red + ((size_t)q * WT + j * 32 + r) * LD + el);
+          v.x += o.x;
+          v.y += o.y;
+          v.z += o.z;
+          v.w += o.w;
+        }
+        if (n >= N) continue;
+        float* dst = logits + n * E + e0 + el;
+        if (vec4 && e0 + el + 3 < E) {
+          *reinterpret_cast<float4*>(dst) = v;
+        } else {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+          for (int c = 0; c < 4; ++c)
+            if (e0 + el + c < E) dst[c] = vv[c];
+        }
+      }
+    }
 }
 
 // ------------------------------------------------------------------ top-K
@@ -163,8 +255,30 @@ topk_kernel(int64_t N, int E, int K, int gating, const float* __restrict__ logit
 
 hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, float* logits,
                               hipStream_t s) {
-  dim3 grid((d.E + RT_TE - 1) / RT_TE, (unsigned)((d.N + RT_TM - 1) / RT_TM));
-  hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, s, d.N, d.D, d.E, x, w, logits);
+  // 64x64 tiles with 4 waves when they alone give the chip at least one
+  // workgroup per CU; otherwise 32x32 tiles and as many waves per tile
+  // (up to 8, at most one per 64-deep k block) as bring the grid to about
+  // 512 waves.  LDS: (S-1) partial tiles, at most 52 KB.
+  const int nkb = d.D / 64;
+  // 16-byte stores of four logits when every row start is 16-byte aligned
+  const int vec4 = (d.E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0);
+  const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
+  if (t64 >= device_cu_count()) {
+    const int S = nkb < 4 ? nkb : 4;
+    dim3 grid((unsigned)((d.N + 63) / 64), (unsigned)((d.E + 63) / 64));
+    hipLaunchKernelGGL(router_mfma_kernel<64>, grid, dim3(64 * S),
+                       (S - 1) * 64 * 68 * sizeof(float), s, d.N, d.D, d.E, vec4, x, w,
+                       logits);
+    return hipGetLastError();
+  }
+  const int64_t t32 = ((d.N + 31) / 32) * ((d.E + 31) / 32);
+  int S = (int)((512 + t32 - 1) / t32);
+  if (S > 8) S = 8;
+  if (S > nkb) S = nkb;
+  if (S < 1) S = 1;
+  dim3 grid((unsigned)((d.N + 31) / 32), (unsigned)((d.E + 31) / 32));
+  hipLaunchKernelGGL(router_mfma_kernel<32>, grid, dim3(64 * S), (S - 1) * 32 * 36 * sizeof(float), s,
+                     d.N, d.D, d.E, vec4, x, w, logits);
   return hipGetLastError();
 }
 

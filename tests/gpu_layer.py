@@ -39,16 +39,30 @@ def assert_fp_close(got, ref, what: str):
 
 
 def assert_logits_bound(gpu_logits, x_bits, w_router, rows=None):
-    """|gpu - exact| <= gamma_D * sum_d |x_d w_d| (fp32 dot-product error bound)."""
+    """Router logits against the exact dot products, within the fp32
+    summation bound.
+
+    The kernel evaluates x.w as an fp32 sum of exact products: each fp32
+    weight is cut exactly into three bf16 pieces (|pieces| sum to at most
+    (1 + 2**-7)|w|) and every bf16 x bf16 product is exact in fp32.  Each
+    product passes through at most 2D + 8 fp32 additions, so
+    |gpu - exact| <= gamma_(2D+8) * (1 + 2**-7) * sum_d |x_d w_d|,
+    gamma_n = n u / (1 - n u), u = 2**-24.
+    """
     x = O.bf16_to_f64(x_bits if rows is None else x_bits[rows])
     w = np.asarray(w_router, dtype=np.float64)
     exact = x @ w.T
     mag = np.abs(x) @ np.abs(w).T
     D = x.shape[1]
     u = 2.0 ** -24
-    gamma = D * u / (1 - D * u)
+    n = 2 * D + 8
+    gamma = n * u / (1 - n * u)
     g = np.asarray(gpu_logits if rows is None else gpu_logits[rows], dtype=np.float64)
-    assert np.all(np.abs(g - exact) <= gamma * mag + 1e-30)
+    err = np.abs(g - exact)
+    assert np.all(err <= gamma * (1 + 2.0 ** -7) * mag + 1e-30)
+    # and the observed error is that of a well-conditioned fp32 sum, far
+    # inside the worst case
+    assert err.max() <= 64 * u * max(1.0, float(np.abs(exact).max())) * np.sqrt(D)
 
 
 class Layer:

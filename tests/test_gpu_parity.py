@@ -34,6 +34,11 @@ SMALL = {
     # strong Zipf bias: several experts receive no token at all
     "empty_experts": C("empty_experts", N=90, D=128, E=16, K=2, F=128, gating="softmax",
                        seed=106, zipf_s=1.2, zipf_alpha=4.0),
+    # about 550 rows per expert: 256 x 256 ring tiles, ragged last row tile,
+    # F = 192 leaves half of the second h column tile empty
+    "large_tiles": C("large_tiles", N=1100, D=320, E=2, K=1, F=192, gating="softmax", seed=109),
+    # about 240 rows per expert: 128 x 256 ring tiles
+    "mid_tiles": C("mid_tiles", N=960, D=384, E=8, K=2, F=320, gating="sigmoid", seed=110),
     "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
                 zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
     "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,

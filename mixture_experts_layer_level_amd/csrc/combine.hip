@@ -8,54 +8,79 @@
 // Each work item is one 16-byte chunk (8 bf16) of one token's output row: it
 // gathers that chunk from the token's K expert rows, accumulates w * value in
 // fp32 in k order and writes the bf16 result.  HBM-bound: every kept out_perm
-// row is read once and every y row written once.
+// row is read once and every y row written once.  Grid-stride over the
+// N * D / 8 items, blocks of 256.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
 namespace {
 
+// y chunk c (8 bf16) of token n: the K slot rows and weights of the token are
+// read first (the same addresses for every thread of the token), then up to 8
+// gathers are in flight before the first is used; the sum runs in k order.
+__device__ __forceinline__ void combine_chunk(int64_t n, int c, int D, int K,
+                                              const uint16_t* __restrict__ out_perm,
+                                              const int32_t* __restrict__ slot_row,
+                                              const float* __restrict__ w,
+                                              uint16_t* __restrict__ y) {
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    int32_t r[8];
+    float wk[8];
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool in = k0 + j < K;
+      r[j] = in ? slot_row[n * K + k0 + j] : -1;
+      wk[j] = in ? w[n * K + k0 + j] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = r[j] >= 0 ? reinterpret_cast<const uint4*>(out_perm + (int64_t)r[j] * D)[c]
+                       : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (r[j] < 0) continue;
+      const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __builtin_fmaf(wk[j], bf16_bits_to_f32(u[i] & 0xffffu), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(wk[j], bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
+      }
+    }
+  }
+  uint4 o;
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
+  reinterpret_cast<uint4*>(y + n * D)[c] = o;
+}
+
+// One thread per (token, 16-byte chunk), grid-stride.
 __global__ void __launch_bounds__(256)
-combine_kernel(int64_t N, int D, int K, int tpb, const uint16_t* __restrict__ out_perm,
+combine_kernel(int64_t N, int D, int K, const uint16_t* __restrict__ out_perm,
                const int32_t* __restrict__ slot_row, const float* __restrict__ w,
                uint16_t* __restrict__ y) {
   const int cpr = D / 8;
-  const int64_t t0 = (int64_t)blockIdx.x * tpb;
-  for (int wi = threadIdx.x; wi < tpb * cpr; wi += 256) {
-    const int64_t n = t0 + wi / cpr;
-    if (n >= N) break;
-    const int c = wi % cpr;
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int32_t r = slot_row[n * K + k];
-      if (r < 0) continue;
-      const float wk = w[n * K + k];
-      const uint4 v = reinterpret_cast<const uint4*>(out_perm + (int64_t)r * D)[c];
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = __builtin_fmaf(wk, bf16_bits_to_f32(u[i] & 0xffffu), acc[2 * i]);
-        acc[2 * i + 1] = __builtin_fmaf(wk, bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
-      }
-    }
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    reinterpret_cast<uint4*>(y + n * D)[c] = o;
-  }
+  const int64_t items = N * cpr;
+  for (int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x; item < items;
+       item += (int64_t)gridDim.x * 256)
+    combine_chunk(item / cpr, (int)(item % cpr), D, K, out_perm, slot_row, w, y);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const Dims& d, const uint16_t* out_perm, const int32_t* slot_row,
                           const float* weights, uint16_t* y, hipStream_t s) {
-  const int cpr = d.D / 8;
-  const int tpb = cpr >= 2048 ? 1 : 2048 / cpr;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((d.N + tpb - 1) / tpb)), dim3(256), 0, s,
-                     d.N, d.D, d.K, tpb, out_perm, slot_row, weights, y);
+  const int64_t items = d.N * (d.D / 8);
+  const int64_t blocks = std::min<int64_t>((items + 255) / 256, 1 << 20);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, d.N,
+                     d.D, d.K, out_perm, slot_row, weights, y);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 // (ybb.press) 2.2 runs over destination GPUs.
 //
 // Kernels (one stream, no host synchronisation):
+//   0. small : for at most 1024 slots, steps 1-3 in one workgroup.
 //   1. count : per-workgroup expert histogram of a chunk of slots.
 //   2. scan  : per-expert exclusive prefix over workgroups, expert totals and
 //              the segment offsets.
@@ -17,6 +18,8 @@
 //   4. copy  : each token row is read once and written to its K rows.
 //   5. pad   : (padded layout) row_token = -1 and zero rows past each
 //              expert's kept slots.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -120,21 +123,88 @@ perm_rank_kernel(int64_t S, int E, int K, int nbits, int64_t cap, int padded,
   }
 }
 
-// Each token row is read once (16-byte chunks) and written to its kept rows.
+// One thread per (token, 16-byte chunk), grid-stride: the chunk is read
+// once and written to each kept row of the token (up to 8 slot rows are
+// loaded before the stores).
 __global__ void __launch_bounds__(256)
-perm_copy_kernel(int64_t N, int D, int K, int tpb, const uint16_t* __restrict__ x,
+perm_copy_kernel(int64_t N, int D, int K, const uint16_t* __restrict__ x,
                  const int32_t* __restrict__ slot_row, uint16_t* __restrict__ x_perm) {
   const int cpr = D / 8;
-  const int64_t t0 = (int64_t)blockIdx.x * tpb;
-  for (int w = threadIdx.x; w < tpb * cpr; w += 256) {
-    const int64_t n = t0 + w / cpr;
-    if (n >= N) break;
-    const int c = w % cpr;
+  const int64_t items = N * cpr;
+  for (int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x; item < items;
+       item += (int64_t)gridDim.x * 256) {
+    const int64_t n = item / cpr;
+    const int c = (int)(item % cpr);
     const uint4 v = reinterpret_cast<const uint4*>(x + n * D)[c];
-    for (int k = 0; k < K; ++k) {
-      const int32_t r = slot_row[n * K + k];
-      if (r >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)r * D)[c] = v;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      int32_t r[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = k0 + j < K ? slot_row[n * K + k0 + j] : -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r[j] >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)r[j] * D)[c] = v;
     }
+  }
+}
+
+// Small problems (N*K <= 1024 slots): histogram, scan and stable rank in one
+// workgroup of 16 waves; wave w ranks slots [64w, 64w + 64).  Same results as
+// count + scan + rank.
+constexpr int kSmallSlots = 1024;
+__global__ void __launch_bounds__(1024)
+perm_small_kernel(int64_t S, int E, int K, int nbits, int64_t cap, int padded,
+                  const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+                  int32_t* __restrict__ offsets, int32_t* __restrict__ slot_row,
+                  int32_t* __restrict__ row_token) {
+  __shared__ int32_t wcnt[16 * 1024];   // [wave][expert]: count, then exclusive prefix over waves
+  __shared__ int32_t sh[1024];          // per-expert segment sizes, then inclusive prefix
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 16 * E; i += 1024) wcnt[i] = 0;
+  __syncthreads();
+  const int64_t slot = tid;
+  int id = slot < S ? ids[slot] : -1;
+  const bool valid = valid_id(id, E);
+  if (!valid) id = 0;
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const int bit = (id >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(peers & lt_mask);
+  if (valid && lane == __ffsll((unsigned long long)peers) - 1) wcnt[wave * E + id] = __popcll(peers);
+  __syncthreads();
+  if (tid < E) {
+    int32_t run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int32_t t = wcnt[w * E + tid];
+      wcnt[w * E + tid] = run;
+      run += t;
+    }
+    counts[tid] = run;
+    sh[tid] = padded ? (int32_t)cap : run;
+  } else {
+    sh[tid] = 0;
+  }
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) offsets[tid + 1] = sh[tid];
+  if (tid == 0) offsets[0] = 0;
+  if (slot < S) {
+    int32_t row = -1;
+    if (valid) {
+      const int64_t pos = (int64_t)wcnt[wave * E + id] + rank;
+      if (!padded) row = (id ? sh[id - 1] : 0) + (int32_t)pos;
+      else if (pos < cap) row = (int32_t)(id * cap + pos);
+    }
+    slot_row[slot] = row;
+    if (row >= 0) row_token[row] = (int32_t)(slot / K);
   }
 }
 
@@ -167,17 +237,22 @@ hipError_t launch_permute(const Dims& d, const uint16_t* x, const int32_t* ids, 
   int32_t* table = static_cast<int32_t*>(ws);
   int nbits = 0;
   while ((1 << nbits) < d.E) ++nbits;
-  hipLaunchKernelGGL(perm_count_kernel, dim3(nb), dim3(256), d.E * sizeof(int32_t), s, d.S, d.E,
-                     ids, table);
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, nb, d.E, d.cap, (int)d.padded,
-                     table, counts, offsets);
-  hipLaunchKernelGGL(perm_rank_kernel, dim3(nb), dim3(256), 4 * d.E * sizeof(int32_t), s, d.S,
-                     d.E, d.K, nbits, d.cap, (int)d.padded, ids, table, offsets, slot_row,
-                     row_token);
-  const int cpr = d.D / 8;
-  const int tpb = cpr >= 2048 ? 1 : 2048 / cpr;
-  hipLaunchKernelGGL(perm_copy_kernel, dim3((unsigned)((d.N + tpb - 1) / tpb)), dim3(256), 0, s,
-                     d.N, d.D, d.K, tpb, x, slot_row, x_perm);
+  if (d.S <= kSmallSlots) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, s, d.S, d.E, d.K, nbits, d.cap,
+                       (int)d.padded, ids, counts, offsets, slot_row, row_token);
+  } else {
+    hipLaunchKernelGGL(perm_count_kernel, dim3(nb), dim3(256), d.E * sizeof(int32_t), s, d.S,
+                       d.E, ids, table);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, nb, d.E, d.cap,
+                       (int)d.padded, table, counts, offsets);
+    hipLaunchKernelGGL(perm_rank_kernel, dim3(nb), dim3(256), 4 * d.E * sizeof(int32_t), s, d.S,
+                       d.E, d.K, nbits, d.cap, (int)d.padded, ids, table, offsets, slot_row,
+                       row_token);
+  }
+  const int64_t items = d.N * (d.D / 8);
+  const int64_t blocks = std::min<int64_t>((items + 255) / 256, 1 << 20);
+  hipLaunchKernelGGL(perm_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, d.N, d.D, d.K, x,
+                     slot_row, x_perm);
   if (d.padded)
     hipLaunchKernelGGL(perm_pad_kernel, dim3(d.E), dim3(256), 0, s, d.E, d.cap, d.D, counts,
                        row_token, x_perm);

@@ -97,28 +97,62 @@ router_mfma_kernel(int64_t N, int D, int E, int vec4, const uint16_t* __restrict
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc_hi[i][j][v] = acc_lo[i][j][v] = 0.f;
 
-  const int nkb = D / 64;
-  for (int kb = wave; kb < nkb; kb += S) {
+  // One 64-deep k block of raw operands.  With 32x32 tiles the next block is
+  // loaded while the MFMAs of the current one run (two register sets,
+  // alternating).
+  struct Blk {
+    uint4 x[4][TB];
+    float4 wa[4][TB], wb[4][TB];
+  };
+  auto load = [&](Blk& b, int kb) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int k = kb * 64 + ks * 8;
-      bf16x8_t xa[TB];
 #pragma unroll
-      for (int b = 0; b < TB; ++b)
-        xa[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr[b] + k));
+      for (int t = 0; t < TB; ++t) {
+        b.x[ks][t] = *reinterpret_cast<const uint4*>(xr[t] + k);
+        b.wa[ks][t] = *reinterpret_cast<const float4*>(wr[t] + k);
+        b.wb[ks][t] = *reinterpret_cast<const float4*>(wr[t] + k + 4);
+      }
+    }
+  };
+  auto compute = [&](const Blk& b) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
-        const float4 wa = *reinterpret_cast<const float4*>(wr[i] + k);
-        const float4 wb = *reinterpret_cast<const float4*>(wr[i] + k + 4);
         bf16x8_t hi, mid, lo;
-        split3(wa, wb, hi, mid, lo);
+        split3(b.wa[ks][i], b.wb[ks][i], hi, mid, lo);
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
-          acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, xa[j], acc_hi[i][j], 0, 0, 0);
-          acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, xa[j], acc_lo[i][j], 0, 0, 0);
-          acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, xa[j], acc_lo[i][j], 0, 0, 0);
+          const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, b.x[ks][j]);
+          acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, xa, acc_hi[i][j], 0, 0, 0);
+          acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, xa, acc_lo[i][j], 0, 0, 0);
+          acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, xa, acc_lo[i][j], 0, 0, 0);
         }
       }
+  };
+  const int nkb = D / 64;
+  if constexpr (WT == 64) {
+    // 64x64 tiles are issued when the grid already fills the chip: one
+    // register set, no look-ahead (two sets would spill).
+    Blk b0;
+    for (int kb = wave; kb < nkb; kb += S) {
+      load(b0, kb);
+      compute(b0);
+    }
+  } else {
+    Blk b0, b1;
+    int kb = wave;
+    if (kb < nkb) load(b0, kb);
+    while (kb < nkb) {
+      if (kb + S < nkb) load(b1, kb + S);
+      compute(b0);
+      kb += S;
+      if (kb >= nkb) break;
+      if (kb + S < nkb) load(b0, kb + S);
+      compute(b1);
+      kb += S;
     }
   }
   // Block (i, j): lane l, register v holds expert 8*(v/4) + 4*(l/32) + v%4 of

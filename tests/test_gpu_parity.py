@@ -39,6 +39,8 @@ SMALL = {
     "large_tiles": C("large_tiles", N=1100, D=320, E=2, K=1, F=192, gating="softmax", seed=109),
     # about 240 rows per expert: 128 x 256 ring tiles
     "mid_tiles": C("mid_tiles", N=960, D=384, E=8, K=2, F=320, gating="sigmoid", seed=110),
+    # K = 12: the combine and copy kernels take the slots of a token in groups of 8
+    "wide_topk": C("wide_topk", N=80, D=128, E=32, K=12, F=128, gating="softmax", seed=111),
     "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
                 zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
     "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,
@@ -115,7 +117,11 @@ def test_route_on_given_logits(E, K, kind, gating):
 
 @pytest.mark.parametrize("N,E,K,cap", [(1, 1, 1, None), (1000, 3, 2, None), (4097, 256, 8, None),
                                        (333, 1024, 6, None), (2500, 64, 2, (5, 4)),
-                                       (999, 8, 3, (1, 3)), (64, 128, 8, (1, 1))])
+                                       (999, 8, 3, (1, 3)), (64, 128, 8, (1, 1)),
+                                       # at and just past the one-workgroup limit of 1024 slots
+                                       (128, 64, 8, None), (129, 64, 8, None),
+                                       (100, 1024, 10, None), (512, 2, 2, (1, 2)),
+                                       (60, 16, 12, None)])
 def test_permute_random_routing(N, E, K, cap):
     rng = np.random.default_rng(N + E)
     # skewed, distinct experts per token

@@ -104,13 +104,15 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         moe.expert_down(p, h, offsets, wd, out_perm, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
         moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
            for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -122,16 +124,31 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    gateup_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    gateup_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / args.steps
+    down_ms = sum(b.elapsed_time(c) for _, b, c in evs) / args.steps
 
     counts_h = counts.cpu().numpy().astype(np.int64)
     kept = int(np.minimum(counts_h, capv).sum()) if capv else cfg.S
     flops = 2.0 * N * D * E + 6.0 * D * F * kept        # router + SwiGLU FFN, kept slots
-    gateup_flops = 4.0 * D * F * kept
     tflops = flops / (ms_step * 1e-3) / 1e12
-    gateup_tflops = gateup_flops / (gateup_ms * 1e-3) / 1e12
     touched = int((counts_h > 0).sum())
     weight_bytes = 3.0 * touched * F * D * 2
+    # gate/up grouped GEMM (the dominant kernel): algorithmic work per launch
+    gu_flops = 4.0 * D * F * kept
+    gu_bytes = 2.0 * touched * F * D * 2 + kept * D * 2 + kept * F * 2   # Wg+Wu, x_perm, h
+    t_mfma = gu_flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = gu_bytes / (PEAK_HBM_GBPS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": gu_flops / (gateup_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": gu_bytes / (gateup_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(args.config) if not capv else None
+    roof["kernel"] = "grouped gate/up GEMM + SwiGLU"
+    roof["avg_ms"] = gateup_ms
+    roof["algorithmic"] = {"flop": gu_flops, "bytes": gu_bytes}
     line = {
         "metric": "MoE-layer tokens/sec + TFLOPS (% bf16 MFMA peak) / HBM GB/s (% peak), 1 GPU",
         "value": N / (ms_step * 1e-3),
@@ -151,18 +168,12 @@ def main():
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "weight_stream_gbps": weight_bytes / (ms_step * 1e-3) / 1e9,
+        "ffn_weight_stream_gbps": weight_bytes / ((gateup_ms + down_ms) * 1e-3) / 1e9,
+        "gateup_ms": gateup_ms,
+        "down_ms": down_ms,
         "max_expert_rows": int(counts_h.max()),
         "dropped_slots": int(cfg.S - kept),
-        "roofline": {
-            "kernel": "grouped_gemm_kernel (gate/up + SwiGLU)",
-            "bound": "mfma",
-            "achieved": gateup_tflops,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": gateup_tflops / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic(args.config) if not capv else None,
-            "avg_ms": gateup_ms,
-        },
+        "roofline": roof,
         "cpu_baseline": None,
     }
     print(f"[bench] {ms_step:.3f} ms/step, gate/up {gateup_ms:.3f} ms", file=sys.stderr,

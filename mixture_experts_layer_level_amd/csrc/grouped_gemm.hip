@@ -25,8 +25,9 @@
 //     global memory into an S-stage LDS ring with LDS-DMA
 //     (global_load_lds_dwordx4), BK-deep stages, one barrier per stage.  The
 //     DMA for stage kt+S is issued right after the barrier of stage kt, when
-//     every wave has read all of stage kt; the fragments of the first k-step
-//     of stage kt+1 are read from LDS while the last MFMAs of stage kt run.
+//     every wave has read all of stage kt, behind the last MFMAs of stage kt;
+//     the fragments of the first k-step of stage kt+1 are read from LDS while
+//     those MFMAs run.
 //   grouped_gemm_regs  (decode-sized experts, 32-row tiles): operands staged
 //     through registers into a double-buffered LDS tile.
 // Both accumulate k in the same order (ascending, 16 at a time), so they give
@@ -349,11 +350,16 @@ grouped_gemm_ring(GemmArgs p) {
       wait_lgkmcnt0();
       if (kt + 1 < nk) wait_stages<PW, S>(min(S - 2, nk - 2 - kt));
       barrier();
+      // The last k-step's MFMAs go first (their fragments are already in
+      // registers), so the MFMA pipe does not idle while the DMA and the next
+      // stage's fragment reads are issued; sched_barrier keeps that order.
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(acc, fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
       if (kt + S < nk) dma(kt % S, kt + S);
       if (kt + 1 < nk)
         read_frags<MB, NB, TM, TN, BM, BK>(fa[KS & 1], fb[KS & 1], lds[(kt + 1) % S], 0, wm, wn,
                                            lane);
-      mfma_step(acc, fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
     }
     store_tile<MB, NB, TM, TN, BN, GATEUP>(p, t, acc, wm, wn, lane);
   }

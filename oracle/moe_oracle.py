@@ -30,6 +30,10 @@ What it computes, step by step, in the order and notation of the pages:
   is SwiGLU: ``h = silu(x Wg^T) * (x Wu^T)``, ``out = h Wd^T``.
 * Un-permutation: results put back in token order, multiplied by the router
   weights and summed [zoe.im 范式 A Step 3 and the opening dataflow].
+* Routing statistics (outside the forward pass): the batch's per-expert
+  fraction of slots folded into an EMA, and the per-expert bias moved by
+  (E * normalised EMA - 1) * step [ybb.press 4.1, ``_update_load_balance_stats``
+  and the bias update in ``load_balance_loss``].
 
 Precision: every sum is taken in float64.  Values are rounded only where the
 layer stores them: logits and router weights to fp32, and the bf16 tensors
@@ -354,3 +358,35 @@ def token_outputs(x_bits, topk_ids, topk_w, kept_mask, expert_weights):
     for k in range(K):
         y += np.where(np.asarray(kept_mask)[:, k:k + 1], w[:, k:k + 1] * outs[:, k], 0.0)
     return round_bf16(y), outs
+
+
+# --------------------------------------------------------------------------
+# routing statistics (ybb.press 4.1)
+# --------------------------------------------------------------------------
+
+def routing_stats(counts, ema, bias, decay: float = 0.99, step: float = 0.1):
+    """One update of the router's load statistics and dynamic bias.
+
+    ybb.press 4.1: the batch's expert fraction f_e = count_e / sum(count)
+    (``_update_load_balance_stats``), the EMA ema_e <- decay*ema_e +
+    (1-decay)*f_e, then ``expert_fraction = ema / ema.sum()`` and
+    ``dynamic_bias += (E * expert_fraction - 1) * step`` (``load_balance_loss``,
+    step 0.1 on the page).  As printed the update raises the bias of experts
+    above the uniform share; ``step`` is a parameter, so a caller wanting the
+    opposite direction passes a negative step.
+
+    Reading for a batch with no slots (sum of counts 0): nothing changes.
+    Returns (ema, bias) as float64.
+    """
+    c = np.asarray(counts, dtype=np.float64)
+    ema = np.asarray(ema, dtype=np.float64)
+    bias = np.asarray(bias, dtype=np.float64)
+    E = c.shape[0]
+    tot = c.sum()
+    if tot == 0:
+        return ema.copy(), bias.copy()
+    f = c / tot
+    ema_new = decay * ema + (1.0 - decay) * f
+    frac = ema_new / ema_new.sum()
+    bias_new = bias + (E * frac - 1.0) * step
+    return ema_new, bias_new

@@ -355,3 +355,53 @@ def test_hot_skew_top_expert_share():
     share = np.bincount(ids.reshape(-1), minlength=cfg.E).max() / ids.size
     assert 0.21 <= share <= 0.29
     assert O.capacity(cfg.N, cfg.K, cfg.E, *cfg.capacity) == 640
+
+
+# ---------------------------------------------------------------- routing statistics
+
+def test_routing_stats_uniform_is_a_fixed_point():
+    """Uniform counts and a uniform EMA: the EMA stays 1/E and the bias moves
+    by (E * 1/E - 1) * step = 0 (ybb.press 4.1)."""
+    E = 16
+    ema, bias = O.routing_stats(np.full(E, 5), np.full(E, 1 / E), np.arange(E) * 0.25)
+    assert np.allclose(ema, 1 / E, rtol=0, atol=1e-15)
+    assert np.allclose(bias, np.arange(E) * 0.25, rtol=0, atol=1e-15)
+
+
+def test_routing_stats_single_hot_expert_closed_form():
+    """All slots on expert 0, EMA uniform: ema_0 = d/E + (1-d), ema_e = d/E;
+    the EMA still sums to 1, so frac = ema and bias_e += (E*ema_e - 1)*step."""
+    E, d, st = 8, 0.9, 0.1
+    counts = np.zeros(E, dtype=np.int64)
+    counts[0] = 40
+    ema, bias = O.routing_stats(counts, np.full(E, 1 / E), np.zeros(E), decay=d, step=st)
+    want = np.full(E, d / E)
+    want[0] += 1 - d
+    assert np.allclose(ema, want, rtol=0, atol=1e-15)
+    assert np.allclose(bias, (E * want - 1) * st, rtol=0, atol=1e-15)
+    assert bias[0] > 0 > bias[1]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_routing_stats_invariants(seed):
+    """The EMA is a convex combination (its sum stays 1 when it starts at 1)
+    and the bias updates sum to zero over the experts (sum_e (E f_e - 1) = 0);
+    scaling the counts changes nothing (only fractions enter)."""
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(2, 300))
+    counts = rng.integers(0, 50, E)
+    counts[0] += 1
+    ema0 = rng.dirichlet(np.ones(E))
+    bias0 = rng.standard_normal(E)
+    ema, bias = O.routing_stats(counts, ema0, bias0, decay=0.97, step=-0.05)
+    assert abs(ema.sum() - 1) < 1e-12
+    assert abs((bias - bias0).sum()) < 1e-9
+    ema3, bias3 = O.routing_stats(counts * 3, ema0, bias0, decay=0.97, step=-0.05)
+    assert np.allclose(ema3, ema, rtol=1e-14, atol=0) and np.allclose(bias3, bias, rtol=1e-14, atol=0)
+
+
+def test_routing_stats_empty_batch_changes_nothing():
+    E = 5
+    ema0, bias0 = np.full(E, 0.2), np.linspace(-1, 1, E)
+    ema, bias = O.routing_stats(np.zeros(E, dtype=np.int64), ema0, bias0)
+    assert np.array_equal(ema, ema0) and np.array_equal(bias, bias0)

@@ -189,6 +189,27 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                        float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------ routing statistics */
+
+/* Router load statistics and dynamic expert bias ("MoE 大规模分布式推理工程实战"
+ * (ybb.press), 4.1: the EMA of the per-expert routing fraction and the bias
+ * update of its load-balancing step).  In place, on `stream`:
+ *   f[e]    = expert_counts[e] / sum(expert_counts)
+ *   ema[e]  = decay * ema[e] + (1 - decay) * f[e]
+ *   bias[e] = bias[e] + (E * ema[e] / sum(ema) - 1) * step
+ * A batch with sum(expert_counts) == 0 changes nothing.  As printed on the
+ * page (step 0.1, decay 0.99) the update raises the bias of experts above the
+ * uniform share; pass a negative step for the opposite direction.  The bias
+ * buffer is the expert_bias that moe_route / moe_forward add to the logits.
+ *   num_experts    E, 1 <= E <= 1024 (MOE_ERR_UNSUPPORTED above)
+ *   expert_counts  [E] int32 (as written by moe_permute / moe_forward)
+ *   ema            [E] fp32, in/out (start from 1/E)
+ *   expert_bias    [E] fp32, in/out
+ *   decay          in [0, 1]; step: any finite value (MOE_ERR_INVALID_ARG else)
+ * fp32 arithmetic; the sums over experts use a fixed reduction order. */
+moe_status moe_routing_stats(int32_t num_experts, const int32_t* expert_counts, float* ema,
+                             float* expert_bias, float decay, float step, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

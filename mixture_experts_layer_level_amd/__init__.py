@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     permuted_rows,
     problem,
     route,
+    routing_stats,
     status_str,
     unpermute_combine,
     workspace_size,

@@ -56,6 +56,8 @@ def _load():
     L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_permute.restype = ctypes.c_int
     L.moe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_routing_stats.restype = ctypes.c_int
+    L.moe_routing_stats.argtypes = [ctypes.c_int32, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
     L.moe_grouped_ffn.restype = ctypes.c_int
     L.moe_grouped_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_gateup.restype = ctypes.c_int
@@ -174,3 +176,9 @@ def forward(p, x, w_router, bias, w_gate, w_up, w_down, y, ws, logits=None, topk
                                           _ptr(logits), _ptr(topk_ids), _ptr(topk_weights),
                                           _ptr(counts), _ptr(offsets), _ptr(ws), _nbytes(ws),
                                           _stream(stream)))
+
+
+def routing_stats(num_experts, expert_counts, ema, expert_bias, decay=0.99, step=0.1, stream=None):
+    _check("moe_routing_stats", lib.moe_routing_stats(int(num_experts), _ptr(expert_counts),
+                                                      _ptr(ema), _ptr(expert_bias), float(decay),
+                                                      float(step), _stream(stream)))

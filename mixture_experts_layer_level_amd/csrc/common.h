@@ -76,6 +76,10 @@ hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32
 hipError_t launch_combine(const Dims& d, const uint16_t* out_perm, const int32_t* slot_row,
                           const float* weights, uint16_t* y, hipStream_t s);
 
+// stats.hip
+hipError_t launch_routing_stats(int E, const int32_t* counts, float* ema, float* bias, float decay,
+                                float step, hipStream_t s);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

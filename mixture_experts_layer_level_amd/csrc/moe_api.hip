@@ -284,4 +284,14 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
   return hip_status(launch_combine(d, out_perm, slot_row, topk_weights, y, s));
 }
 
+moe_status moe_routing_stats(int32_t num_experts, const int32_t* expert_counts, float* ema,
+                             float* expert_bias, float decay, float step, void* stream) {
+  if (num_experts < 1 || !expert_counts || !ema || !expert_bias) return MOE_ERR_INVALID_ARG;
+  if (!(decay >= 0.f && decay <= 1.f) || !(step == step)) return MOE_ERR_INVALID_ARG;
+  if (num_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_routing_stats(num_experts, expert_counts, ema, expert_bias, decay, step,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -134,3 +134,13 @@ def test_product_does_not_use_the_oracle():
                 txt = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "oracle" not in txt.lower(), f
                 assert "moe_synth" not in txt, f
+
+
+def test_routing_stats_argument_checks():
+    f = moe.lib.moe_routing_stats
+    assert f(0, FAKE, FAKE, FAKE, 0.9, 0.1, None) == INVALID
+    assert f(8, None, FAKE, FAKE, 0.9, 0.1, None) == INVALID
+    assert f(8, FAKE, FAKE, FAKE, 1.5, 0.1, None) == INVALID
+    assert f(8, FAKE, FAKE, FAKE, float("nan"), 0.1, None) == INVALID
+    assert f(8, FAKE, FAKE, FAKE, 0.9, float("nan"), None) == INVALID
+    assert f(2048, FAKE, FAKE, FAKE, 0.9, 0.1, None) == UNSUPPORTED

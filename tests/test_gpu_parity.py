@@ -188,3 +188,48 @@ def test_full_size(name, padded):
         assert 0.2 <= share <= 0.3
     del L
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("E,scale,decay,step", [(1, 10, 0.99, 0.1), (8, 100, 0.99, 0.1),
+                                                (256, 40, 0.9, -0.05), (1024, 3, 0.5, 0.1),
+                                                (64, 0, 0.99, 0.1)])
+def test_routing_stats(E, scale, decay, step):
+    """moe_routing_stats against the oracle.  Bounds from the fp32 operations:
+    ema: a divide, two products and a sum (<= 8 roundings, relative); bias:
+    frac = ema / (tree sum of <= 1024 positive terms) is within 24u
+    relative, so |d bias| <= |step| (E frac 24u + 2u) + 2u |bias|."""
+    rng = np.random.default_rng(E + scale)
+    counts = rng.integers(0, scale + 1, E).astype(np.int32)
+    ema0 = rng.dirichlet(np.ones(E)).astype(np.float32)
+    bias0 = rng.standard_normal(E).astype(np.float32)
+    c_d = torch.from_numpy(counts).to(DEV)
+    ema_d = torch.from_numpy(ema0).to(DEV)
+    bias_d = torch.from_numpy(bias0).to(DEV)
+    moe.routing_stats(E, c_d, ema_d, bias_d, decay, step)
+    torch.cuda.synchronize()
+    ema_ref, bias_ref = O.routing_stats(counts, ema0, bias0, decay, step)
+    u = 2.0 ** -24
+    assert np.all(np.abs(np_(ema_d) - ema_ref) <= 8 * u * np.abs(ema_ref) + 1e-30)
+    frac = ema_ref / ema_ref.sum()
+    tol = abs(step) * (E * frac * 24 * u + 2 * u) + 2 * u * np.abs(bias_ref)
+    assert np.all(np.abs(np_(bias_d) - bias_ref) <= tol)
+    if counts.sum() == 0:
+        assert np.array_equal(np_(ema_d), ema0) and np.array_equal(np_(bias_d), bias0)
+
+
+def test_routing_stats_from_a_layer():
+    """Fed by the expert_counts of a real permute, ten updates in a row track
+    the float64 oracle run on the same counts."""
+    L = Layer(SMALL["decode_like"])
+    L.staged()
+    E = L.cfg.E
+    ema_d = torch.full((E,), 1.0 / E, dtype=torch.float32, device=DEV)
+    bias_d = torch.zeros(E, dtype=torch.float32, device=DEV)
+    ema, bias = np.full(E, 1.0 / E), np.zeros(E)
+    counts = np_(L.counts)
+    for _ in range(10):
+        moe.routing_stats(E, L.counts, ema_d, bias_d)
+        torch.cuda.synchronize()
+        ema, bias = O.routing_stats(counts, ema, bias)
+    assert np.allclose(np_(ema_d), ema, rtol=1e-5, atol=1e-9)
+    assert np.allclose(np_(bias_d), bias, rtol=1e-5, atol=1e-6)

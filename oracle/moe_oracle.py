@@ -34,6 +34,10 @@ What it computes, step by step, in the order and notation of the pages:
   fraction of slots folded into an EMA, and the per-expert bias moved by
   (E * normalised EMA - 1) * step [ybb.press 4.1, ``_update_load_balance_stats``
   and the bias update in ``load_balance_loss``].
+* Block-scaled FP8 expert weights: E4M3 codes with one power-of-two scale
+  per 32 values along a weight row's input dimension, and the FFN run on
+  their dequantised values [zoe.im 第四层 DeepGEMM & MegaMoE Kernel (FP8
+  weights); jsqmd.com 5.3 技巧2 (8-bit expert weights, dequantised for use)].
 
 Precision: every sum is taken in float64.  Values are rounded only where the
 layer stores them: logits and router weights to fp32, and the bf16 tensors
@@ -390,3 +394,125 @@ def routing_stats(counts, ema, bias, decay: float = 0.99, step: float = 0.1):
     frac = ema_new / ema_new.sum()
     bias_new = bias + (E * frac - 1.0) * step
     return ema_new, bias_new
+
+
+# --------------------------------------------------------------------------
+# block-scaled FP8 expert weights
+# --------------------------------------------------------------------------
+#
+# The pages store expert weights in fewer bits: FP8 weights inside the
+# grouped-GEMM kernel ("MoE 推理完整机制" (zoe.im), 第四层 DeepGEMM & MegaMoE
+# Kernel) and 8-bit expert weights dequantised before use ("MoE工程实战"
+# (jsqmd.com), 5.3 技巧2).  Neither fixes a format.  Reading taken here: the
+# OCP microscaling layout with FP8 E4M3 elements -- blocks of 32 consecutive
+# values along the contraction (input) dimension of a weight row share one
+# power-of-two scale 2^s stored as a biased 8-bit exponent (E8M0, byte
+# s + 127); each element is an E4M3 code (1 sign, 4 exponent bits with bias
+# 7, 3 mantissa bits; the all-ones magnitude S.1111.111 is NaN, there is no
+# infinity, the largest finite value is 448).
+
+E4M3_MAX = 448.0
+E4M3_MIN_NORMAL = 2.0 ** -6
+E4M3_SUBNORMAL_STEP = 2.0 ** -9
+MX_BLOCK = 32
+MX_EMAX_ELEM = 8          # exponent of the largest E4M3 binade (448 = 1.75 * 2^8)
+MX_SCALE_MIN = -117       # 2^-9 * 2^-117 = 2^-126: every dequantised value stays normal
+MX_SCALE_MAX = 119        # floor(log2(largest bf16)) - 8
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 codes (uint8) -> float64 values.
+
+    exponent field 0: subnormal, M * 2^-9; else (8 + M) * 2^(E - 10), i.e.
+    (1 + M/8) * 2^(E - 7); S.1111.111 is NaN.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    neg = (c >> 7) & 1
+    ef = (c >> 3) & 15
+    mf = c & 7
+    mag = np.where(ef == 0, mf * E4M3_SUBNORMAL_STEP,
+                   np.ldexp((8 + mf).astype(np.float64), ef - 10))
+    mag = np.where((ef == 15) & (mf == 7), np.nan, mag)
+    return np.where(neg == 1, -mag, mag)
+
+
+def e4m3_encode(t) -> np.ndarray:
+    """float64 values -> E4M3 codes, round to nearest even, saturating.
+
+    Finite magnitudes above 448 become 448 (the OCP MX conversion saturates);
+    non-finite values become NaN (0x7F with the input's sign bit).  The grid
+    step is 2^(floor(log2|t|) - 3) in the normal range (|t| >= 2^-6) and
+    2^-9 below it; a carry out of the mantissa moves to the next binade.
+    """
+    t = np.asarray(t, dtype=np.float64)
+    neg = np.signbit(t)
+    fin = np.isfinite(t)
+    a = np.where(fin, np.minimum(np.abs(t), E4M3_MAX), 0.0)
+    _, ex = np.frexp(a)                       # a = m * 2^ex, 0.5 <= m < 1
+    step = np.where(a >= E4M3_MIN_NORMAL, ex - 1 - 3, -9)
+    v = np.ldexp(np.rint(np.ldexp(a, -step)), step)   # rounded magnitude
+    mv, ev = np.frexp(v)
+    normal = v >= E4M3_MIN_NORMAL
+    mag = np.where(normal,
+                   ((ev - 1 + 7) << 3) + np.rint((2.0 * mv - 1.0) * 8).astype(np.int64),
+                   np.rint(v / E4M3_SUBNORMAL_STEP).astype(np.int64))
+    mag = np.where(fin, mag, 0x7F)
+    return (mag | (neg.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def mx_block_exponent(amax) -> np.ndarray:
+    """Shared exponent of a block from its largest finite magnitude.
+
+    floor(log2(amax)) - 8, so the block's largest value lands in the top
+    E4M3 binade [256, 512) (saturating above 448); clamped to
+    [-117, 119] so that every dequantised value is a normal bf16 number.  An
+    all-zero block takes the lower clamp.
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(amax)
+    e = np.where(amax > 0, ex - 1 - MX_EMAX_ELEM, MX_SCALE_MIN)
+    return np.clip(e, MX_SCALE_MIN, MX_SCALE_MAX).astype(np.int64)
+
+
+def quantize_fp8(w_bits):
+    """bf16 weights [..., K] -> (codes uint8 [..., K], scales uint8 [..., K/32]).
+
+    Per block of 32 consecutive values of the last (contraction) axis:
+    s = mx_block_exponent(largest finite |w|), element code =
+    e4m3_encode(w / 2^s) (the division by a power of two is exact), scale
+    byte = s + 127.
+    """
+    w = bf16_to_f64(w_bits)
+    K = w.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("contraction length must be a multiple of 32")
+    blk = w.reshape(w.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.where(np.isfinite(blk), np.abs(blk), 0.0), axis=-1)
+    s = mx_block_exponent(amax)
+    codes = e4m3_encode(np.ldexp(blk, -s[..., None]))
+    return codes.reshape(w.shape), (s + 127).astype(np.uint8)
+
+
+def dequantize_fp8(codes, scales) -> np.ndarray:
+    """value = e4m3_decode(code) * 2^(scale - 127), float64 (exact in bf16)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    s = np.asarray(scales, dtype=np.uint8).astype(np.int64) - 127
+    K = c.shape[-1]
+    v = e4m3_decode(c).reshape(c.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    return np.ldexp(v, s[..., None]).reshape(c.shape)
+
+
+def dequantize_fp8_bits(codes, scales) -> np.ndarray:
+    """dequantize_fp8 as raw bf16 bit patterns (the conversion is exact)."""
+    return f64_to_bf16_bits(dequantize_fp8(codes, scales))
+
+
+def expert_ffn_fp8(x_perm_bits, offsets, wg_q, wu_q, wd_q):
+    """Grouped SwiGLU FFN with block-scaled FP8 weights.
+
+    Each weight argument is a (codes, scales) pair from quantize_fp8.  The
+    weights enter the FFN as their dequantised values (exact bf16 numbers),
+    so this is expert_ffn on those values.
+    """
+    return expert_ffn(x_perm_bits, offsets, dequantize_fp8_bits(*wg_q),
+                      dequantize_fp8_bits(*wu_q), dequantize_fp8_bits(*wd_q))

@@ -405,3 +405,146 @@ def test_routing_stats_empty_batch_changes_nothing():
     ema0, bias0 = np.full(E, 0.2), np.linspace(-1, 1, E)
     ema, bias = O.routing_stats(np.zeros(E, dtype=np.int64), ema0, bias0)
     assert np.array_equal(ema, ema0) and np.array_equal(bias, bias0)
+
+
+# ------------------------------------------------------ block-scaled FP8 weights
+# Independent references: torch's float8_e4m3fn conversions (a separate
+# implementation of the OCP E4M3 format), closed forms of the format, and exact
+# round trips of values built from known codes and exponents.
+
+def _all_codes():
+    return np.arange(256, dtype=np.uint8)
+
+
+def test_e4m3_decode_matches_torch():
+    c = _all_codes()
+    mine = O.e4m3_decode(c)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).float().double().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.isnan(mine).sum() == 2 and np.isnan(mine[[0x7F, 0xFF]]).all()
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_e4m3_encode_matches_torch(seed):
+    """Random fp32 values across every binade of the format, plus every
+    midpoint between neighbouring codes (ties go to the even code)."""
+    rng = np.random.default_rng(seed)
+    v = (rng.standard_normal(100000) * np.exp2(rng.integers(-16, 9, 100000))).astype(np.float32)
+    v = v[np.abs(v) <= O.E4M3_MAX]
+    d = O.e4m3_decode(_all_codes())[:127]
+    mids = ((d[:-1] + d[1:]) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, -mids, [0.0, -0.0]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(v.astype(np.float64)), ref)
+
+
+def test_e4m3_encode_closed_forms():
+    cases = {448.0: 0x7E, -448.0: 0xFE, 1.0: 0x38, 2.0 ** -9: 0x01, 2.0 ** -6: 0x08,
+             2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02, 1.0625: 0x38, 1.1875: 0x3A,
+             15.5: 0x58,          # tie between 15 (0x57) and 16: even mantissa
+             464.0: 0x7E, 500.0: 0x7E, 1e30: 0x7E, -1e30: 0xFE,
+             math.inf: 0x7F, -math.inf: 0xFF, math.nan: 0x7F, -0.0: 0x80,
+             -(2.0 ** -11): 0x80}
+    got = O.e4m3_encode(np.array(list(cases.keys())))
+    assert got.tolist() == list(cases.values())
+
+
+def test_mx_block_scale_closed_forms():
+    """Shared exponent floor(log2 amax) - 8: the block maximum lands in
+    [256, 512) and saturates to 448 above it; zero and tiny blocks take the
+    lower clamp -117 (byte 10), the largest bf16 block the upper 119 (byte 246)."""
+    def q(vals):
+        w = np.zeros((1, 32))
+        w[0, :len(vals)] = vals
+        return O.quantize_fp8(O.f64_to_bf16_bits(w))
+    c, s = q([1.0, 0.5, -0.25])
+    assert s.tolist() == [[119]] and c[0, :3].tolist() == [0x78, 0x70, 0xE8]
+    c, s = q([1.9921875])                           # 1.99 * 2^8 = 510 -> 448
+    assert s.tolist() == [[119]] and c[0, 0] == 0x7E
+    c, s = q([-3.0, 2.0 ** -20])                    # -3 * 2^7 = -1.5 * 2^8; 2^-13 -> 0
+    assert s.tolist() == [[120]] and c[0, :2].tolist() == [0xFC, 0x00]
+    c, s = q([])
+    assert s.tolist() == [[10]] and not c.any()
+    c, s = q([2.0 ** -130])                         # a bf16 subnormal
+    assert s.tolist() == [[10]] and c[0, 0] == 0
+    bmax = O.bf16_to_f64(np.array([0x7F7F], dtype=np.uint16))[0]
+    c, s = q([bmax, -bmax])
+    assert s.tolist() == [[246]] and c[0, :2].tolist() == [0x7E, 0xFE]
+    c, s = q([2.0, math.inf, math.nan])             # non-finite: NaN code, scale from the finite ones
+    assert s.tolist() == [[120]] and c[0, :3].tolist() == [0x78, 0x7F, 0x7F]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fp8_round_trip_exact(seed):
+    """Weights built as code * 2^s, with one code of each block in the top
+    binade [256, 448], quantise back to exactly those codes and exponents,
+    on a 3-D [E, F, D] tensor (rows and blocks must not mix)."""
+    rng = np.random.default_rng(seed)
+    E, F, D = 3, 5, 128
+    nb = D // 32
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    codes = rng.choice(finite, size=(E, F, D)).astype(np.uint8)
+    top = rng.integers(0x78, 0x7F, size=(E, F, nb)) | (rng.integers(0, 2, (E, F, nb)) << 7)
+    pos = rng.integers(0, 32, size=(E, F, nb))
+    for idx in np.ndindex(E, F, nb):
+        codes[idx[0], idx[1], idx[2] * 32 + pos[idx]] = top[idx]
+    s = rng.integers(O.MX_SCALE_MIN, O.MX_SCALE_MAX + 1, size=(E, F, nb))
+    w = np.ldexp(O.e4m3_decode(codes).reshape(E, F, nb, 32), s[..., None]).reshape(E, F, D)
+    w_bits = O.f64_to_bf16_bits(w)
+    assert np.array_equal(O.bf16_to_f64(w_bits), w)          # the weights are bf16 values
+    qc, qs = O.quantize_fp8(w_bits)
+    assert qs.shape == (E, F, nb) and qs.dtype == np.uint8
+    assert np.array_equal(qc, codes) and np.array_equal(qs.astype(np.int64), s + 127)
+    assert np.array_equal(O.dequantize_fp8_bits(qc, qs), w_bits)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fp8_error_bound_and_exactness(seed):
+    """Each dequantised value is within half a grid step of the weight
+    (2^(floor(log2|w/2^s|) - 4) in the normal range, 2^-10 below, times 2^s),
+    saturated values excepted; dequantised values are bf16 numbers; the
+    rounding is monotone within a block."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((16, 256)) * 0.02
+    w[rng.random(w.shape) < 0.01] *= 40                    # outliers
+    w_bits = O.f64_to_bf16_bits(w)
+    w = O.bf16_to_f64(w_bits)
+    c, s = O.quantize_fp8(w_bits)
+    deq = O.dequantize_fp8(c, s)
+    assert np.array_equal(O.round_bf16(deq), deq)
+    sc = np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=-1)
+    t = np.abs(w) / sc
+    _, ex = np.frexp(t)
+    half = np.where(t >= O.E4M3_MIN_NORMAL, np.ldexp(1.0, ex - 1 - 4), 2.0 ** -10)
+    sat = t > O.E4M3_MAX
+    assert np.all(np.abs(deq - w)[~sat] <= (half * sc)[~sat])
+    assert np.all(np.abs(deq[sat]) == O.E4M3_MAX * sc[sat])
+    order = np.argsort(w[0, :32], kind="stable")
+    assert np.all(np.diff(deq[0, :32][order]) >= 0)
+
+
+def test_expert_ffn_fp8_on_representable_weights():
+    """With weights that FP8 represents exactly, the FP8 FFN equals the bf16
+    FFN bit for bit (gate and up not swapped, down not transposed)."""
+    rng = np.random.default_rng(7)
+    E, F, D, R = 3, 64, 96, 10
+
+    def rep(shape):
+        codes = rng.integers(0x20, 0x50, size=shape).astype(np.uint8) | \
+            (rng.integers(0, 2, shape) << 7).astype(np.uint8)
+        codes[..., ::32] = 0x78                          # pin each block's exponent
+        s = np.full(shape[:-1] + (shape[-1] // 32,), 127 - 12, dtype=np.uint8)
+        return codes, s
+
+    wg, wu, wd = rep((E, F, D)), rep((E, F, D)), rep((E, D, F))
+    x = O.f64_to_bf16_bits(rng.standard_normal((R, D)))
+    offs = np.array([0, 4, 4, R])
+    want = O.expert_ffn(x, offs, O.dequantize_fp8_bits(*wg), O.dequantize_fp8_bits(*wu),
+                        O.dequantize_fp8_bits(*wd))
+    for q in (wg, wu, wd):
+        assert np.array_equal(O.quantize_fp8(O.dequantize_fp8_bits(*q))[0], q[0])
+    got = O.expert_ffn_fp8(x, offs, wg, wu, wd)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    assert np.abs(got[1]).max() > 0

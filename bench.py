@@ -8,6 +8,10 @@ issued separately so the dominant kernel (the gate/up grouped GEMM) can be
 bracketed with HIP events on the stream it runs on.  Inputs are synthetic,
 seeded and already resident in HBM when timing starts.
 
+With ``--weights fp8`` the expert weights are stored as block-scaled FP8
+(E4M3 codes, one power-of-two scale per 32 values; quantised once before
+timing) and the two grouped GEMMs read them through the FP8 entry points.
+
 Prints one JSON line.  ``value`` is tokens/s of the layer on this GPU.
 """
 from __future__ import annotations
@@ -50,6 +54,8 @@ def main():
     ap.add_argument("--config", default="mixtral",
                     help="tiny | mixtral | deepseek_v3 | qwen3_decode | hot_skew")
     ap.add_argument("--padded", action="store_true", help="capacity-padded layout (hot_skew)")
+    ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
+                    help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
     ap.add_argument("--cpu-tokens", type=int, default=192,
                     help="tokens of the CPU-oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -94,16 +100,33 @@ def main():
     x, wr, bias = inp["x"], inp["w_router"], inp["bias"]
     wg, wu, wd = inp["w_gate"], inp["w_up"], inp["w_down"]
     stream = torch.cuda.current_stream()
+    fp8 = args.weights == "fp8"
+    if fp8:
+        def quant(wt):
+            rows, cols = wt.shape[-2], wt.shape[-1]
+            c = torch.empty(wt.shape, dtype=torch.uint8, device=dev)
+            sc = torch.empty(wt.shape[0], rows // 32, cols // 32, 32, dtype=torch.uint8,
+                             device=dev)
+            moe.quantize_fp8(wt.numel() // cols, cols, wt, c, sc, stream=stream)
+            return c, sc
+        qg, qu, qd = quant(wg), quant(wu), quant(wd)
+        torch.cuda.synchronize()
 
     def step(ev=None):
         moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        moe.expert_gateup(p, x_perm, offsets, wg, wu, h, stream=stream)
+        if fp8:
+            moe.expert_gateup_fp8(p, x_perm, offsets, qg, qu, h, stream=stream)
+        else:
+            moe.expert_gateup(p, x_perm, offsets, wg, wu, h, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        moe.expert_down(p, h, offsets, wd, out_perm, stream=stream)
+        if fp8:
+            moe.expert_down_fp8(p, h, offsets, qd, out_perm, stream=stream)
+        else:
+            moe.expert_down(p, h, offsets, wd, out_perm, stream=stream)
         if ev is not None:
             ev[2].record(stream)
         moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
@@ -132,10 +155,11 @@ def main():
     flops = 2.0 * N * D * E + 6.0 * D * F * kept        # router + SwiGLU FFN, kept slots
     tflops = flops / (ms_step * 1e-3) / 1e12
     touched = int((counts_h > 0).sum())
-    weight_bytes = 3.0 * touched * F * D * 2
+    wb = (1.0 + 1.0 / 32) if fp8 else 2.0          # weight bytes per element (FP8: + scales)
+    weight_bytes = 3.0 * touched * F * D * wb
     # gate/up grouped GEMM (the dominant kernel): algorithmic work per launch
     gu_flops = 4.0 * D * F * kept
-    gu_bytes = 2.0 * touched * F * D * 2 + kept * D * 2 + kept * F * 2   # Wg+Wu, x_perm, h
+    gu_bytes = 2.0 * touched * F * D * wb + kept * D * 2 + kept * F * 2   # Wg+Wu, x_perm, h
     t_mfma = gu_flops / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = gu_bytes / (PEAK_HBM_GBPS * 1e9)
     if t_mfma >= t_hbm:
@@ -145,7 +169,8 @@ def main():
         roof = {"bound": "hbm", "achieved": gu_bytes / (gateup_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(args.config) if not capv else None
+    roof["traffic"] = (measured_traffic(args.config + ("_fp8" if fp8 else ""))
+                       if not capv else None)
     roof["kernel"] = "grouped gate/up GEMM + SwiGLU"
     roof["avg_ms"] = gateup_ms
     roof["algorithmic"] = {"flop": gu_flops, "bytes": gu_bytes}
@@ -164,7 +189,9 @@ def main():
         "data": "synthetic (seeded counter-based draws, random-init weights)",
         "config": {"workload": cfg.note + (" [capacity-padded]" if capv else ""),
                    "tokens": N, "hidden": D, "experts": E, "top_k": K, "ffn": F,
-                   "gating": cfg.gating, "capacity": capv or None},
+                   "gating": cfg.gating, "capacity": capv or None,
+                   "expert_weights": ("fp8 e4m3, power-of-two scale per 32 values"
+                                      if fp8 else "bf16")},
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "weight_stream_gbps": weight_bytes / (ms_step * 1e-3) / 1e9,
@@ -180,7 +207,7 @@ def main():
           flush=True)
 
     if args.cpu_tokens > 0:
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, N), capv)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, N), capv, fp8)
     print(json.dumps(line), flush=True)
 
 
@@ -197,8 +224,10 @@ def calib_copy(mib: int):
     print(f"[calib] copied {n} bytes three times", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, inp, n, capv):
-    """The CPU oracle, as it stands, on the first n tokens of the same layer."""
+def cpu_baseline(cfg, inp, n, capv, fp8=False):
+    """The CPU oracle, as it stands, on the first n tokens of the same layer
+    (FP8 weights: quantised by the oracle before the timed run, as the GPU's
+    are before its timed steps)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -218,6 +247,8 @@ def cpu_baseline(cfg, inp, n, capv):
     wr = inp["w_router"].cpu().numpy()
     bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
     wg, wu, wd = b(inp["w_gate"]), b(inp["w_up"]), b(inp["w_down"])
+    if fp8:
+        wg, wu, wd = (O.dequantize_fp8_bits(*O.quantize_fp8(m)) for m in (wg, wu, wd))
     cap = None
     if capv:
         cap = O.capacity(n, cfg.K, cfg.E, *cfg.capacity)

@@ -189,6 +189,66 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                        float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------ block-scaled FP8 weights */
+/* Expert weights stored as FP8 with block scales, read by the grouped FFN and
+ * dequantised inside its kernels: the FP8 weights of the grouped-GEMM kernel
+ * in "MoE 推理完整机制" (zoe.im) 第四层 (DeepGEMM & MegaMoE Kernel) and the
+ * 8-bit expert weights of "MoE工程实战" (jsqmd.com) 5.3 技巧2.  Format (the
+ * OCP microscaling layout with E4M3 elements; the pages fix no format):
+ *   - 32 consecutive values along a weight row's input dimension (the
+ *     contraction dimension: D for gate/up, F for down) form a block with one
+ *     scale 2^s, stored as the byte s + 127 (E8M0).
+ *   - codes [rows, cols] uint8, each an E4M3 value (sign, 4 exponent bits with
+ *     bias 7, 3 mantissa bits; S.1111.111 is NaN, no infinity, max 448).
+ *   - scales, blocked by 32 rows: the scale of rows [32g, 32g+32) and k-block
+ *     kb sits at byte ((g * (cols/32)) + kb) * 32 + (row - 32g), i.e. a
+ *     [rows/32, cols/32, 32] uint8 array.
+ *   - weight value = E4M3(code) * 2^(byte - 127), exactly a bf16 number for the
+ *     scale bytes 10..246 that moe_quantize_fp8 writes; other bytes give
+ *     unspecified values (never a fault).
+ * An expert stack [E, rows, cols] is E such matrices back to back (codes
+ * [E, rows, cols], scales [E, rows/32, cols/32, 32]).  The FFN runs on the
+ * dequantised values: the FP8 entry points give bit-identical results to the
+ * bf16 ones called with the dequantised weights. */
+
+/* Quantise bf16 weights [rows, cols] (rows, cols multiples of 32; w and
+ * codes 16-byte aligned; MOE_ERR_UNSUPPORTED else) into codes and scales as
+ * above.  Per block: s = floor(log2(largest finite |w|)) - 8, clamped to
+ * [-117, 119] (all-zero blocks take -117); code = w / 2^s rounded to the
+ * nearest E4M3 value, ties to even, saturating at +-448; infinities and NaNs
+ * give NaN codes.  Pass rows = E * per-expert rows for a whole stack.  Exact
+ * integer work: the output depends only on the input bits.  Needs no
+ * workspace; rows == 0 launches nothing. */
+moe_status moe_quantize_fp8(int64_t rows, int32_t cols, const uint16_t* w, uint8_t* codes,
+                            uint8_t* scales, void* stream);
+
+/* moe_expert_gateup / moe_expert_down / moe_grouped_ffn / moe_forward with
+ * FP8 weight stacks in place of the bf16 ones: w_gate_*, w_up_* [E, F, D]
+ * (scales [E, F/32, D/32, 32]), w_down_* [E, D, F] (scales
+ * [E, D/32, F/32, 32]).  Codes and scales must be 16-byte aligned
+ * (MOE_ERR_UNSUPPORTED else).  Everything else -- shapes, layouts, row
+ * coverage, workspace, errors -- as in the bf16 calls. */
+moe_status moe_expert_gateup_fp8(const moe_problem* p, const uint16_t* x_perm,
+                                 const int32_t* expert_offsets, const uint8_t* w_gate_codes,
+                                 const uint8_t* w_gate_scales, const uint8_t* w_up_codes,
+                                 const uint8_t* w_up_scales, uint16_t* h, void* stream);
+moe_status moe_expert_down_fp8(const moe_problem* p, const uint16_t* h,
+                               const int32_t* expert_offsets, const uint8_t* w_down_codes,
+                               const uint8_t* w_down_scales, uint16_t* out_perm, void* stream);
+moe_status moe_grouped_ffn_fp8(const moe_problem* p, const uint16_t* x_perm,
+                               const int32_t* expert_offsets, const uint8_t* w_gate_codes,
+                               const uint8_t* w_gate_scales, const uint8_t* w_up_codes,
+                               const uint8_t* w_up_scales, const uint8_t* w_down_codes,
+                               const uint8_t* w_down_scales, uint16_t* out_perm, uint16_t* h,
+                               void* ws, size_t ws_bytes, void* stream);
+moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float* w_router,
+                           const float* expert_bias, const uint8_t* w_gate_codes,
+                           const uint8_t* w_gate_scales, const uint8_t* w_up_codes,
+                           const uint8_t* w_up_scales, const uint8_t* w_down_codes,
+                           const uint8_t* w_down_scales, uint16_t* y, float* logits,
+                           int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                           int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------ routing statistics */
 
 /* Router load statistics and dynamic expert bias ("MoE 大规模分布式推理工程实战"

@@ -14,14 +14,19 @@ from ._lib import (  # noqa: F401
     MoEProblem,
     abi_version,
     expert_down,
+    expert_down_fp8,
     expert_gateup,
+    expert_gateup_fp8,
     forward,
+    forward_fp8,
     grouped_ffn,
+    grouped_ffn_fp8,
     lib,
     library_path,
     permute,
     permuted_rows,
     problem,
+    quantize_fp8,
     route,
     routing_stats,
     status_str,

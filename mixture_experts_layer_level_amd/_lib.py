@@ -68,6 +68,17 @@ def _load():
     L.moe_unpermute_combine.argtypes = [P, vp, vp, vp, vp, vp]
     L.moe_forward.restype = ctypes.c_int
     L.moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_quantize_fp8.restype = ctypes.c_int
+    L.moe_quantize_fp8.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp]
+    L.moe_expert_gateup_fp8.restype = ctypes.c_int
+    L.moe_expert_gateup_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_down_fp8.restype = ctypes.c_int
+    L.moe_expert_down_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.moe_grouped_ffn_fp8.restype = ctypes.c_int
+    L.moe_grouped_ffn_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_forward_fp8.restype = ctypes.c_int
+    L.moe_forward_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, sz, vp]
     return L
 
 
@@ -182,3 +193,42 @@ def routing_stats(num_experts, expert_counts, ema, expert_bias, decay=0.99, step
     _check("moe_routing_stats", lib.moe_routing_stats(int(num_experts), _ptr(expert_counts),
                                                       _ptr(ema), _ptr(expert_bias), float(decay),
                                                       float(step), _stream(stream)))
+
+
+# Block-scaled FP8 weights: each weight argument below is a (codes, scales)
+# pair as written by quantize_fp8.
+
+def quantize_fp8(rows, cols, w, codes, scales, stream=None):
+    _check("moe_quantize_fp8", lib.moe_quantize_fp8(int(rows), int(cols), _ptr(w), _ptr(codes),
+                                                    _ptr(scales), _stream(stream)))
+
+
+def expert_gateup_fp8(p, x_perm, offsets, w_gate, w_up, h, stream=None):
+    _check("moe_expert_gateup_fp8",
+           lib.moe_expert_gateup_fp8(ctypes.byref(p), _ptr(x_perm), _ptr(offsets), _ptr(w_gate[0]),
+                                     _ptr(w_gate[1]), _ptr(w_up[0]), _ptr(w_up[1]), _ptr(h),
+                                     _stream(stream)))
+
+
+def expert_down_fp8(p, h, offsets, w_down, out_perm, stream=None):
+    _check("moe_expert_down_fp8",
+           lib.moe_expert_down_fp8(ctypes.byref(p), _ptr(h), _ptr(offsets), _ptr(w_down[0]),
+                                   _ptr(w_down[1]), _ptr(out_perm), _stream(stream)))
+
+
+def grouped_ffn_fp8(p, x_perm, offsets, w_gate, w_up, w_down, out_perm, h, ws, stream=None):
+    _check("moe_grouped_ffn_fp8",
+           lib.moe_grouped_ffn_fp8(ctypes.byref(p), _ptr(x_perm), _ptr(offsets), _ptr(w_gate[0]),
+                                   _ptr(w_gate[1]), _ptr(w_up[0]), _ptr(w_up[1]), _ptr(w_down[0]),
+                                   _ptr(w_down[1]), _ptr(out_perm), _ptr(h), _ptr(ws),
+                                   _nbytes(ws), _stream(stream)))
+
+
+def forward_fp8(p, x, w_router, bias, w_gate, w_up, w_down, y, ws, logits=None, topk_ids=None,
+                topk_weights=None, counts=None, offsets=None, stream=None):
+    _check("moe_forward_fp8",
+           lib.moe_forward_fp8(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
+                               _ptr(w_gate[0]), _ptr(w_gate[1]), _ptr(w_up[0]), _ptr(w_up[1]),
+                               _ptr(w_down[0]), _ptr(w_down[1]), _ptr(y), _ptr(logits),
+                               _ptr(topk_ids), _ptr(topk_weights), _ptr(counts), _ptr(offsets),
+                               _ptr(ws), _nbytes(ws), _stream(stream)))

@@ -72,6 +72,25 @@ hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32
                               const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                               uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s);
 
+// Block-scaled FP8 weights of one matrix stack [E, rows, cols]: E4M3 codes
+// [E, rows, cols] and scale bytes [E, rows/32, cols/32, 32].
+struct Fp8Weight {
+  const uint8_t* codes;
+  const uint8_t* scales;
+};
+hipError_t launch_expert_gateup_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                                    const Fp8Weight& wg, const Fp8Weight& wu, uint16_t* h,
+                                    hipStream_t s);
+hipError_t launch_expert_down_fp8(const Dims& d, const uint16_t* h, const int32_t* offsets,
+                                  const Fp8Weight& wd, uint16_t* out_perm, hipStream_t s);
+hipError_t launch_grouped_ffn_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                                  const Fp8Weight& wg, const Fp8Weight& wu, const Fp8Weight& wd,
+                                  uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s);
+
+// quant.hip
+hipError_t launch_quantize_fp8(int64_t rows, int cols, const uint16_t* w, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
+
 // combine.hip
 hipError_t launch_combine(const Dims& d, const uint16_t* out_perm, const int32_t* slot_row,
                           const float* weights, uint16_t* y, hipStream_t s);

@@ -32,6 +32,20 @@
 //     through registers into a double-buffered LDS tile.
 // Both accumulate k in the same order (ascending, 16 at a time), so they give
 // bit-identical results.
+//
+// Block-scaled FP8 weights (FP8 = true; the FP8 weights of 第四层 DeepGEMM &
+// MegaMoE Kernel): the weight operand arrives as E4M3 codes plus one E8M0
+// scale byte per 32 k of a weight row and is dequantised on the way into the
+// MFMA with v_cvt_scalef32_pk_bf16_fp8.  code * 2^s is exact in bf16, so the
+// MFMAs see exactly the dequantised weights and the result is bit-identical to
+// the bf16 kernel run on them; only the weight bytes read from memory halve.
+// The register-staged kernel converts while staging into its bf16 LDS tile;
+// the ring kernel moves codes and scales by LDS-DMA and converts each fragment
+// after its LDS read.
+//
+// Scale layout: for weight rows [32 g, 32 g + 32) and k-block kb, the 32 scale
+// bytes are contiguous at ((g * (Kd / 32)) + kb) * 32, so the scales of one
+// 32-row group for consecutive k-blocks are one contiguous run.
 #include "common.h"
 
 namespace moe {
@@ -41,12 +55,38 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct GemmArgs {
   const uint16_t* A;        // [rows, Kd]
-  const uint16_t* B0;       // [E, Nout, Kd]  (gate or down weights)
-  const uint16_t* B1;       // [E, Nout, Kd]  (up weights; gate/up only)
+  const void* B0;           // [E, Nout, Kd] bf16 or E4M3 codes (gate or down weights)
+  const void* B1;           // [E, Nout, Kd] (up weights; gate/up only)
   uint16_t* C;              // [rows, Nout]
   const int32_t* offsets;   // [E+1]
   int E, Kd, Nout, n_tiles;
+  const uint8_t* S0;        // FP8 only: scales of B0, [E, Nout/32, Kd/32, 32]
+  const uint8_t* S1;        // FP8 only: scales of B1
 };
+
+// LDS swizzle for rows of RB bytes (16-byte chunks): chunk c of row r is stored
+// at c ^ swz_rows<RB>(r).  256 / RB consecutive rows share one 256-byte bank
+// window; consecutive windows get distinct XOR masks.
+template <int RB>
+__device__ __forceinline__ int swz_rows(int r) {
+  return (r / (256 / RB)) % (RB / 16);
+}
+
+// Eight E4M3 codes (two dwords) times 2^(sbyte - 127) -> eight bf16 values;
+// the scale operand of the conversion contributes only its exponent.
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t lo, uint32_t hi, float scale) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, a),
+                                                 __builtin_bit_cast(uint32_t, b),
+                                                 __builtin_bit_cast(uint32_t, c),
+                                                 __builtin_bit_cast(uint32_t, d)));
+}
+
+__device__ __forceinline__ float scale_of(uint32_t sbyte) { return __uint_as_float(sbyte << 23); }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.f + expf(-g)) * u;
@@ -238,25 +278,36 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // the pragma); nothing else in these kernels reads or writes it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const uint16_t* base, uint32_t voff) {
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                ::"s"(lds_addr), "v"(voff), "s"(base)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
-template <int BM, int BN, int WM, int WN, int BK, int S>
+template <int BM, int BN, int WM, int WN, int BK, int S, bool FP8>
 struct Ring {
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN, MB = TM / 32, NB = TN / 32;
-  static constexpr int CH = BK / 8;          // 16-byte chunks per tile row
-  static constexpr int RPI = 64 / CH;        // tile rows per DMA instruction
-  static constexpr int ROWS = BM + BN;
-  static constexpr int PW = ROWS / RPI / NW; // DMA instructions per wave per stage
-  static constexpr int KS = BK / 16;         // MFMA k-steps per stage
-  static_assert(ROWS % (RPI * NW) == 0 && BM % RPI == 0 && 32 % RPI == 0, "DMA split");
+  static constexpr int KS = BK / 16;                  // MFMA k-steps per stage
+  static constexpr int CHA = BK / 8;                  // 16-byte chunks per A row
+  static constexpr int BRB = FP8 ? BK : 2 * BK;       // bytes per B row
+  static constexpr int CHB = BRB / 16;                // 16-byte chunks per B row
+  static constexpr int RPIA = 64 / CHA, RPIB = 64 / CHB;   // rows per DMA instruction
+  static constexpr int PWA = BM / RPIA / NW, PWB = BN / RPIB / NW;
+  static constexpr int KB = BK / 32;                  // scale blocks per stage (FP8)
+  static constexpr int LS = FP8 ? BN * KB / 16 / NW : 0;   // scale DMA lanes per wave
+  static constexpr int GPW = FP8 ? LS / (2 * KB) : 0;      // 32-row groups per wave
+  static constexpr int PW = PWA + PWB + (FP8 ? 1 : 0);     // DMA instructions per wave per stage
+  static constexpr int A_U4 = BM * CHA, B_U4 = BN * CHB, S_U4 = FP8 ? BN * KB / 16 : 0;
+  static constexpr int STAGE_U4 = A_U4 + B_U4 + S_U4;
+  static_assert(PWA * RPIA * NW == BM && PWB * RPIB * NW == BN, "DMA split");
+  static_assert(32 % RPIA == 0 && 32 % RPIB == 0, "one DMA instruction stays in a 32-row block");
+  static_assert(!FP8 || (BK % 32 == 0 && LS * 16 * NW == BN * KB && GPW >= 1 &&
+                         GPW * 2 * KB == LS && GPW * NW == BN / 32 && NW % 2 == 0),
+                "scale DMA split");
   static_assert(PW * (S - 1) <= 63, "vmcnt range");
-  static_assert((size_t)S * ROWS * BK * 2 + 4100 <= 160 * 1024, "LDS budget");
+  static_assert((size_t)S * STAGE_U4 * 16 + 4100 <= 160 * 1024, "LDS budget");
 };
 
 // Wait until at most n stages of this wave's DMA are still outstanding
@@ -273,19 +324,81 @@ __device__ __forceinline__ void wait_stages(int n) {
   wait_vmcnt<0>();
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int S, bool GATEUP>
+// FP8 scale area of a stage: wave w fetches LS 16-byte units, unit
+// (i * KB + kbl) * 2 + half holding rows 16*half .. 16*half+15 of its i-th
+// 32-row group for k-block kbl.  In gate/up tiles the first half of the waves
+// fetch the gate groups (even tile groups) and the second half the up groups,
+// so that each wave's fetch reads one matrix.  Returns the byte offset, within
+// the scale area, of group g's k-block kbl.
+template <class R, bool GATEUP>
+__device__ __forceinline__ int scale_slot(int g, int kbl) {
+  int w, i;
+  if (GATEUP) {
+    const int m = g & 1, gi = g >> 1;
+    w = m * (R::NW / 2) + gi / R::GPW;
+    i = gi % R::GPW;
+  } else {
+    w = g / R::GPW;
+    i = g % R::GPW;
+  }
+  return (w * R::LS + (i * R::KB + kbl) * 2) * 16;
+}
+
+// MFMA fragments of k-step ks from a ring stage.  bf16: A rows then B rows,
+// swizzled 16-byte chunks.  FP8: the B fragment is eight codes (8 bytes) of
+// chunk ks, dequantised with the scale of its row and 32-deep k-block; sc
+// holds the scales of the current k-block and is refreshed on its first
+// k-step.
+template <class R, bool FP8, bool GATEUP>
+__device__ __forceinline__ void read_frags_ring(bf16x8_t (&af)[R::MB], bf16x8_t (&bfr)[R::NB],
+                                                float (&sc)[R::NB], const uint4* st, int ks,
+                                                int wm, int wn, int lane) {
+  constexpr int BK = R::CHA * 8;
+  const int kc = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int mb = 0; mb < R::MB; ++mb) {
+    const int r = wm * R::TM + mb * 32 + (lane & 31);
+    af[mb] = __builtin_bit_cast(bf16x8_t, st[r * R::CHA + (kc ^ swz<BK>(r))]);
+  }
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int nb = 0; nb < R::NB; ++nb) {
+      const int r = wn * R::TN + nb * 32 + (lane & 31);
+      bfr[nb] = __builtin_bit_cast(bf16x8_t, st[R::A_U4 + r * R::CHB + (kc ^ swz<BK>(r))]);
+    }
+  } else {
+    const uint8_t* stb = reinterpret_cast<const uint8_t*>(st + R::A_U4);
+    const uint8_t* sts = reinterpret_cast<const uint8_t*>(st + R::A_U4 + R::B_U4);
+    if (ks % 2 == 0) {
+#pragma unroll
+      for (int nb = 0; nb < R::NB; ++nb)
+        sc[nb] = scale_of(sts[scale_slot<R, GATEUP>(wn * R::NB + nb, ks / 2) + (lane & 31)]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < R::NB; ++nb) {
+      const int r = wn * R::TN + nb * 32 + (lane & 31);
+      const uint2 q = *reinterpret_cast<const uint2*>(
+          stb + r * R::BRB + (ks ^ swz_rows<R::BRB>(r)) * 16 + (lane >> 5) * 8);
+      bfr[nb] = dequant8(q.x, q.y, sc[nb]);
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int S, bool GATEUP, bool FP8>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_ring(GemmArgs p) {
-  using R = Ring<BM, BN, WM, WN, BK, S>;
-  constexpr int MB = R::MB, NB = R::NB, TM = R::TM, TN = R::TN;
-  constexpr int CH = R::CH, RPI = R::RPI, PW = R::PW, KS = R::KS;
-  __shared__ uint4 lds[S][R::ROWS * CH];
+  using R = Ring<BM, BN, WM, WN, BK, S, FP8>;
+  constexpr int MB = R::MB, NB = R::NB, TN = R::TN;
+  constexpr int PWA = R::PWA, PWB = R::PWB, PW = R::PW, KS = R::KS;
+  __shared__ uint4 lds[S][R::STAGE_U4];
   __shared__ int32_t mstart[1025];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const int lr = lane / CH, lc = lane % CH;   // DMA: lane -> (row in group, LDS chunk)
+  // DMA lane roles: lane -> (row in its instruction's group, LDS chunk)
+  const int lra = lane / R::CHA, lca = lane % R::CHA;
+  const int lrb = lane / R::CHB, lcb = lane % R::CHB;
 
   if (wave == 0) build_work_list<BM>(p, mstart, lane);
   __syncthreads();
@@ -295,35 +408,68 @@ grouped_gemm_ring(GemmArgs p) {
   const int end = (int)((int64_t)total * (xcd + 1) / 8);
   const int nk = p.Kd / BK;
   const size_t wmat = (size_t)p.Nout * p.Kd;     // elements of one expert's matrix
+  (void)TN;
 
   for (int l = begin + j0; l < end; l += P8) {
     const Tile t = decode_tile<BM>(p, mstart, l);
-    // DMA sources: instruction j of this wave moves tile rows g0..g0+RPI-1
-    // (g0 wave-uniform) from base[j] + off[j]; the lane reading LDS chunk lc
-    // of a row fetches global chunk lc ^ swz(row), which realises the swizzle.
-    const uint16_t* base[PW];
-    uint32_t off[PW];
+    // DMA sources: instruction j moves 1 KB into LDS at byte ldso[j] of the
+    // stage from base[j] + off[j] (+ the per-stage advance); the lane writing
+    // LDS chunk c of a row fetches global chunk c ^ swizzle(row), which
+    // realises the swizzle.  Instructions [0, PWA) carry A rows, [PWA,
+    // PWA + PWB) B rows and, for FP8, the last one (lanes < LS only) scales.
+    const void* base[PW];
+    uint32_t off[PW], ldso[PW];
 #pragma unroll
-    for (int j = 0; j < PW; ++j) {
-      const int g0 = (wave * PW + j) * RPI;
-      const int trow = (g0 < BM ? g0 : g0 - BM) + lr;
-      const uint32_t gc = (uint32_t)(lc ^ swz<BK>(trow));
-      if (g0 < BM) {
-        base[j] = p.A + t.row0 * p.Kd;
-        off[j] = (uint32_t)min(trow, t.rows - 1) * p.Kd + gc * 8;
+    for (int j = 0; j < PWA; ++j) {
+      const int q = wave * PWA + j;
+      const int trow = q * R::RPIA + lra;
+      base[j] = p.A + t.row0 * p.Kd;
+      off[j] = ((uint32_t)min(trow, t.rows - 1) * p.Kd + (uint32_t)(lca ^ swz<BK>(trow)) * 8) * 2u;
+      ldso[j] = q * 1024;
+    }
+#pragma unroll
+    for (int jb = 0; jb < PWB; ++jb) {
+      const int q = wave * PWB + jb;
+      const int g0 = q * R::RPIB, trow = g0 + lrb;
+      bool up;
+      const int wrow = min(weight_row<BN, GATEUP>(t.nt, g0, up) + lrb, p.Nout - 1);
+      const char* b = static_cast<const char*>(up ? p.B1 : p.B0);
+      if (FP8) {
+        base[PWA + jb] = b + (size_t)t.e * wmat;
+        off[PWA + jb] = (uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz_rows<R::BRB>(trow)) * 16;
       } else {
-        bool up;
-        const int wrow = weight_row<BN, GATEUP>(t.nt, g0 - BM, up) + lr;  // block of g0 holds all RPI rows
-        base[j] = (up ? p.B1 : p.B0) + (size_t)t.e * wmat;
-        off[j] = (uint32_t)min(wrow, p.Nout - 1) * p.Kd + gc * 8;
+        base[PWA + jb] = b + (size_t)t.e * wmat * 2;
+        off[PWA + jb] = ((uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz<BK>(trow)) * 8) * 2u;
       }
+      ldso[PWA + jb] = R::A_U4 * 16 + q * 1024;
+    }
+    if constexpr (FP8) {
+      const int lam = min(lane, R::LS - 1);
+      const int half = lam & 1, kbl = (lam >> 1) % R::KB, i = (lam >> 1) / R::KB;
+      int m = 0, rg;
+      if (GATEUP) {
+        m = wave / (R::NW / 2);
+        rg = t.nt * (BN / 64) + (wave % (R::NW / 2)) * R::GPW + i;
+      } else {
+        rg = t.nt * (BN / 32) + wave * R::GPW + i;
+      }
+      rg = min(rg, p.Nout / 32 - 1);
+      base[PW - 1] = (m ? p.S1 : p.S0) + (size_t)t.e * (wmat / 32);
+      off[PW - 1] = ((uint32_t)rg * (uint32_t)(p.Kd / 32) + kbl) * 32 + half * 16;
+      ldso[PW - 1] = (R::A_U4 + R::B_U4) * 16 + wave * R::LS * 16;
     }
     auto dma = [&](int s, int kt) {
       const uint32_t l0 = (uint32_t)(uintptr_t)(lds_void_t*)&lds[s][0];
 #pragma unroll
-      for (int j = 0; j < PW; ++j)
-        lds_dma16(__builtin_amdgcn_readfirstlane(l0 + (wave * PW + j) * 1024), base[j],
-                  (off[j] + (uint32_t)(kt * BK)) * 2u);
+      for (int j = 0; j < PW; ++j) {
+        const uint32_t adv = j < PWA ? BK * 2 : j < PWA + PWB ? R::BRB : R::KB * 32;
+        const uint32_t la = __builtin_amdgcn_readfirstlane(l0 + ldso[j]);
+        if (FP8 && j == PW - 1) {
+          if (lane < R::LS) lds_dma16(la, base[j], off[j] + (uint32_t)kt * adv);
+        } else {
+          lds_dma16(la, base[j], off[j] + (uint32_t)kt * adv);
+        }
+      }
     };
 
     f32x16_t acc[MB][NB];
@@ -337,13 +483,14 @@ grouped_gemm_ring(GemmArgs p) {
     wait_stages<PW, S>(min(S - 1, nk - 1));
     barrier();
     bf16x8_t fa[2][MB], fb[2][NB];
-    read_frags<MB, NB, TM, TN, BM, BK>(fa[0], fb[0], lds[0], 0, wm, wn, lane);
+    float sc[NB];
+    read_frags_ring<R, FP8, GATEUP>(fa[0], fb[0], sc, lds[0], 0, wm, wn, lane);
     for (int kt = 0; kt < nk; ++kt) {
       const uint4* cur = lds[kt % S];
 #pragma unroll
       for (int ks = 0; ks + 1 < KS; ++ks) {
-        read_frags<MB, NB, TM, TN, BM, BK>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], cur, ks + 1, wm,
-                                           wn, lane);
+        read_frags_ring<R, FP8, GATEUP>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sc, cur, ks + 1, wm,
+                                        wn, lane);
         mfma_step(acc, fa[ks & 1], fb[ks & 1]);
       }
       // this wave has read all of stage kt and its part of stage kt+1 landed
@@ -358,33 +505,47 @@ grouped_gemm_ring(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       if (kt + S < nk) dma(kt % S, kt + S);
       if (kt + 1 < nk)
-        read_frags<MB, NB, TM, TN, BM, BK>(fa[KS & 1], fb[KS & 1], lds[(kt + 1) % S], 0, wm, wn,
-                                           lane);
+        read_frags_ring<R, FP8, GATEUP>(fa[KS & 1], fb[KS & 1], sc, lds[(kt + 1) % S], 0, wm, wn,
+                                        lane);
     }
-    store_tile<MB, NB, TM, TN, BN, GATEUP>(p, t, acc, wm, wn, lane);
+    store_tile<MB, NB, R::TM, R::TN, BN, GATEUP>(p, t, acc, wm, wn, lane);
   }
 }
 
 // ------------------------------------------------------------ register-staged
 
 constexpr int RBK = 64;            // k depth of one LDS stage
-constexpr int RCH = RBK / 8;       // 16-byte chunks per tile row
+constexpr int RCH = RBK / 8;       // 16-byte chunks per tile row (bf16)
+constexpr int QCH = RBK / 16;      // 16-byte chunks per weight row (FP8 codes)
 
-template <int NA, int NB_>
-__device__ __forceinline__ void stage_gload(uint4 (&ra)[NA], uint4 (&rb)[NB_],
+// One stage's global loads: A rows (bf16), then the weight rows -- bf16
+// chunks, or FP8 code chunks with the scale byte of each chunk's k-block.
+template <int NA, int NB_, bool FP8>
+__device__ __forceinline__ void stage_gload(uint4 (&ra)[NA], uint4 (&rb)[NB_], uint32_t (&rs)[NB_],
                                             const uint16_t* a_base, const uint32_t (&a_off)[NA],
-                                            const uint16_t* b0_base, const uint16_t* b1_base,
-                                            const uint32_t (&b_off)[NB_], uint32_t b_up, int k0) {
+                                            const char* b0_base, const char* b1_base,
+                                            const uint32_t (&b_off)[NB_], const uint8_t* s0_base,
+                                            const uint8_t* s1_base, const uint32_t (&s_off)[NB_],
+                                            uint32_t b_up, int kt) {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_base + a_off[i] + k0);
+  for (int i = 0; i < NA; ++i)
+    ra[i] = *reinterpret_cast<const uint4*>(a_base + a_off[i] + kt * RBK);
 #pragma unroll
-  for (int i = 0; i < NB_; ++i)
-    rb[i] = *reinterpret_cast<const uint4*>(((b_up >> i) & 1 ? b1_base : b0_base) + b_off[i] + k0);
+  for (int i = 0; i < NB_; ++i) {
+    const bool up = (b_up >> i) & 1;
+    if (FP8) {
+      rb[i] = *reinterpret_cast<const uint4*>((up ? b1_base : b0_base) + b_off[i] + kt * RBK);
+      rs[i] = (up ? s1_base : s0_base)[s_off[i] + kt * (RBK / 32) * 32];
+    } else {
+      rb[i] = *reinterpret_cast<const uint4*>((up ? b1_base : b0_base) + b_off[i] + kt * RBK * 2);
+    }
+  }
 }
 
-template <int NA, int NB_, int RPP, int BM>
+template <int NA, int NB_, int RPP, int QRPP, int BM, bool FP8>
 __device__ __forceinline__ void stage_lstore(uint4* st, const uint4 (&ra)[NA],
-                                             const uint4 (&rb)[NB_], int lrow, int lchunk) {
+                                             const uint4 (&rb)[NB_], const uint32_t (&rs)[NB_],
+                                             int lrow, int lchunk, int qrow, int qchunk) {
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int r = lrow + i * RPP;
@@ -392,22 +553,34 @@ __device__ __forceinline__ void stage_lstore(uint4* st, const uint4 (&ra)[NA],
   }
 #pragma unroll
   for (int i = 0; i < NB_; ++i) {
-    const int r = lrow + i * RPP;
-    st[(BM + r) * RCH + (lchunk ^ swz<RBK>(r))] = rb[i];
+    if (FP8) {
+      // 16 codes = bf16 chunks 2*qchunk and 2*qchunk + 1 of the row
+      const int r = qrow + i * QRPP;
+      const float sc = scale_of(rs[i]);
+      st[(BM + r) * RCH + ((2 * qchunk) ^ swz<RBK>(r))] =
+          __builtin_bit_cast(uint4, dequant8(rb[i].x, rb[i].y, sc));
+      st[(BM + r) * RCH + ((2 * qchunk + 1) ^ swz<RBK>(r))] =
+          __builtin_bit_cast(uint4, dequant8(rb[i].z, rb[i].w, sc));
+    } else {
+      const int r = lrow + i * RPP;
+      st[(BM + r) * RCH + (lchunk ^ swz<RBK>(r))] = rb[i];
+    }
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool GATEUP>
+template <int BM, int BN, int WM, int WN, bool GATEUP, bool FP8>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_regs(GemmArgs p) {
   constexpr int NT = 64 * WM * WN;                // threads
   constexpr int TM = BM / WM, TN = BN / WN;       // wave tile
   constexpr int MB = TM / 32, NB = TN / 32;       // 32x32 MFMA blocks per wave
   static_assert(!GATEUP || NB % 2 == 0, "gate/up pairs");
-  constexpr int RPP = NT / RCH;                   // tile rows loaded per pass
+  constexpr int RPP = NT / RCH;                   // bf16 tile rows loaded per pass
+  constexpr int QRPP = NT / QCH;                  // FP8 weight rows loaded per pass
   constexpr int A_LD = BM / RPP;                  // 16-byte loads per thread per stage
-  constexpr int B_LD = BN / RPP;
-  static_assert(A_LD >= 1 && B_LD >= 1 && BM % RPP == 0 && BN % RPP == 0, "loader shape");
+  constexpr int B_LD = FP8 ? BN / QRPP : BN / RPP;
+  static_assert(A_LD >= 1 && B_LD >= 1 && BM % RPP == 0 && BN % (FP8 ? QRPP : RPP) == 0,
+                "loader shape");
 
   __shared__ uint4 lds[2][(BM + BN) * RCH];
   __shared__ int32_t mstart[1025];
@@ -415,7 +588,8 @@ grouped_gemm_regs(GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int lrow = tid / RCH, lchunk = tid % RCH;   // loader mapping
+  const int lrow = tid / RCH, lchunk = tid % RCH;   // bf16 loader mapping
+  const int qrow = tid / QCH, qchunk = tid % QCH;   // FP8 weight loader mapping
 
   if (wave == 0) build_work_list<BM>(p, mstart, lane);
   __syncthreads();
@@ -424,43 +598,59 @@ grouped_gemm_regs(GemmArgs p) {
   const int begin = (int)((int64_t)total * xcd / 8);
   const int end = (int)((int64_t)total * (xcd + 1) / 8);
   const size_t wmat = (size_t)p.Nout * p.Kd;
+  const int ebytes = FP8 ? 1 : 2;                 // bytes per weight element
 
   for (int l = begin + j0; l < end; l += P8) {
     const Tile t = decode_tile<BM>(p, mstart, l);
     const uint16_t* a_base = p.A + t.row0 * p.Kd + lchunk * 8;
-    const uint16_t* b0_base = p.B0 + (size_t)t.e * wmat + lchunk * 8;
-    const uint16_t* b1_base = GATEUP ? p.B1 + (size_t)t.e * wmat + lchunk * 8 : b0_base;
-    uint32_t a_off[A_LD], b_off[B_LD];
+    const int bcol = FP8 ? qchunk * 16 : lchunk * 16;   // byte column of this thread's chunk
+    const char* b0_base = static_cast<const char*>(p.B0) + t.e * wmat * ebytes + bcol;
+    const char* b1_base = GATEUP ? static_cast<const char*>(p.B1) + t.e * wmat * ebytes + bcol
+                                 : b0_base;
+    const uint8_t* s0_base = nullptr;
+    const uint8_t* s1_base = nullptr;
+    if (FP8) {
+      s0_base = p.S0 + t.e * (wmat / 32) + (qchunk >> 1) * 32;
+      s1_base = GATEUP ? p.S1 + t.e * (wmat / 32) + (qchunk >> 1) * 32 : s0_base;
+    }
+    uint32_t a_off[A_LD], b_off[B_LD], s_off[B_LD];
     uint32_t b_up = 0;                               // bit i: load i reads the up matrix
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) a_off[i] = (uint32_t)min(lrow + i * RPP, t.rows - 1) * p.Kd;
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       bool up;
-      const int wrow = weight_row<BN, GATEUP>(t.nt, lrow + i * RPP, up);
+      const int wrow =
+          min(weight_row<BN, GATEUP>(t.nt, (FP8 ? qrow + i * QRPP : lrow + i * RPP), up),
+              p.Nout - 1);
       b_up |= (uint32_t)up << i;
-      b_off[i] = (uint32_t)min(wrow, p.Nout - 1) * p.Kd;
+      b_off[i] = (uint32_t)wrow * p.Kd * ebytes;
+      s_off[i] = (uint32_t)(wrow >> 5) * (uint32_t)p.Kd + (uint32_t)(wrow & 31);
     }
 
     f32x16_t acc[MB][NB];
     zero(acc);
     uint4 ra[A_LD], rb[B_LD];
+    uint32_t rs[B_LD];
     const int nk = p.Kd / RBK;
     // Stage 0 is rewritten below: wait until every wave is done with the
     // previous tile's last stage.
     __syncthreads();
-    stage_gload(ra, rb, a_base, a_off, b0_base, b1_base, b_off, b_up, 0);
-    stage_lstore<A_LD, B_LD, RPP, BM>(lds[0], ra, rb, lrow, lchunk);
+    stage_gload<A_LD, B_LD, FP8>(ra, rb, rs, a_base, a_off, b0_base, b1_base, b_off, s0_base,
+                                 s1_base, s_off, b_up, 0);
+    stage_lstore<A_LD, B_LD, RPP, QRPP, BM, FP8>(lds[0], ra, rb, rs, lrow, lchunk, qrow, qchunk);
     __syncthreads();
     for (int kt = 0; kt + 1 < nk; ++kt) {
-      stage_gload(ra, rb, a_base, a_off, b0_base, b1_base, b_off, b_up, (kt + 1) * RBK);
+      stage_gload<A_LD, B_LD, FP8>(ra, rb, rs, a_base, a_off, b0_base, b1_base, b_off, s0_base,
+                                   s1_base, s_off, b_up, kt + 1);
       bf16x8_t af[MB], bfr[NB];
 #pragma unroll
       for (int ks = 0; ks < RBK / 16; ++ks) {
         read_frags<MB, NB, TM, TN, BM, RBK>(af, bfr, lds[kt & 1], ks, wm, wn, lane);
         mfma_step(acc, af, bfr);
       }
-      stage_lstore<A_LD, B_LD, RPP, BM>(lds[(kt & 1) ^ 1], ra, rb, lrow, lchunk);
+      stage_lstore<A_LD, B_LD, RPP, QRPP, BM, FP8>(lds[(kt & 1) ^ 1], ra, rb, rs, lrow, lchunk,
+                                                   qrow, qchunk);
       __syncthreads();
     }
     {
@@ -489,16 +679,16 @@ int64_t grid_size(const Dims& d, int n_tiles, int occupancy) {
   return (g + 7) / 8 * 8;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int S, bool GATEUP>
+template <int BM, int BN, int WM, int WN, int BK, int S, bool GATEUP, bool FP8>
 hipError_t launch_ring(const Dims& d, const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_ring<BM, BN, WM, WN, BK, S, GATEUP>),
+  hipLaunchKernelGGL((grouped_gemm_ring<BM, BN, WM, WN, BK, S, GATEUP, FP8>),
                      dim3((unsigned)grid_size<BM>(d, a.n_tiles, 1)), dim3(64 * WM * WN), 0, s, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, bool GATEUP>
+template <int BM, int BN, int WM, int WN, bool GATEUP, bool FP8>
 hipError_t launch_regs(const Dims& d, const GemmArgs& a, int occupancy, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_regs<BM, BN, WM, WN, GATEUP>),
+  hipLaunchKernelGGL((grouped_gemm_regs<BM, BN, WM, WN, GATEUP, FP8>),
                      dim3((unsigned)grid_size<BM>(d, a.n_tiles, occupancy)), dim3(64 * WM * WN),
                      0, s, a);
   return hipGetLastError();
@@ -506,7 +696,7 @@ hipError_t launch_regs(const Dims& d, const GemmArgs& a, int occupancy, hipStrea
 
 // Tile shape by the average number of rows per expert (R / E):
 //   <= 48  : 32 x 256 register-staged tiles (decode: the weight stream rules)
-//   <= 384 : 128 x 256 tiles, 4 waves, 64-deep stages, 3-stage ring
+//   <= 384 : 128 x 256 tiles, 8 waves (64 x 64 each), 64-deep stages, 3-stage ring
 //   else   : 256 x 256 tiles, 8 waves, 32-deep stages, 4-stage ring
 enum class Shape { Small, Mid, Large };
 inline Shape pick(const Dims& d) {
@@ -520,26 +710,41 @@ inline Shape pick(const Dims& d) {
 
 size_t ffn_ws_bytes(const Dims& d) { return align_up((size_t)d.R * d.F * 2); }
 
+namespace {
+
+// gate/up: every tile covers 128 columns of h (256 weight rows: 128 gate +
+// 128 up); down: 256 columns of out_perm.
+template <bool FP8>
+hipError_t gateup(const Dims& d, const GemmArgs& a, hipStream_t s) {
+  switch (pick(d)) {
+    case Shape::Small: return launch_regs<32, 256, 1, 4, true, FP8>(d, a, 2, s);
+    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, 3, true, FP8>(d, a, s);
+    default: return launch_ring<256, 256, 2, 4, 32, 4, true, FP8>(d, a, s);
+  }
+}
+
+template <bool FP8>
+hipError_t down(const Dims& d, const GemmArgs& a, hipStream_t s) {
+  switch (pick(d)) {
+    case Shape::Small: return launch_regs<32, 256, 1, 4, false, FP8>(d, a, 2, s);
+    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, 3, false, FP8>(d, a, s);
+    default: return launch_ring<256, 256, 2, 4, 32, 4, false, FP8>(d, a, s);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                 const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                                 hipStream_t s) {
-  // every tile covers 128 columns of h (256 weight rows: 128 gate + 128 up)
-  GemmArgs a{x_perm, wg, wu, h, offsets, d.E, d.D, d.F, (d.F + 127) / 128};
-  switch (pick(d)) {
-    case Shape::Small: return launch_regs<32, 256, 1, 4, true>(d, a, 2, s);
-    case Shape::Mid: return launch_ring<128, 256, 2, 2, 64, 3, true>(d, a, s);
-    default: return launch_ring<256, 256, 2, 4, 32, 4, true>(d, a, s);
-  }
+  return gateup<false>(d, GemmArgs{x_perm, wg, wu, h, offsets, d.E, d.D, d.F, (d.F + 127) / 128,
+                                   nullptr, nullptr}, s);
 }
 
 hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
                               const uint16_t* wd, uint16_t* out_perm, hipStream_t s) {
-  GemmArgs a{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D, (d.D + 255) / 256};
-  switch (pick(d)) {
-    case Shape::Small: return launch_regs<32, 256, 1, 4, false>(d, a, 2, s);
-    case Shape::Mid: return launch_ring<128, 256, 2, 2, 64, 3, false>(d, a, s);
-    default: return launch_ring<256, 256, 2, 4, 32, 4, false>(d, a, s);
-  }
+  return down<false>(d, GemmArgs{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D,
+                                 (d.D + 255) / 256, nullptr, nullptr}, s);
 }
 
 hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
@@ -549,6 +754,28 @@ hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32
   hipError_t e = launch_expert_gateup(d, x_perm, offsets, wg, wu, h, s);
   if (e != hipSuccess) return e;
   return launch_expert_down(d, h, offsets, wd, out_perm, s);
+}
+
+hipError_t launch_expert_gateup_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                                    const Fp8Weight& wg, const Fp8Weight& wu, uint16_t* h,
+                                    hipStream_t s) {
+  return gateup<true>(d, GemmArgs{x_perm, wg.codes, wu.codes, h, offsets, d.E, d.D, d.F,
+                                  (d.F + 127) / 128, wg.scales, wu.scales}, s);
+}
+
+hipError_t launch_expert_down_fp8(const Dims& d, const uint16_t* h, const int32_t* offsets,
+                                  const Fp8Weight& wd, uint16_t* out_perm, hipStream_t s) {
+  return down<true>(d, GemmArgs{h, wd.codes, nullptr, out_perm, offsets, d.E, d.F, d.D,
+                                (d.D + 255) / 256, wd.scales, nullptr}, s);
+}
+
+hipError_t launch_grouped_ffn_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                                  const Fp8Weight& wg, const Fp8Weight& wu, const Fp8Weight& wd,
+                                  uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s) {
+  if (!h) h = static_cast<uint16_t*>(ws);
+  hipError_t e = launch_expert_gateup_fp8(d, x_perm, offsets, wg, wu, h, s);
+  if (e != hipSuccess) return e;
+  return launch_expert_down_fp8(d, h, offsets, wd, out_perm, s);
 }
 
 }  // namespace moe

@@ -1,6 +1,7 @@
 // C ABI of libmoe: argument checks, workspace layout and launch sequencing.
 // Every check runs on the host before the first HIP call of an entry point.
 #include <atomic>
+#include <cmath>
 
 #include "common.h"
 
@@ -86,6 +87,57 @@ inline moe_status hip_status(hipError_t e) {
   t_last_hip_error = e;
   return MOE_ERR_HIP;
 }
+
+// The layer: route, permute, the grouped FFN given by `ffn`, combine.
+// weights_present / weights_aligned: the caller's checks of its expert weights.
+template <class Ffn>
+moe_status forward_impl(const moe_problem* p, const uint16_t* x, const float* w_router,
+                        const float* expert_bias, bool weights_present, bool weights_aligned,
+                        uint16_t* y, float* logits, int32_t* topk_ids, float* topk_weights,
+                        int32_t* expert_counts, int32_t* expert_offsets, void* ws,
+                        size_t ws_bytes, void* stream, Ffn ffn) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !y || !weights_present) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(y) || !weights_aligned)
+    return MOE_ERR_UNSUPPORTED;
+  const ForwardWs L = forward_layout(d);
+  if (d.N > 0 && (!ws || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  char* base = static_cast<char*>(ws);
+  if (!logits) logits = reinterpret_cast<float*>(base + L.logits);
+  if (!topk_ids) topk_ids = reinterpret_cast<int32_t*>(base + L.ids);
+  if (!topk_weights) topk_weights = reinterpret_cast<float*>(base + L.weights);
+  if (!expert_counts) expert_counts = reinterpret_cast<int32_t*>(base + L.counts);
+  if (!expert_offsets) expert_offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* row_token = reinterpret_cast<int32_t*>(base + L.row_token);
+  int32_t* slot_row = reinterpret_cast<int32_t*>(base + L.slot_row);
+  uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);
+  uint16_t* out_perm = reinterpret_cast<uint16_t*>(base + L.out_perm);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(launch_router_gemm(d, x, w_router, logits, s));
+  if (st != MOE_OK) return st;
+  st = hip_status(launch_topk(d, logits, expert_bias, topk_ids, topk_weights, s));
+  if (st != MOE_OK) return st;
+  st = hip_status(launch_permute(d, x, topk_ids, expert_counts, expert_offsets, row_token,
+                                 slot_row, x_perm, base + L.perm, s));
+  if (st != MOE_OK) return st;
+  st = hip_status(ffn(d, x_perm, expert_offsets, out_perm, base + L.ffn, s));
+  if (st != MOE_OK) return st;
+  return hip_status(launch_combine(d, out_perm, slot_row, topk_weights, y, s));
+}
+
+// Block-scaled FP8 weight stack: codes and scales present and 16-byte aligned.
+inline moe_status check_fp8(const uint8_t* codes, const uint8_t* scales) {
+  if (!codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(scales)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+inline bool fp8_present(const uint8_t* c, const uint8_t* s) { return c && s; }
+inline bool fp8_aligned(const uint8_t* c, const uint8_t* s) { return aligned16(c) && aligned16(s); }
 
 }  // namespace
 
@@ -248,50 +300,123 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                        const uint16_t* w_down, uint16_t* y, float* logits, int32_t* topk_ids,
                        float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
                        void* ws, size_t ws_bytes, void* stream) {
-  Dims d;
-  moe_status st = check_problem(p, &d);
-  if (st != MOE_OK) return st;
-  if (!x || !w_router || !w_gate || !w_up || !w_down || !y) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
-      !aligned16(w_down) || !aligned16(y))
-    return MOE_ERR_UNSUPPORTED;
-  const ForwardWs L = forward_layout(d);
-  if (d.N > 0 && (!ws || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
-  if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
-  if (d.N == 0) return MOE_OK;
-  (void)hipGetLastError();  // report only this call's launch errors
-  char* base = static_cast<char*>(ws);
-  if (!logits) logits = reinterpret_cast<float*>(base + L.logits);
-  if (!topk_ids) topk_ids = reinterpret_cast<int32_t*>(base + L.ids);
-  if (!topk_weights) topk_weights = reinterpret_cast<float*>(base + L.weights);
-  if (!expert_counts) expert_counts = reinterpret_cast<int32_t*>(base + L.counts);
-  if (!expert_offsets) expert_offsets = reinterpret_cast<int32_t*>(base + L.offsets);
-  int32_t* row_token = reinterpret_cast<int32_t*>(base + L.row_token);
-  int32_t* slot_row = reinterpret_cast<int32_t*>(base + L.slot_row);
-  uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);
-  uint16_t* out_perm = reinterpret_cast<uint16_t*>(base + L.out_perm);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(launch_router_gemm(d, x, w_router, logits, s));
-  if (st != MOE_OK) return st;
-  st = hip_status(launch_topk(d, logits, expert_bias, topk_ids, topk_weights, s));
-  if (st != MOE_OK) return st;
-  st = hip_status(launch_permute(d, x, topk_ids, expert_counts, expert_offsets, row_token,
-                                 slot_row, x_perm, base + L.perm, s));
-  if (st != MOE_OK) return st;
-  st = hip_status(launch_grouped_ffn(d, x_perm, expert_offsets, w_gate, w_up, w_down, out_perm,
-                                     nullptr, base + L.ffn, s));
-  if (st != MOE_OK) return st;
-  return hip_status(launch_combine(d, out_perm, slot_row, topk_weights, y, s));
+  const bool present = w_gate && w_up && w_down;
+  const bool aligned = aligned16(w_gate) && aligned16(w_up) && aligned16(w_down);
+  return forward_impl(p, x, w_router, expert_bias, present, aligned, y, logits, topk_ids,
+                      topk_weights, expert_counts, expert_offsets, ws, ws_bytes, stream,
+                      [&](const Dims& d, const uint16_t* xp, const int32_t* offs, uint16_t* op,
+                          void* fws, hipStream_t s) {
+                        return launch_grouped_ffn(d, xp, offs, w_gate, w_up, w_down, op, nullptr,
+                                                  fws, s);
+                      });
 }
 
 moe_status moe_routing_stats(int32_t num_experts, const int32_t* expert_counts, float* ema,
                              float* expert_bias, float decay, float step, void* stream) {
   if (num_experts < 1 || !expert_counts || !ema || !expert_bias) return MOE_ERR_INVALID_ARG;
-  if (!(decay >= 0.f && decay <= 1.f) || !(step == step)) return MOE_ERR_INVALID_ARG;
+  if (!(decay >= 0.f && decay <= 1.f) || !std::isfinite(step)) return MOE_ERR_INVALID_ARG;
   if (num_experts > 1024) return MOE_ERR_UNSUPPORTED;
   (void)hipGetLastError();  // report only this call's launch errors
   return hip_status(launch_routing_stats(num_experts, expert_counts, ema, expert_bias, decay, step,
                                          static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_quantize_fp8(int64_t rows, int32_t cols, const uint16_t* w, uint8_t* codes,
+                            uint8_t* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || !w || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (rows % 32 != 0 || cols % 32 != 0 || !aligned16(w) || !aligned16(codes))
+    return MOE_ERR_UNSUPPORTED;
+  if (rows > (int64_t)1 << 40 || (int64_t)cols > ((int64_t)1 << 40) / (rows > 0 ? rows : 1))
+    return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(
+      launch_quantize_fp8(rows, cols, w, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_gateup_fp8(const moe_problem* p, const uint16_t* x_perm,
+                                 const int32_t* expert_offsets, const uint8_t* w_gate_codes,
+                                 const uint8_t* w_gate_scales, const uint8_t* w_up_codes,
+                                 const uint8_t* w_up_scales, uint16_t* h, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !h) return MOE_ERR_INVALID_ARG;
+  if ((st = check_fp8(w_gate_codes, w_gate_scales)) != MOE_OK) return st;
+  if ((st = check_fp8(w_up_codes, w_up_scales)) != MOE_OK) return st;
+  if (!aligned16(x_perm) || !aligned16(h)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_gateup_fp8(d, x_perm, expert_offsets,
+                                             Fp8Weight{w_gate_codes, w_gate_scales},
+                                             Fp8Weight{w_up_codes, w_up_scales}, h,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_down_fp8(const moe_problem* p, const uint16_t* h,
+                               const int32_t* expert_offsets, const uint8_t* w_down_codes,
+                               const uint8_t* w_down_scales, uint16_t* out_perm, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!h || !expert_offsets || !out_perm) return MOE_ERR_INVALID_ARG;
+  if ((st = check_fp8(w_down_codes, w_down_scales)) != MOE_OK) return st;
+  if (!aligned16(h) || !aligned16(out_perm)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_down_fp8(d, h, expert_offsets,
+                                           Fp8Weight{w_down_codes, w_down_scales}, out_perm,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_ffn_fp8(const moe_problem* p, const uint16_t* x_perm,
+                               const int32_t* expert_offsets, const uint8_t* w_gate_codes,
+                               const uint8_t* w_gate_scales, const uint8_t* w_up_codes,
+                               const uint8_t* w_up_scales, const uint8_t* w_down_codes,
+                               const uint8_t* w_down_scales, uint16_t* out_perm, uint16_t* h,
+                               void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !out_perm) return MOE_ERR_INVALID_ARG;
+  if ((st = check_fp8(w_gate_codes, w_gate_scales)) != MOE_OK) return st;
+  if ((st = check_fp8(w_up_codes, w_up_scales)) != MOE_OK) return st;
+  if ((st = check_fp8(w_down_codes, w_down_scales)) != MOE_OK) return st;
+  if (!aligned16(x_perm) || !aligned16(out_perm) || (h && !aligned16(h)))
+    return MOE_ERR_UNSUPPORTED;
+  const size_t need = h ? 0 : ffn_ws_bytes(d);
+  if (d.N > 0 && need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_grouped_ffn_fp8(
+      d, x_perm, expert_offsets, Fp8Weight{w_gate_codes, w_gate_scales},
+      Fp8Weight{w_up_codes, w_up_scales}, Fp8Weight{w_down_codes, w_down_scales}, out_perm, h, ws,
+      static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float* w_router,
+                           const float* expert_bias, const uint8_t* w_gate_codes,
+                           const uint8_t* w_gate_scales, const uint8_t* w_up_codes,
+                           const uint8_t* w_up_scales, const uint8_t* w_down_codes,
+                           const uint8_t* w_down_scales, uint16_t* y, float* logits,
+                           int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                           int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream) {
+  const bool present = fp8_present(w_gate_codes, w_gate_scales) &&
+                       fp8_present(w_up_codes, w_up_scales) &&
+                       fp8_present(w_down_codes, w_down_scales);
+  const bool aligned = fp8_aligned(w_gate_codes, w_gate_scales) &&
+                       fp8_aligned(w_up_codes, w_up_scales) &&
+                       fp8_aligned(w_down_codes, w_down_scales);
+  const Fp8Weight wg{w_gate_codes, w_gate_scales}, wu{w_up_codes, w_up_scales},
+      wd{w_down_codes, w_down_scales};
+  return forward_impl(p, x, w_router, expert_bias, present, aligned, y, logits, topk_ids,
+                      topk_weights, expert_counts, expert_offsets, ws, ws_bytes, stream,
+                      [&](const Dims& d, const uint16_t* xp, const int32_t* offs, uint16_t* op,
+                          void* fws, hipStream_t s) {
+                        return launch_grouped_ffn_fp8(d, xp, offs, wg, wu, wd, op, nullptr, fws,
+                                                      s);
+                      });
 }
 
 }  // extern "C"

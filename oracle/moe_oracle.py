@@ -482,15 +482,21 @@ def quantize_fp8(w_bits):
     e4m3_encode(w / 2^s) (the division by a power of two is exact), scale
     byte = s + 127.
     """
-    w = bf16_to_f64(w_bits)
-    K = w.shape[-1]
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    K = w_bits.shape[-1]
     if K % MX_BLOCK:
         raise ValueError("contraction length must be a multiple of 32")
-    blk = w.reshape(w.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
-    amax = np.max(np.where(np.isfinite(blk), np.abs(blk), 0.0), axis=-1)
-    s = mx_block_exponent(amax)
-    codes = e4m3_encode(np.ldexp(blk, -s[..., None]))
-    return codes.reshape(w.shape), (s + 127).astype(np.uint8)
+    flat = w_bits.reshape(-1, K)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scales = np.empty((flat.shape[0], K // MX_BLOCK), dtype=np.uint8)
+    for r0 in range(0, flat.shape[0], 256):     # rows are independent; 256 at a time
+        blk = bf16_to_f64(flat[r0:r0 + 256]).reshape(-1, K // MX_BLOCK, MX_BLOCK)
+        amax = np.max(np.where(np.isfinite(blk), np.abs(blk), 0.0), axis=-1)
+        s = mx_block_exponent(amax)
+        codes[r0:r0 + 256] = e4m3_encode(np.ldexp(blk, -s[..., None])).reshape(-1, K)
+        scales[r0:r0 + 256] = s + 127
+    return (codes.reshape(w_bits.shape),
+            scales.reshape(w_bits.shape[:-1] + (K // MX_BLOCK,)))
 
 
 def dequantize_fp8(codes, scales) -> np.ndarray:

@@ -14,6 +14,37 @@ from oracle import moe_oracle as O
 
 DEV = "cuda"
 
+# Small workloads that together cover every tile shape and edge case of the
+# path; each runs in seconds against the oracle.
+C = ms.MoEConfig
+SMALL = {
+    "tiny": ms.CONFIGS["tiny"],
+    # ragged: N not a tile multiple, F = 192 leaves a half-empty column tile
+    "ragged": C("ragged", N=333, D=320, E=6, K=2, F=192, gating="softmax", seed=101),
+    # small-row tiles (about 6 rows per expert), sigmoid gating
+    "decode_like": C("decode_like", N=50, D=128, E=32, K=4, F=256, gating="sigmoid", seed=102),
+    # two experts of about 350 rows: two row tiles each, the second ragged
+    "two_big_experts": C("two_big_experts", N=700, D=256, E=2, K=1, F=128, gating="softmax",
+                         seed=103),
+    "single_expert": C("single_expert", N=300, D=192, E=1, K=1, F=128, gating="softmax", seed=104),
+    "k_equals_e": C("k_equals_e", N=40, D=128, E=4, K=4, F=64, gating="sigmoid", seed=105),
+    # strong Zipf bias: several experts receive no token at all
+    "empty_experts": C("empty_experts", N=90, D=128, E=16, K=2, F=128, gating="softmax",
+                       seed=106, zipf_s=1.2, zipf_alpha=4.0),
+    # about 550 rows per expert: 256 x 256 ring tiles, ragged last row tile,
+    # F = 192 leaves half of the second h column tile empty
+    "large_tiles": C("large_tiles", N=1100, D=320, E=2, K=1, F=192, gating="softmax", seed=109),
+    # about 240 rows per expert: 128 x 256 ring tiles
+    "mid_tiles": C("mid_tiles", N=960, D=384, E=8, K=2, F=320, gating="sigmoid", seed=110),
+    # K = 12: the combine and copy kernels take the slots of a token in groups of 8
+    "wide_topk": C("wide_topk", N=80, D=128, E=32, K=12, F=128, gating="softmax", seed=111),
+    "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
+                zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
+    "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,
+                           gating="softmax", seed=108, zipf_s=1.2, zipf_alpha=1.0,
+                           capacity=(1, 2)),
+}
+
 
 def bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

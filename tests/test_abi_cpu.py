@@ -144,3 +144,41 @@ def test_routing_stats_argument_checks():
     assert f(8, FAKE, FAKE, FAKE, float("nan"), 0.1, None) == INVALID
     assert f(8, FAKE, FAKE, FAKE, 0.9, float("nan"), None) == INVALID
     assert f(2048, FAKE, FAKE, FAKE, 0.9, 0.1, None) == UNSUPPORTED
+    assert f(8, FAKE, FAKE, FAKE, 0.9, float("inf"), None) == INVALID
+
+
+def test_fp8_argument_checks():
+    L = moe.lib
+    q = L.moe_quantize_fp8
+    assert q(64, 128, None, FAKE, FAKE, None) == INVALID
+    assert q(-32, 128, FAKE, FAKE, FAKE, None) == INVALID
+    assert q(64, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert q(48, 128, FAKE, FAKE, FAKE, None) == UNSUPPORTED      # rows not a multiple of 32
+    assert q(64, 80, FAKE, FAKE, FAKE, None) == UNSUPPORTED       # cols not a multiple of 32
+    assert q(64, 128, FAKE + 2, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(0, 128, FAKE, FAKE, FAKE, None) == OK                # nothing to do
+    p = P()
+    bp = ctypes.byref(p)
+    g = L.moe_expert_gateup_fp8
+    assert g(bp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == INVALID
+    assert g(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, None) == UNSUPPORTED
+    assert g(ctypes.byref(P(N=0)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == OK
+    d = L.moe_expert_down_fp8
+    assert d(bp, FAKE, FAKE, None, FAKE, FAKE, None) == INVALID
+    assert d(bp, FAKE, FAKE, FAKE + 4, FAKE, FAKE, None) == UNSUPPORTED
+    ffn = L.moe_grouped_ffn_fp8
+    assert ffn(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) \
+        == WORKSPACE
+    assert ffn(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) \
+        == INVALID
+    fw = L.moe_forward_fp8
+    need = moe.workspace_size(p)
+    args = [bp, FAKE, FAKE, None] + [FAKE] * 6 + [FAKE] + [None] * 5
+    bad = list(args)
+    bad[5] = None                                                 # gate scales missing
+    assert fw(*bad, FAKE, need, None) == INVALID
+    bad = list(args)
+    bad[9] = FAKE + 1                                             # down scales misaligned
+    assert fw(*bad, FAKE, need, None) == UNSUPPORTED
+    assert fw(*args, FAKE, need - 1, None) == WORKSPACE
+    assert fw(ctypes.byref(P(N=0)), *args[1:], None, 0, None) == OK

@@ -15,39 +15,10 @@ from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
 
-from gpu_layer import (DEV, Layer, assert_fp_close, bits, check_permutation,  # noqa: E402
-                       check_routing, np_, sample_tokens, check_sampled_outputs)
+from gpu_layer import (DEV, SMALL, Layer, assert_fp_close, bits,  # noqa: E402
+                       check_permutation, check_routing, np_, sample_tokens,
+                       check_sampled_outputs)
 import mixture_experts_layer_level_amd as moe  # noqa: E402
-
-C = ms.MoEConfig
-SMALL = {
-    "tiny": ms.CONFIGS["tiny"],
-    # ragged: N not a tile multiple, F = 192 leaves a half-empty column tile
-    "ragged": C("ragged", N=333, D=320, E=6, K=2, F=192, gating="softmax", seed=101),
-    # small-row tiles (about 6 rows per expert), sigmoid gating
-    "decode_like": C("decode_like", N=50, D=128, E=32, K=4, F=256, gating="sigmoid", seed=102),
-    # two experts of about 350 rows: two row tiles each, the second ragged
-    "two_big_experts": C("two_big_experts", N=700, D=256, E=2, K=1, F=128, gating="softmax",
-                         seed=103),
-    "single_expert": C("single_expert", N=300, D=192, E=1, K=1, F=128, gating="softmax", seed=104),
-    "k_equals_e": C("k_equals_e", N=40, D=128, E=4, K=4, F=64, gating="sigmoid", seed=105),
-    # strong Zipf bias: several experts receive no token at all
-    "empty_experts": C("empty_experts", N=90, D=128, E=16, K=2, F=128, gating="softmax",
-                       seed=106, zipf_s=1.2, zipf_alpha=4.0),
-    # about 550 rows per expert: 256 x 256 ring tiles, ragged last row tile,
-    # F = 192 leaves half of the second h column tile empty
-    "large_tiles": C("large_tiles", N=1100, D=320, E=2, K=1, F=192, gating="softmax", seed=109),
-    # about 240 rows per expert: 128 x 256 ring tiles
-    "mid_tiles": C("mid_tiles", N=960, D=384, E=8, K=2, F=320, gating="sigmoid", seed=110),
-    # K = 12: the combine and copy kernels take the slots of a token in groups of 8
-    "wide_topk": C("wide_topk", N=80, D=128, E=32, K=12, F=128, gating="softmax", seed=111),
-    "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
-                zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
-    "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,
-                           gating="softmax", seed=108, zipf_s=1.2, zipf_alpha=1.0,
-                           capacity=(1, 2)),
-}
-
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_staged_path_small(name):

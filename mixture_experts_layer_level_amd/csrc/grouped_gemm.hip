@@ -30,7 +30,7 @@
 //     those MFMAs run.
 //   grouped_gemm_regs  (decode-sized experts, 32-row tiles): operands staged
 //     through registers into a double-buffered LDS tile.
-// Both accumulate k in the same order (ascending, 16 at a time), so they give
+// Both accumulate k in the same order (kchunk below), so they give
 // bit-identical results.
 //
 // Block-scaled FP8 weights (FP8 = true; the FP8 weights of 第四层 DeepGEMM &
@@ -59,7 +59,7 @@ struct GemmArgs {
   const void* B1;           // [E, Nout, Kd] (up weights; gate/up only)
   uint16_t* C;              // [rows, Nout]
   const int32_t* offsets;   // [E+1]
-  int E, Kd, Nout, n_tiles;
+  int E, Kd, Nout, n_tiles;  // n_tiles: column tiles per expert (set by the launcher)
   const uint8_t* S0;        // FP8 only: scales of B0, [E, Nout/32, Kd/32, 32]
   const uint8_t* S1;        // FP8 only: scales of B1
 };
@@ -221,13 +221,23 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& t,
   }
 }
 
+// k order of the MFMAs.  Each 32-deep k-block b takes two 16-deep k-steps;
+// in k-step j the lanes of half h (lane / 32) hold the 8 values at
+// 32 b + 16 h + 8 j.  So over the block's two k-steps a lane's values are one
+// contiguous run of 16 (one 16-byte read of FP8 codes), and every kernel and
+// tile depth accumulates k in this same order.  Returns the 8-value chunk of
+// the stage row that a lane reads at k-step ks.
+__device__ __forceinline__ int kchunk(int ks, int lane) {
+  return 4 * (ks >> 1) + 2 * (lane >> 5) + (ks & 1);
+}
+
 // MFMA fragments of one 16-deep k-step from an LDS stage of BM A rows
 // followed by BN B rows, CH 16-byte chunks per row.
 template <int MB, int NB, int TM, int TN, int BM, int BK>
 __device__ __forceinline__ void read_frags(bf16x8_t (&af)[MB], bf16x8_t (&bfr)[NB],
                                            const uint4* st, int ks, int wm, int wn, int lane) {
   constexpr int CH = BK / 8;
-  const int kc = ks * 2 + (lane >> 5);
+  const int kc = kchunk(ks, lane);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int r = wm * TM + mb * 32 + (lane & 31);
@@ -240,14 +250,19 @@ __device__ __forceinline__ void read_frags(bf16x8_t (&af)[MB], bf16x8_t (&bfr)[N
   }
 }
 
+// One k-step of MFMAs; 32-row blocks mb >= nmb (wholly past the tile's last
+// row) are skipped, which frees the SIMD's matrix pipe for the other waves.
 template <int MB, int NB>
 __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[MB][NB], const bf16x8_t (&af)[MB],
-                                          const bf16x8_t (&bfr)[NB]) {
+                                          const bf16x8_t (&bfr)[NB], int nmb = MB) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
+    if (mb < nmb) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[mb][nb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[mb][nb], 0, 0, 0);
+    }
 }
 
 template <int MB, int NB>
@@ -285,8 +300,9 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* base, u
 }
 #pragma clang diagnostic pop
 
-template <int BM, int BN, int WM, int WN, int BK, int S, bool FP8>
+template <int BM, int BN, int WM, int WN, int BK, int S_, bool FP8>
 struct Ring {
+  static constexpr int S = S_;
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN, MB = TM / 32, NB = TN / 32;
   static constexpr int KS = BK / 16;                  // MFMA k-steps per stage
@@ -306,8 +322,8 @@ struct Ring {
   static_assert(!FP8 || (BK % 32 == 0 && LS * 16 * NW == BN * KB && GPW >= 1 &&
                          GPW * 2 * KB == LS && GPW * NW == BN / 32 && NW % 2 == 0),
                 "scale DMA split");
-  static_assert(PW * (S - 1) <= 63, "vmcnt range");
-  static_assert((size_t)S * STAGE_U4 * 16 + 4100 <= 160 * 1024, "LDS budget");
+  static_assert(PW * (S_ - 1) <= 63, "vmcnt range");
+  static_assert((size_t)S_ * STAGE_U4 * 16 + 4100 <= 160 * 1024, "LDS budget");
 };
 
 // Wait until at most n stages of this wave's DMA are still outstanding
@@ -344,21 +360,22 @@ __device__ __forceinline__ int scale_slot(int g, int kbl) {
   return (w * R::LS + (i * R::KB + kbl) * 2) * 16;
 }
 
-// MFMA fragments of k-step ks from a ring stage.  bf16: A rows then B rows,
-// swizzled 16-byte chunks.  FP8: the B fragment is eight codes (8 bytes) of
-// chunk ks, dequantised with the scale of its row and 32-deep k-block; sc
-// holds the scales of the current k-block and is refreshed on its first
-// k-step.
+// MFMA fragments of k-step ks from a ring stage (A blocks mb >= nmb are not
+// read).  bf16: A rows then B rows, swizzled 16-byte chunks.  FP8: on the
+// first k-step of a 32-deep block each lane reads its 16 codes of the block
+// (qb) and the block's scale of its row (sc); the two k-steps dequantise the
+// first and second 8 of them.
 template <class R, bool FP8, bool GATEUP>
 __device__ __forceinline__ void read_frags_ring(bf16x8_t (&af)[R::MB], bf16x8_t (&bfr)[R::NB],
-                                                float (&sc)[R::NB], const uint4* st, int ks,
-                                                int wm, int wn, int lane) {
+                                                float (&sc)[R::NB], uint4 (&qb)[R::NB],
+                                                const uint4* st, int ks, int wm, int wn,
+                                                int lane, int nmb) {
   constexpr int BK = R::CHA * 8;
-  const int kc = ks * 2 + (lane >> 5);
+  const int kc = kchunk(ks, lane);
 #pragma unroll
   for (int mb = 0; mb < R::MB; ++mb) {
     const int r = wm * R::TM + mb * 32 + (lane & 31);
-    af[mb] = __builtin_bit_cast(bf16x8_t, st[r * R::CHA + (kc ^ swz<BK>(r))]);
+    if (mb < nmb) af[mb] = __builtin_bit_cast(bf16x8_t, st[r * R::CHA + (kc ^ swz<BK>(r))]);
   }
   if constexpr (!FP8) {
 #pragma unroll
@@ -371,16 +388,71 @@ __device__ __forceinline__ void read_frags_ring(bf16x8_t (&af)[R::MB], bf16x8_t 
     const uint8_t* sts = reinterpret_cast<const uint8_t*>(st + R::A_U4 + R::B_U4);
     if (ks % 2 == 0) {
 #pragma unroll
-      for (int nb = 0; nb < R::NB; ++nb)
+      for (int nb = 0; nb < R::NB; ++nb) {
+        const int r = wn * R::TN + nb * 32 + (lane & 31);
+        const int c = 2 * (ks >> 1) + (lane >> 5);    // 16-code chunk of this lane's half
+        qb[nb] = *reinterpret_cast<const uint4*>(stb + r * R::BRB +
+                                                 (c ^ swz_rows<R::BRB>(r)) * 16);
         sc[nb] = scale_of(sts[scale_slot<R, GATEUP>(wn * R::NB + nb, ks / 2) + (lane & 31)]);
+      }
     }
 #pragma unroll
-    for (int nb = 0; nb < R::NB; ++nb) {
-      const int r = wn * R::TN + nb * 32 + (lane & 31);
-      const uint2 q = *reinterpret_cast<const uint2*>(
-          stb + r * R::BRB + (ks ^ swz_rows<R::BRB>(r)) * 16 + (lane >> 5) * 8);
-      bfr[nb] = dequant8(q.x, q.y, sc[nb]);
+    for (int nb = 0; nb < R::NB; ++nb)
+      bfr[nb] = (ks & 1) ? dequant8(qb[nb].z, qb[nb].w, sc[nb])
+                         : dequant8(qb[nb].x, qb[nb].y, sc[nb]);
+  }
+}
+
+// The k loop of one ring tile, for a wave whose first NMB 32-row blocks hold
+// rows of the tile (the MFMAs and A reads of the others are skipped; the
+// wave still issues its DMA and meets every barrier).  The tile's first
+// stages are already in flight or landed: stage 0 has landed and every wave
+// has passed the barrier after it.
+template <class R, int NMB, bool FP8, bool GATEUP, class Dma>
+__device__ __forceinline__ void ring_kloop(f32x16_t (&acc)[R::MB][R::NB],
+                                           uint4 (*lds)[R::STAGE_U4], int nk, int wm, int wn,
+                                           int lane, const Dma& dma) {
+  constexpr int MB = R::MB, NB = R::NB, PW = R::PW, KS = R::KS, S = R::S;
+  bf16x8_t fa[2][MB], fb[2][NB];
+  float sc[NB];
+  uint4 qb[NB];
+  read_frags_ring<R, FP8, GATEUP>(fa[0], fb[0], sc, qb, lds[0], 0, wm, wn, lane, NMB);
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint4* cur = lds[kt % S];
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      read_frags_ring<R, FP8, GATEUP>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sc, qb, cur, ks + 1,
+                                      wm, wn, lane, NMB);
+      mfma_step(acc, fa[ks & 1], fb[ks & 1], NMB);
     }
+    // this wave has read all of stage kt and its part of stage kt+1 landed
+    wait_lgkmcnt0();
+    if (kt + 1 < nk) wait_stages<PW, S>(min(S - 2, nk - 2 - kt));
+    barrier();
+    // The last k-step's MFMAs go first (their fragments are already in
+    // registers), so the MFMA pipe does not idle while the DMA and the next
+    // stage's fragment reads are issued; sched_barrier keeps that order.
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(acc, fa[(KS - 1) & 1], fb[(KS - 1) & 1], NMB);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + S < nk) dma(kt % S, kt + S);
+    if (kt + 1 < nk)
+      read_frags_ring<R, FP8, GATEUP>(fa[KS & 1], fb[KS & 1], sc, qb, lds[(kt + 1) % S], 0, wm,
+                                      wn, lane, NMB);
+  }
+}
+
+// ring_kloop with NMB = nmb, chosen outside the loop so that the loop body
+// holds no branch on it.
+template <class R, int N, bool FP8, bool GATEUP, class Dma>
+__device__ __forceinline__ void ring_kloop_n(int nmb, f32x16_t (&acc)[R::MB][R::NB],
+                                             uint4 (*lds)[R::STAGE_U4], int nk, int wm, int wn,
+                                             int lane, const Dma& dma) {
+  if constexpr (N == 0) {
+    ring_kloop<R, 0, FP8, GATEUP>(acc, lds, nk, wm, wn, lane, dma);
+  } else {
+    if (nmb == N) ring_kloop<R, N, FP8, GATEUP>(acc, lds, nk, wm, wn, lane, dma);
+    else ring_kloop_n<R, N - 1, FP8, GATEUP>(nmb, acc, lds, nk, wm, wn, lane, dma);
   }
 }
 
@@ -389,7 +461,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_ring(GemmArgs p) {
   using R = Ring<BM, BN, WM, WN, BK, S, FP8>;
   constexpr int MB = R::MB, NB = R::NB, TN = R::TN;
-  constexpr int PWA = R::PWA, PWB = R::PWB, PW = R::PW, KS = R::KS;
+  constexpr int PWA = R::PWA, PWB = R::PWB, PW = R::PW;
   __shared__ uint4 lds[S][R::STAGE_U4];
   __shared__ int32_t mstart[1025];
 
@@ -482,32 +554,9 @@ grouped_gemm_ring(GemmArgs p) {
       if (s < nk) dma(s, s);
     wait_stages<PW, S>(min(S - 1, nk - 1));
     barrier();
-    bf16x8_t fa[2][MB], fb[2][NB];
-    float sc[NB];
-    read_frags_ring<R, FP8, GATEUP>(fa[0], fb[0], sc, lds[0], 0, wm, wn, lane);
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint4* cur = lds[kt % S];
-#pragma unroll
-      for (int ks = 0; ks + 1 < KS; ++ks) {
-        read_frags_ring<R, FP8, GATEUP>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sc, cur, ks + 1, wm,
-                                        wn, lane);
-        mfma_step(acc, fa[ks & 1], fb[ks & 1]);
-      }
-      // this wave has read all of stage kt and its part of stage kt+1 landed
-      wait_lgkmcnt0();
-      if (kt + 1 < nk) wait_stages<PW, S>(min(S - 2, nk - 2 - kt));
-      barrier();
-      // The last k-step's MFMAs go first (their fragments are already in
-      // registers), so the MFMA pipe does not idle while the DMA and the next
-      // stage's fragment reads are issued; sched_barrier keeps that order.
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(acc, fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + S < nk) dma(kt % S, kt + S);
-      if (kt + 1 < nk)
-        read_frags_ring<R, FP8, GATEUP>(fa[KS & 1], fb[KS & 1], sc, lds[(kt + 1) % S], 0, wm, wn,
-                                        lane);
-    }
+    // 32-row blocks of this wave that hold at least one row of the tile
+    const int nmb = min(MB, max(0, (t.rows - wm * R::TM + 31) / 32));
+    ring_kloop_n<R, MB, FP8, GATEUP>(nmb, acc, lds, nk, wm, wn, lane, dma);
     store_tile<MB, NB, R::TM, R::TN, BN, GATEUP>(p, t, acc, wm, wn, lane);
   }
 }
@@ -679,15 +728,26 @@ int64_t grid_size(const Dims& d, int n_tiles, int occupancy) {
   return (g + 7) / 8 * 8;
 }
 
+// Column tiles per expert: a gate/up tile covers BN / 2 columns of h (BN / 2
+// gate rows and the matching up rows), a down tile BN columns of out_perm.
+template <int BN, bool GATEUP>
+GemmArgs with_tiles(GemmArgs a) {
+  const int cols = GATEUP ? BN / 2 : BN;
+  a.n_tiles = (a.Nout + cols - 1) / cols;
+  return a;
+}
+
 template <int BM, int BN, int WM, int WN, int BK, int S, bool GATEUP, bool FP8>
-hipError_t launch_ring(const Dims& d, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_ring(const Dims& d, const GemmArgs& a0, hipStream_t s) {
+  const GemmArgs a = with_tiles<BN, GATEUP>(a0);
   hipLaunchKernelGGL((grouped_gemm_ring<BM, BN, WM, WN, BK, S, GATEUP, FP8>),
                      dim3((unsigned)grid_size<BM>(d, a.n_tiles, 1)), dim3(64 * WM * WN), 0, s, a);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, bool GATEUP, bool FP8>
-hipError_t launch_regs(const Dims& d, const GemmArgs& a, int occupancy, hipStream_t s) {
+hipError_t launch_regs(const Dims& d, const GemmArgs& a0, int occupancy, hipStream_t s) {
+  const GemmArgs a = with_tiles<BN, GATEUP>(a0);
   hipLaunchKernelGGL((grouped_gemm_regs<BM, BN, WM, WN, GATEUP, FP8>),
                      dim3((unsigned)grid_size<BM>(d, a.n_tiles, occupancy)), dim3(64 * WM * WN),
                      0, s, a);
@@ -697,6 +757,7 @@ hipError_t launch_regs(const Dims& d, const GemmArgs& a, int occupancy, hipStrea
 // Tile shape by the average number of rows per expert (R / E):
 //   <= 48  : 32 x 256 register-staged tiles (decode: the weight stream rules)
 //   <= 384 : 128 x 256 tiles, 8 waves (64 x 64 each), 64-deep stages, 3-stage ring
+//            (4 stages with FP8 weights, whose stages are a third smaller)
 //   else   : 256 x 256 tiles, 8 waves, 32-deep stages, 4-stage ring
 enum class Shape { Small, Mid, Large };
 inline Shape pick(const Dims& d) {
@@ -712,13 +773,11 @@ size_t ffn_ws_bytes(const Dims& d) { return align_up((size_t)d.R * d.F * 2); }
 
 namespace {
 
-// gate/up: every tile covers 128 columns of h (256 weight rows: 128 gate +
-// 128 up); down: 256 columns of out_perm.
 template <bool FP8>
 hipError_t gateup(const Dims& d, const GemmArgs& a, hipStream_t s) {
   switch (pick(d)) {
     case Shape::Small: return launch_regs<32, 256, 1, 4, true, FP8>(d, a, 2, s);
-    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, 3, true, FP8>(d, a, s);
+    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, FP8 ? 4 : 3, true, FP8>(d, a, s);
     default: return launch_ring<256, 256, 2, 4, 32, 4, true, FP8>(d, a, s);
   }
 }
@@ -727,7 +786,7 @@ template <bool FP8>
 hipError_t down(const Dims& d, const GemmArgs& a, hipStream_t s) {
   switch (pick(d)) {
     case Shape::Small: return launch_regs<32, 256, 1, 4, false, FP8>(d, a, 2, s);
-    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, 3, false, FP8>(d, a, s);
+    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, FP8 ? 4 : 3, false, FP8>(d, a, s);
     default: return launch_ring<256, 256, 2, 4, 32, 4, false, FP8>(d, a, s);
   }
 }
@@ -737,14 +796,14 @@ hipError_t down(const Dims& d, const GemmArgs& a, hipStream_t s) {
 hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                 const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                                 hipStream_t s) {
-  return gateup<false>(d, GemmArgs{x_perm, wg, wu, h, offsets, d.E, d.D, d.F, (d.F + 127) / 128,
+  return gateup<false>(d, GemmArgs{x_perm, wg, wu, h, offsets, d.E, d.D, d.F, 0,
                                    nullptr, nullptr}, s);
 }
 
 hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
                               const uint16_t* wd, uint16_t* out_perm, hipStream_t s) {
   return down<false>(d, GemmArgs{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D,
-                                 (d.D + 255) / 256, nullptr, nullptr}, s);
+                                 0, nullptr, nullptr}, s);
 }
 
 hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
@@ -760,13 +819,13 @@ hipError_t launch_expert_gateup_fp8(const Dims& d, const uint16_t* x_perm, const
                                     const Fp8Weight& wg, const Fp8Weight& wu, uint16_t* h,
                                     hipStream_t s) {
   return gateup<true>(d, GemmArgs{x_perm, wg.codes, wu.codes, h, offsets, d.E, d.D, d.F,
-                                  (d.F + 127) / 128, wg.scales, wu.scales}, s);
+                                  0, wg.scales, wu.scales}, s);
 }
 
 hipError_t launch_expert_down_fp8(const Dims& d, const uint16_t* h, const int32_t* offsets,
                                   const Fp8Weight& wd, uint16_t* out_perm, hipStream_t s) {
   return down<true>(d, GemmArgs{h, wd.codes, nullptr, out_perm, offsets, d.E, d.F, d.D,
-                                (d.D + 255) / 256, wd.scales, nullptr}, s);
+                                0, wd.scales, nullptr}, s);
 }
 
 hipError_t launch_grouped_ffn_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,

@@ -156,8 +156,14 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* ms
   const int mt = idx % mt_e;
   const int seg0 = __builtin_amdgcn_readfirstlane(p.offsets[t.e]);
   const int seg1 = __builtin_amdgcn_readfirstlane(p.offsets[t.e + 1]);
-  t.row0 = (int64_t)seg0 + (int64_t)mt * BM;
-  t.rows = min(BM, (int)(seg1 - t.row0));
+  // The expert's ceil(m / 32) row blocks are spread evenly over its mt_e row
+  // tiles (each gets at most BM / 32 of them; only the expert's last block is
+  // partial), so the row tiles that share a weight panel carry equal work and
+  // stay in step through k, and little is computed past the last row.
+  const int m = seg1 - seg0, nbk = (m + 31) / 32;
+  const int b0 = (int)((int64_t)mt * nbk / mt_e), b1 = (int)((int64_t)(mt + 1) * nbk / mt_e);
+  t.row0 = (int64_t)seg0 + 32 * b0;
+  t.rows = min(32 * (b1 - b0), m - 32 * b0);
   return t;
 }
 

@@ -115,6 +115,9 @@ def uniform_ranks(n: int, seed: int, stream: int) -> list:
 # ---------------------------------------------------------------------------
 
 STREAM_X, STREAM_WR, STREAM_WG, STREAM_WU, STREAM_WD, STREAM_BIAS = range(6)
+# streams of the GELU-expert layer with the MLP router
+(STREAM_WPROJ, STREAM_BPROJ, STREAM_WOUT, STREAM_BOUT, STREAM_W1, STREAM_B1, STREAM_W2,
+ STREAM_B2) = range(6, 14)
 
 
 @dataclass(frozen=True)
@@ -131,6 +134,7 @@ class MoEConfig:
     zipf_alpha: Optional[float] = None   # bias = alpha * log Zipf pmf
     capacity: Optional[Tuple[int, int]] = None  # (num, den) capacity factor for the padded run
     note: str = ""
+    expert: str = "swiglu"   # "swiglu" (gate/up/down) or "gelu" (Linear-GELU-Linear, MLP router)
 
     @property
     def S(self) -> int:
@@ -141,7 +145,10 @@ class MoEConfig:
         return 0 if self.gating == "softmax" else 1
 
     def flops(self) -> float:
-        """Algorithmic flops of one forward pass: router + SwiGLU FFN over all slots."""
+        """Algorithmic flops of one forward pass: router + expert FFN over all slots."""
+        if self.expert == "gelu":
+            R = self.D // 4
+            return 2.0 * self.N * (self.D * R + R * self.E) + 4.0 * self.D * self.F * self.S
         return 2.0 * self.N * self.D * self.E + 6.0 * self.D * self.F * self.S
 
     def scaled(self, **kw) -> "MoEConfig":
@@ -161,6 +168,14 @@ CONFIGS: Dict[str, MoEConfig] = {
     "qwen3_decode": MoEConfig("qwen3_decode", N=64, D=2048, E=128, K=8, F=768,
                               gating="softmax", seed=0x5EED0004,
                               note="Qwen3-30B-A3B layer shape, decode step"),
+    # the GELU-expert layer: Linear(D, 4D)-GELU-Linear(4D, D) experts with biases
+    # and the MLP router D -> D/4 (GELU) -> E; top-2 softmax
+    "gelu_mlp": MoEConfig("gelu_mlp", N=4096, D=4096, E=8, K=2, F=16384, gating="softmax",
+                          seed=0x5EED0006, expert="gelu",
+                          note="GELU-expert layer with MLP router (D=4096, F=4D), prefill"),
+    "gelu_tiny": MoEConfig("gelu_tiny", N=64, D=256, E=8, K=2, F=1024, gating="softmax",
+                           seed=0x5EED0007, expert="gelu",
+                           note="tiny GELU-expert layer, oracle in seconds"),
     # zipf_alpha: chosen so that the most-favoured expert receives about a quarter
     # of all slots at this seed (checked by tests/test_oracle_pins.py with the oracle).
     "hot_skew": MoEConfig("hot_skew", N=16384, D=4096, E=64, K=2, F=8192, gating="softmax",
@@ -209,3 +224,29 @@ def make_inputs(cfg: MoEConfig, device="cpu", with_experts: bool = True) -> dict
                 t[e] = expert_weight(cfg, which, e, device)
             out["w_" + which] = t
     return out
+
+
+def make_gelu_inputs(cfg: MoEConfig, device="cpu") -> dict:
+    """All inputs of one GELU-expert layer (nn.Linear layouts, [out, in]).
+
+    Weights have std 1/sqrt(fan_in) and biases std 1/sqrt(3 fan_in) (the
+    spread of nn.Linear's default uniform bias init):
+    x [N,D] bf16 ~ std 1;
+    router: w_proj [D/4, D] bf16, b_proj [D/4] fp32, w_out [E, D/4] fp32, b_out [E] fp32;
+    experts: w1 [E,F,D] bf16, b1 [E,F] fp32, w2 [E,D,F] bf16, b2 [E,D] fp32.
+    """
+    N, D, E, F = cfg.N, cfg.D, cfg.E, cfg.F
+    Dr = D // 4
+    sd, sdr, sf = 1.0 / math.sqrt(D), 1.0 / math.sqrt(Dr), 1.0 / math.sqrt(F)
+    s = cfg.seed
+    return {
+        "x": normal_bf16(N * D, 1.0, s, STREAM_X, device=device).view(N, D),
+        "w_proj": normal_bf16(Dr * D, sd, s, STREAM_WPROJ, device=device).view(Dr, D),
+        "b_proj": normal_f32(Dr, sd / math.sqrt(3.0), s, STREAM_BPROJ, device=device),
+        "w_out": normal_f32(E * Dr, sdr, s, STREAM_WOUT, device=device).view(E, Dr),
+        "b_out": normal_f32(E, sdr / math.sqrt(3.0), s, STREAM_BOUT, device=device),
+        "w1": normal_bf16(E * F * D, sd, s, STREAM_W1, device=device).view(E, F, D),
+        "b1": normal_f32(E * F, sd / math.sqrt(3.0), s, STREAM_B1, device=device).view(E, F),
+        "w2": normal_bf16(E * D * F, sf, s, STREAM_W2, device=device).view(E, D, F),
+        "b2": normal_f32(E * D, sf / math.sqrt(3.0), s, STREAM_B2, device=device).view(E, D),
+    }

@@ -34,6 +34,10 @@ What it computes, step by step, in the order and notation of the pages:
   fraction of slots folded into an EMA, and the per-expert bias moved by
   (E * normalised EMA - 1) * step [ybb.press 4.1, ``_update_load_balance_stats``
   and the bias update in ``load_balance_loss``].
+* The second layer of the pages: experts ``Linear(D, 4D) - GELU -
+  Linear(4D, D)`` with biases, and a router that first compresses the hidden
+  state with a 2-layer MLP (D -> D/4, GELU) before the gate Linear
+  ["MoE工程实战" (jsqmd.com), 3.1 输入表征 and the ``MoELayer`` of 4.2].
 * Block-scaled FP8 expert weights: E4M3 codes with one power-of-two scale
   per 32 values along a weight row's input dimension, and the FFN run on
   their dequantised values [zoe.im 第四层 DeepGEMM & MegaMoE Kernel (FP8
@@ -56,7 +60,10 @@ renormalised; padding rows are zero.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
+from scipy.special import erfc
 
 GATING_SOFTMAX = "softmax"
 GATING_SIGMOID = "sigmoid"
@@ -522,3 +529,95 @@ def expert_ffn_fp8(x_perm_bits, offsets, wg_q, wu_q, wd_q):
     """
     return expert_ffn(x_perm_bits, offsets, dequantize_fp8_bits(*wg_q),
                       dequantize_fp8_bits(*wu_q), dequantize_fp8_bits(*wd_q))
+
+
+# --------------------------------------------------------------------------
+# GELU-expert layer with an MLP router (jsqmd.com 3.1 and 4.2)
+# --------------------------------------------------------------------------
+#
+# Readings: nn.Linear carries a bias unless told otherwise, so every Linear
+# here has one; nn.GELU's default is the exact (erf) form.  Storage points as
+# in the SwiGLU layer: the router's compressed features, the expert hidden
+# activations and the expert outputs are bf16; the gate logits are fp32.  The
+# gate Linear's bias enters the top-K as the per-expert bias (key = logit +
+# bias, one fp32 add), which is the same selection and softmax as on the
+# biased logits.
+
+def gelu(v):
+    """v * Phi(v), Phi(v) = 0.5 (1 + erf(v / sqrt(2))) = 0.5 erfc(-v / sqrt(2)); the
+    erfc form keeps full relative accuracy where 1 + erf cancels (v << 0)."""
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * erfc(-v / math.sqrt(2.0))
+
+
+def mlp_router_features(x_bits, w_proj_bits, b_proj) -> np.ndarray:
+    """a = bf16(GELU(x W_proj^T + b_proj)), [N, D/4]: the compression MLP in
+    front of the gate (jsqmd.com 3.1 输入表征; ``gate_proj`` + ``gate_act``)."""
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_proj_bits)
+    b = np.asarray(b_proj, dtype=np.float32).astype(np.float64)
+    return round_bf16(gelu(x @ w.T + b))
+
+
+def mlp_router_logits(a, w_out) -> np.ndarray:
+    """logits = fp32(a W_out^T) over the compressed features (``gate_out``
+    without its bias, which joins the selection as the per-expert bias)."""
+    a = np.asarray(a, dtype=np.float64)
+    w = np.asarray(w_out, dtype=np.float32).astype(np.float64)
+    return round_f32(a @ w.T)
+
+
+def gelu_ffn_rows(a, w1_bits, b1, w2_bits, b2):
+    """One GELU expert on rows a [m, D]: h = bf16(GELU(a W1^T + b1)),
+    out = bf16(h W2^T + b2); W1 [F, D], W2 [D, F] (nn.Linear layout)."""
+    w1 = bf16_to_f64(w1_bits)
+    w2 = bf16_to_f64(w2_bits)
+    b1 = np.asarray(b1, dtype=np.float32).astype(np.float64)
+    b2 = np.asarray(b2, dtype=np.float32).astype(np.float64)
+    h = round_bf16(gelu(a @ w1.T + b1))
+    out = round_bf16(h @ w2.T + b2)
+    return h, out
+
+
+def expert_ffn_gelu(x_perm_bits, offsets, w1_bits, b1, w2_bits, b2):
+    """Each GELU expert over its own segment; empty experts skipped
+    (jsqmd.com 4.2 ``numel() > 0``).  Padding rows of a capacity-padded
+    buffer are zero inputs and get the expert's response to a zero row.
+    Returns (h [R, F], out_perm [R, D]) as float64 arrays of bf16 values."""
+    xp = bf16_to_f64(x_perm_bits)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = offsets.shape[0] - 1
+    R, D = xp.shape
+    F = np.asarray(w1_bits).shape[1]
+    h_all = np.zeros((R, F))
+    out = np.zeros((R, D))
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi == lo:
+            continue
+        h, o = gelu_ffn_rows(xp[lo:hi], w1_bits[e], b1[e], w2_bits[e], b2[e])
+        h_all[lo:hi] = h
+        out[lo:hi] = o
+    return h_all, out
+
+
+def forward_gelu(x_bits, w_proj_bits, b_proj, w_out, b_out, w1_bits, b1, w2_bits, b2,
+                 K: int, cap: int | None = None, logits=None) -> dict:
+    """The GELU-expert layer: MLP router, top-K with softmax over the K
+    selected (jsqmd.com 4.2), permutation, GELU experts, weighted combine.
+    If ``logits`` is given it replaces the router (selection on exactly the
+    fp32 logits another side produced)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    E = np.asarray(w_out).shape[0]
+    feats = None
+    if logits is None:
+        feats = mlp_router_features(x_bits, w_proj_bits, b_proj)
+        logits = mlp_router_logits(feats, w_out)
+    ids, w = route_from_logits(logits, b_out, K, GATING_SOFTMAX)
+    counts, offsets, row_token, slot_row = permute(ids, E, cap)
+    x_perm = gather_rows(x_bits, row_token)
+    h, out_perm = expert_ffn_gelu(x_perm, offsets, w1_bits, b1, w2_bits, b2)
+    y = combine(out_perm, slot_row, w)
+    return dict(features=feats, logits=logits, topk_ids=ids, topk_weights=w,
+                expert_counts=counts, expert_offsets=offsets, row_token=row_token,
+                slot_row=slot_row, x_perm=x_perm, h=h, out_perm=out_perm, y=y)

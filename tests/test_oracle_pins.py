@@ -548,3 +548,102 @@ def test_expert_ffn_fp8_on_representable_weights():
     got = O.expert_ffn_fp8(x, offs, wg, wu, wd)
     assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
     assert np.abs(got[1]).max() > 0
+
+
+# ------------------------------------------ GELU experts and the MLP router
+# Independent references: torch's own GELU and nn.Linear / nn.Sequential in
+# float64 (the module structure of the page's MoELayer), closed forms of
+# Phi, and a dense brute force of the whole layer.
+
+def _gelu_layer(N, D, E, K, F, seed):
+    cfg = ms.MoEConfig("g", N=N, D=D, E=E, K=K, F=F, gating="softmax", seed=seed, expert="gelu")
+    i = ms.make_gelu_inputs(cfg)
+    return cfg, {k: (_bits(v) if v.dtype == torch.bfloat16 else v.numpy()) for k, v in i.items()}
+
+
+def test_gelu_against_torch_and_closed_forms():
+    v = np.concatenate([np.linspace(-12, 12, 2001), [0.0, 1.0, -1.0, 1e-8, -40.0, 40.0]])
+    ref = torch.nn.functional.gelu(torch.from_numpy(v)).numpy()       # exact erf form
+    assert np.allclose(O.gelu(v), ref, rtol=1e-14, atol=1e-15)   # torch cancels to 0 for v < -8.3
+    assert O.gelu(0.0) == 0.0
+    assert abs(O.gelu(1.0) - 0.8413447460685429) < 1e-15             # Phi(1)
+    assert np.allclose(O.gelu(v) - O.gelu(-v), v, rtol=0, atol=1e-13)  # Phi(v) + Phi(-v) = 1
+    assert O.gelu(40.0) == 40.0 and O.gelu(-40.0) == 0.0
+
+
+def _torch_linear(w, b):
+    lin = torch.nn.Linear(w.shape[1], w.shape[0]).double()
+    with torch.no_grad():
+        lin.weight.copy_(torch.from_numpy(w))
+        lin.bias.copy_(torch.from_numpy(np.asarray(b, dtype=np.float64)))
+    return lin
+
+
+def test_mlp_router_matches_torch_modules():
+    """gate_proj -> GELU -> (bf16 storage) -> gate_out, built as torch modules
+    in float64 from the same weights: features, logits + bias, top-K ids and
+    softmax weights agree."""
+    cfg, t = _gelu_layer(N=40, D=128, E=8, K=2, F=256, seed=71)
+    proj = _torch_linear(O.bf16_to_f64(t["w_proj"]), t["b_proj"])
+    out = _torch_linear(t["w_out"].astype(np.float64), t["b_out"])
+    x = torch.from_numpy(O.bf16_to_f64(t["x"]))
+    with torch.no_grad():
+        a_t = torch.nn.GELU()(proj(x)).to(torch.bfloat16).to(torch.float64)
+        g_t = out(a_t)                                         # biased gate logits
+    a = O.mlp_router_features(t["x"], t["w_proj"], t["b_proj"])
+    assert np.mean(a == a_t.numpy()) > 0.999 and np.abs(a - a_t.numpy()).max() <= 2 ** -6
+    logits = O.mlp_router_logits(a_t.numpy(), t["w_out"])
+    np.testing.assert_allclose(logits + t["b_out"].astype(np.float64), g_t.numpy(),
+                               rtol=1e-6, atol=1e-6)
+    ids, w = O.route_from_logits(logits, t["b_out"], 2, "softmax")
+    tv, ti = torch.topk(g_t, 2, dim=-1)
+    assert np.array_equal(ids, ti.numpy())
+    np.testing.assert_allclose(w, torch.softmax(tv, dim=-1).numpy(), rtol=0, atol=1e-6)
+
+
+def test_gelu_expert_matches_torch_sequential():
+    """One expert as nn.Sequential(Linear(D, F), GELU(), Linear(F, D)) in
+    float64 with the bf16 rounding of the hidden activations: outputs agree
+    to the bf16 rounding (gate/up order, transposes and biases pinned)."""
+    cfg, t = _gelu_layer(N=16, D=64, E=3, K=1, F=256, seed=72)
+    e = 1
+    l1 = _torch_linear(O.bf16_to_f64(t["w1"][e]), t["b1"][e])
+    l2 = _torch_linear(O.bf16_to_f64(t["w2"][e]), t["b2"][e])
+    x = O.bf16_to_f64(t["x"][:16])
+    with torch.no_grad():
+        h_t = torch.nn.GELU()(l1(torch.from_numpy(x))).to(torch.bfloat16).to(torch.float64)
+        o_t = l2(h_t).to(torch.bfloat16).to(torch.float64).numpy()
+    h, o = O.gelu_ffn_rows(x, t["w1"][e], t["b1"][e], t["w2"][e], t["b2"][e])
+    assert np.mean(h == h_t.numpy()) > 0.999
+    o2 = O.gelu_ffn_rows(x, t["w1"][e], t["b1"][e], t["w2"][e], t["b2"][e])[1]
+    assert np.array_equal(o, o2)
+    assert np.mean(o == o_t) > 0.99 and np.abs(o - o_t).max() <= 2 ** -6 * np.abs(o_t).max()
+
+
+@pytest.mark.parametrize("K,cap", [(2, None), (1, None), (2, (5, 4)), (3, (1, 2))])
+def test_gelu_layer_sparse_equals_dense(K, cap):
+    """Every GELU expert on every token, masked by the routing (no
+    permutation), equals the sparse layer; padding rows of a padded buffer
+    hold the experts' response to a zero row and never reach y."""
+    N, D, E, F = 24, 64, 6, 96
+    cfg, t = _gelu_layer(N, D, E, K, F, seed=73)
+    c = O.capacity(N, K, E, *cap) if cap else None
+    res = O.forward_gelu(t["x"], t["w_proj"], t["b_proj"], t["w_out"], t["b_out"], t["w1"],
+                         t["b1"], t["w2"], t["b2"], K, cap=c)
+    ids, w = res["topk_ids"], res["topk_weights"]
+    xs = O.bf16_to_f64(t["x"])
+    outs = np.stack([O.gelu_ffn_rows(xs, t["w1"][e], t["b1"][e], t["w2"][e], t["b2"][e])[1]
+                     for e in range(E)])
+    keep = res["slot_row"].reshape(N, K) >= 0
+    y = np.zeros((N, D))
+    for k in range(K):
+        y += np.where(keep[:, k:k + 1], w[:, k:k + 1].astype(np.float64) * outs[ids[:, k], np.arange(N)], 0.0)
+    ref = O.round_bf16(y)
+    np.testing.assert_allclose(res["y"], ref, rtol=2 ** -7, atol=1e-12)
+    assert np.mean(res["y"] == ref) > 0.99
+    if c is not None:
+        pad = res["row_token"] < 0
+        zero_row = np.stack([O.gelu_ffn_rows(np.zeros((1, D)), t["w1"][e], t["b1"][e], t["w2"][e],
+                                             t["b2"][e])[1][0] for e in range(E)])
+        seg = np.repeat(np.arange(E), c)
+        assert np.array_equal(res["out_perm"][pad], zero_row[seg[pad]])

@@ -8,6 +8,11 @@ issued separately so the dominant kernel (the gate/up grouped GEMM) can be
 bracketed with HIP events on the stream it runs on.  Inputs are synthetic,
 seeded and already resident in HBM when timing starts.
 
+``--config gelu_mlp`` runs the pages' other layer: an MLP router
+(Linear(D, D/4) + GELU, then the gate Linear) and experts
+Linear(D, 4D) - GELU - Linear(4D, D) with biases; its dominant kernel is the
+up GEMM with the bias + GELU epilogue.
+
 With ``--weights fp8`` the expert weights are stored as block-scaled FP8
 (E4M3 codes, one power-of-two scale per 32 values; quantised once before
 timing) and the two grouped GEMMs read them through the FP8 entry points.
@@ -52,7 +57,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral",
-                    help="tiny | mixtral | deepseek_v3 | qwen3_decode | hot_skew")
+                    help="tiny | mixtral | deepseek_v3 | qwen3_decode | hot_skew | gelu_mlp | "
+                         "gelu_tiny")
     ap.add_argument("--padded", action="store_true", help="capacity-padded layout (hot_skew)")
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
@@ -82,8 +88,11 @@ def main():
     cap = cfg.capacity if args.padded else None
     if args.padded and cap is None:
         raise SystemExit(f"{cfg.name} has no capacity factor")
+    gelu = cfg.expert == "gelu"
+    if gelu and args.weights != "bf16":
+        raise SystemExit("the GELU-expert layer runs with bf16 weights")
     t0 = time.time()
-    inp = ms.make_inputs(cfg, device=dev)
+    inp = ms.make_gelu_inputs(cfg, device=dev) if gelu else ms.make_inputs(cfg, device=dev)
     torch.cuda.synchronize()
     print(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
@@ -97,8 +106,12 @@ def main():
     x_perm, h = e(R, D, dt=torch.bfloat16), e(R, F, dt=torch.bfloat16)
     out_perm, y = e(R, D, dt=torch.bfloat16), e(N, D, dt=torch.bfloat16)
     ws = torch.empty(moe.workspace_size(p), dtype=torch.uint8, device=dev)
-    x, wr, bias = inp["x"], inp["w_router"], inp["bias"]
-    wg, wu, wd = inp["w_gate"], inp["w_up"], inp["w_down"]
+    x = inp["x"]
+    if gelu:
+        feats = e(N, D // 4, dt=torch.bfloat16)
+    else:
+        wr, bias = inp["w_router"], inp["bias"]
+        wg, wu, wd = inp["w_gate"], inp["w_up"], inp["w_down"]
     stream = torch.cuda.current_stream()
     fp8 = args.weights == "fp8"
     if fp8:
@@ -112,7 +125,24 @@ def main():
         qg, qu, qd = quant(wg), quant(wu), quant(wd)
         torch.cuda.synchronize()
 
+    def step_gelu(ev=None):
+        i = inp
+        moe.route_mlp(p, x, i["w_proj"], i["b_proj"], i["w_out"], i["b_out"], logits, ids, w, ws,
+                      features=feats, stream=stream)
+        moe.permute(p, x, ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        moe.expert_up_gelu(p, x_perm, offsets, i["w1"], i["b1"], h, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.expert_down_bias(p, h, offsets, i["w2"], i["b2"], out_perm, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
+
     def step(ev=None):
+        if gelu:
+            return step_gelu(ev)
         moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=stream)
         if ev is not None:
@@ -152,14 +182,20 @@ def main():
 
     counts_h = counts.cpu().numpy().astype(np.int64)
     kept = int(np.minimum(counts_h, capv).sum()) if capv else cfg.S
-    flops = 2.0 * N * D * E + 6.0 * D * F * kept        # router + SwiGLU FFN, kept slots
-    tflops = flops / (ms_step * 1e-3) / 1e12
     touched = int((counts_h > 0).sum())
     wb = (1.0 + 1.0 / 32) if fp8 else 2.0          # weight bytes per element (FP8: + scales)
-    weight_bytes = 3.0 * touched * F * D * wb
-    # gate/up grouped GEMM (the dominant kernel): algorithmic work per launch
-    gu_flops = 4.0 * D * F * kept
-    gu_bytes = 2.0 * touched * F * D * wb + kept * D * 2 + kept * F * 2   # Wg+Wu, x_perm, h
+    nmat = 2 if gelu else 3                        # expert matrices
+    if gelu:   # MLP router + Linear-GELU-Linear experts, kept slots
+        flops = 2.0 * N * (D * (D // 4) + (D // 4) * E) + 4.0 * D * F * kept
+    else:      # router + SwiGLU FFN, kept slots
+        flops = 2.0 * N * D * E + 6.0 * D * F * kept
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    weight_bytes = nmat * touched * F * D * wb
+    # the dominant kernel (gate/up grouped GEMM; up GEMM of the GELU experts):
+    # algorithmic work per launch
+    gu_mats = nmat - 1
+    gu_flops = 2.0 * gu_mats * D * F * kept
+    gu_bytes = gu_mats * touched * F * D * wb + kept * D * 2 + kept * F * 2   # weights, x_perm, h
     t_mfma = gu_flops / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = gu_bytes / (PEAK_HBM_GBPS * 1e9)
     if t_mfma >= t_hbm:
@@ -171,7 +207,8 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = (measured_traffic(args.config + ("_fp8" if fp8 else ""))
                        if not capv else None)
-    roof["kernel"] = "grouped gate/up GEMM + SwiGLU"
+    roof["kernel"] = ("grouped up GEMM + bias + GELU" if gelu
+                      else "grouped gate/up GEMM + SwiGLU")
     roof["avg_ms"] = gateup_ms
     roof["algorithmic"] = {"flop": gu_flops, "bytes": gu_bytes}
     line = {
@@ -191,7 +228,9 @@ def main():
                    "tokens": N, "hidden": D, "experts": E, "top_k": K, "ffn": F,
                    "gating": cfg.gating, "capacity": capv or None,
                    "expert_weights": ("fp8 e4m3, power-of-two scale per 32 values"
-                                      if fp8 else "bf16")},
+                                      if fp8 else "bf16"),
+                   "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
+                              else "SwiGLU")},
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "weight_stream_gbps": weight_bytes / (ms_step * 1e-3) / 1e9,
@@ -207,7 +246,8 @@ def main():
           flush=True)
 
     if args.cpu_tokens > 0:
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, N), capv, fp8)
+        line["cpu_baseline"] = (cpu_baseline_gelu(cfg, inp, min(args.cpu_tokens, N)) if gelu else
+                                cpu_baseline(cfg, inp, min(args.cpu_tokens, N), capv, fp8))
     print(json.dumps(line), flush=True)
 
 
@@ -254,6 +294,30 @@ def cpu_baseline(cfg, inp, n, capv, fp8=False):
         cap = O.capacity(n, cfg.K, cfg.E, *cfg.capacity)
     t0 = time.perf_counter()
     O.forward(x, wr, bias, wg, wu, wd, cfg.K, cfg.gating, cap=cap)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.N} tokens, same weights, float64 numpy oracle "
+                      f"({dt:.1f} s)"}
+
+
+def cpu_baseline_gelu(cfg, inp, n):
+    """The CPU oracle of the GELU-expert layer on the first n tokens."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+
+    def h(t):
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    a = {k: h(v) for k, v in inp.items()}
+    t0 = time.perf_counter()
+    O.forward_gelu(a["x"][:n], a["w_proj"], a["b_proj"], a["w_out"], a["b_out"], a["w1"],
+                   a["b1"], a["w2"], a["b2"], cfg.K)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",

@@ -189,6 +189,64 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                        float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------- GELU experts and the MLP router */
+/* The second MoE layer of "MoE工程实战" (jsqmd.com): a router that first
+ * compresses the hidden state with a 2-layer MLP (section 3.1 输入表征:
+ * Linear(D, D/4) + GELU, then the gate Linear(D/4, E)), top-K with softmax
+ * over the selected, and experts Linear(D, 4D) - GELU - Linear(4D, D)
+ * (section 4.2, MoELayer).  Every Linear has its bias (nn.Linear's default);
+ * GELU is the exact form v * Phi(v).  The expert width F is the problem's
+ * `ffn` (4D on the page, any multiple of 64 here).  The MLP router needs
+ * D % 256 == 0 (MOE_ERR_UNSUPPORTED else).  Storage and accumulation as in
+ * the SwiGLU layer: bf16 activations, fp32 accumulation and biases. */
+
+/* MLP router:
+ *   features[n] = bf16( GELU(x[n] . W_proj^T + b_proj) )     [N, D/4]
+ *   logits[n]   = fp32( features[n] . W_out^T )              [N, E] (no bias)
+ *   top-K and weights as moe_route with b_out as the per-expert bias, i.e.
+ *   on the biased gate logits logits + b_out.
+ *   x [N, D] bf16; w_proj [D/4, D] bf16; b_proj [D/4] fp32; w_out [E, D/4]
+ *   fp32; b_out [E] fp32 or NULL (no bias); features bf16 out or NULL (kept in
+ *   the workspace); logits, topk_ids, topk_weights as in moe_route.
+ * Workspace: moe_workspace_size(p) bytes. */
+moe_status moe_route_mlp(const moe_problem* p, const uint16_t* x, const uint16_t* w_proj,
+                         const float* b_proj, const float* w_out, const float* b_out,
+                         uint16_t* features, float* logits, int32_t* topk_ids,
+                         float* topk_weights, void* ws, size_t ws_bytes, void* stream);
+
+/* GELU expert FFN over the permuted rows, for expert e and each row r of its
+ * segment:
+ *   h[r]        = bf16( GELU(x_perm[r] . W1[e]^T + b1[e]) )
+ *   out_perm[r] = bf16( h[r] . W2[e]^T + b2[e] )
+ *   w1 [E, F, D] bf16, b1 [E, F] fp32, w2 [E, D, F] bf16, b2 [E, D] fp32.
+ * Padding rows of a capacity-padded buffer are zero inputs; their out_perm
+ * rows hold the expert's response to a zero row (its biases), which the
+ * combine never reads.  moe_grouped_ffn_gelu = moe_expert_up_gelu followed
+ * by moe_expert_down_bias; arguments, coverage, workspace and errors as in
+ * moe_grouped_ffn / moe_expert_gateup / moe_expert_down. */
+moe_status moe_expert_up_gelu(const moe_problem* p, const uint16_t* x_perm,
+                              const int32_t* expert_offsets, const uint16_t* w1, const float* b1,
+                              uint16_t* h, void* stream);
+moe_status moe_expert_down_bias(const moe_problem* p, const uint16_t* h,
+                                const int32_t* expert_offsets, const uint16_t* w2,
+                                const float* b2, uint16_t* out_perm, void* stream);
+moe_status moe_grouped_ffn_gelu(const moe_problem* p, const uint16_t* x_perm,
+                                const int32_t* expert_offsets, const uint16_t* w1,
+                                const float* b1, const uint16_t* w2, const float* b2,
+                                uint16_t* out_perm, uint16_t* h, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* The whole GELU-expert layer: moe_route_mlp, moe_permute,
+ * moe_grouped_ffn_gelu and moe_unpermute_combine on one stream.  Optional
+ * outputs and workspace as in moe_forward (the features stay in the
+ * workspace). */
+moe_status moe_forward_gelu(const moe_problem* p, const uint16_t* x, const uint16_t* w_proj,
+                            const float* b_proj, const float* w_out, const float* b_out,
+                            const uint16_t* w1, const float* b1, const uint16_t* w2,
+                            const float* b2, uint16_t* y, float* logits, int32_t* topk_ids,
+                            float* topk_weights, int32_t* expert_counts,
+                            int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------ block-scaled FP8 weights */
 /* Expert weights stored as FP8 with block scales, read by the grouped FFN and
  * dequantised inside its kernels: the FP8 weights of the grouped-GEMM kernel

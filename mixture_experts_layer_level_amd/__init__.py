@@ -14,13 +14,17 @@ from ._lib import (  # noqa: F401
     MoEProblem,
     abi_version,
     expert_down,
+    expert_down_bias,
     expert_down_fp8,
     expert_gateup,
     expert_gateup_fp8,
+    expert_up_gelu,
     forward,
     forward_fp8,
+    forward_gelu,
     grouped_ffn,
     grouped_ffn_fp8,
+    grouped_ffn_gelu,
     lib,
     library_path,
     permute,
@@ -28,6 +32,7 @@ from ._lib import (  # noqa: F401
     problem,
     quantize_fp8,
     route,
+    route_mlp,
     routing_stats,
     status_str,
     unpermute_combine,

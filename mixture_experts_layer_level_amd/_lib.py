@@ -68,6 +68,17 @@ def _load():
     L.moe_unpermute_combine.argtypes = [P, vp, vp, vp, vp, vp]
     L.moe_forward.restype = ctypes.c_int
     L.moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route_mlp.restype = ctypes.c_int
+    L.moe_route_mlp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_up_gelu.restype = ctypes.c_int
+    L.moe_expert_up_gelu.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_down_bias.restype = ctypes.c_int
+    L.moe_expert_down_bias.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.moe_grouped_ffn_gelu.restype = ctypes.c_int
+    L.moe_grouped_ffn_gelu.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_forward_gelu.restype = ctypes.c_int
+    L.moe_forward_gelu.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   vp, vp, sz, vp]
     L.moe_quantize_fp8.restype = ctypes.c_int
     L.moe_quantize_fp8.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp]
     L.moe_expert_gateup_fp8.restype = ctypes.c_int
@@ -232,3 +243,43 @@ def forward_fp8(p, x, w_router, bias, w_gate, w_up, w_down, y, ws, logits=None, 
                                _ptr(w_down[0]), _ptr(w_down[1]), _ptr(y), _ptr(logits),
                                _ptr(topk_ids), _ptr(topk_weights), _ptr(counts), _ptr(offsets),
                                _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+# GELU experts and the MLP router.
+
+def route_mlp(p, x, w_proj, b_proj, w_out, b_out, logits, topk_ids, topk_weights, ws,
+              features=None, stream=None):
+    _check("moe_route_mlp", lib.moe_route_mlp(ctypes.byref(p), _ptr(x), _ptr(w_proj),
+                                              _ptr(b_proj), _ptr(w_out), _ptr(b_out),
+                                              _ptr(features), _ptr(logits), _ptr(topk_ids),
+                                              _ptr(topk_weights), _ptr(ws), _nbytes(ws),
+                                              _stream(stream)))
+
+
+def expert_up_gelu(p, x_perm, offsets, w1, b1, h, stream=None):
+    _check("moe_expert_up_gelu", lib.moe_expert_up_gelu(ctypes.byref(p), _ptr(x_perm),
+                                                        _ptr(offsets), _ptr(w1), _ptr(b1),
+                                                        _ptr(h), _stream(stream)))
+
+
+def expert_down_bias(p, h, offsets, w2, b2, out_perm, stream=None):
+    _check("moe_expert_down_bias", lib.moe_expert_down_bias(ctypes.byref(p), _ptr(h),
+                                                            _ptr(offsets), _ptr(w2), _ptr(b2),
+                                                            _ptr(out_perm), _stream(stream)))
+
+
+def grouped_ffn_gelu(p, x_perm, offsets, w1, b1, w2, b2, out_perm, h, ws, stream=None):
+    _check("moe_grouped_ffn_gelu",
+           lib.moe_grouped_ffn_gelu(ctypes.byref(p), _ptr(x_perm), _ptr(offsets), _ptr(w1),
+                                    _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out_perm), _ptr(h),
+                                    _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def forward_gelu(p, x, w_proj, b_proj, w_out, b_out, w1, b1, w2, b2, y, ws, logits=None,
+                 topk_ids=None, topk_weights=None, counts=None, offsets=None, stream=None):
+    _check("moe_forward_gelu",
+           lib.moe_forward_gelu(ctypes.byref(p), _ptr(x), _ptr(w_proj), _ptr(b_proj),
+                                _ptr(w_out), _ptr(b_out), _ptr(w1), _ptr(b1), _ptr(w2),
+                                _ptr(b2), _ptr(y), _ptr(logits), _ptr(topk_ids),
+                                _ptr(topk_weights), _ptr(counts), _ptr(offsets), _ptr(ws),
+                                _nbytes(ws), _stream(stream)))

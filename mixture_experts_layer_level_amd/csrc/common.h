@@ -87,6 +87,22 @@ hipError_t launch_grouped_ffn_fp8(const Dims& d, const uint16_t* x_perm, const i
                                   const Fp8Weight& wg, const Fp8Weight& wu, const Fp8Weight& wd,
                                   uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s);
 
+// GELU-expert layer: up GEMM with bias + GELU epilogue, down GEMM with bias,
+// and the router's compression GEMM (one group of N rows).
+hipError_t launch_expert_up_gelu(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                                 const uint16_t* w1, const float* b1, uint16_t* h,
+                                 hipStream_t s);
+hipError_t launch_expert_down_bias(const Dims& d, const uint16_t* h, const int32_t* offsets,
+                                   const uint16_t* w2, const float* b2, uint16_t* out_perm,
+                                   hipStream_t s);
+hipError_t launch_grouped_ffn_gelu(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                                   const uint16_t* w1, const float* b1, const uint16_t* w2,
+                                   const float* b2, uint16_t* out_perm, uint16_t* h, void* ws,
+                                   hipStream_t s);
+// C[N, Nout] = bf16(GELU(A W^T + bias)); offsets2: 2 int32 of device scratch.
+hipError_t launch_dense_gelu(int64_t N, int Kd, int Nout, const uint16_t* A, const uint16_t* W,
+                             const float* bias, uint16_t* C, int32_t* offsets2, hipStream_t s);
+
 // quant.hip
 hipError_t launch_quantize_fp8(int64_t rows, int cols, const uint16_t* w, uint8_t* codes,
                                uint8_t* scales, hipStream_t s);

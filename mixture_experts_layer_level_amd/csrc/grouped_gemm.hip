@@ -62,7 +62,18 @@ struct GemmArgs {
   int E, Kd, Nout, n_tiles;  // n_tiles: column tiles per expert (set by the launcher)
   const uint8_t* S0;        // FP8 only: scales of B0, [E, Nout/32, Kd/32, 32]
   const uint8_t* S1;        // FP8 only: scales of B1
+  const float* bias;        // bias epilogues: [E, Nout] fp32
 };
+
+// Epilogues: what a tile writes to C.
+constexpr int kEpiSwiglu = 0;    // gate/up tile (interleaved Wg/Wu rows): bf16(silu(g) * u)
+constexpr int kEpiStore = 1;     // bf16(acc)
+constexpr int kEpiBiasGelu = 2;  // bf16(GELU(acc + bias)), GELU(v) = v * Phi(v)
+constexpr int kEpiBias = 3;      // bf16(acc + bias)
+
+__device__ __forceinline__ float gelu(float v) {
+  return 0.5f * v * erfcf(-0.70710678118654752f * v);
+}
 
 // LDS swizzle for rows of RB bytes (16-byte chunks): chunk c of row r is stored
 // at c ^ swz_rows<RB>(r).  256 / RB consecutive rows share one 256-byte bank
@@ -186,7 +197,7 @@ __device__ __forceinline__ int weight_row(int nt, int r, bool& up) {
 // 32x32 block holds C^T: lane l, register v has C row (l % 32) and C column
 // 8*(v/4) + 4*(l/32) + v%4; four consecutive registers are four consecutive
 // columns of one row, stored as one 8-byte write.
-template <int MB, int NB, int TM, int TN, int BN, bool GATEUP>
+template <int MB, int NB, int TM, int TN, int BN, int EPI>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& t,
                                            const f32x16_t (&acc)[MB][NB], int wm, int wn,
                                            int lane) {
@@ -195,7 +206,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& t,
     const int r = wm * TM + mb * 32 + (lane & 31);
     if (r >= t.rows) continue;
     uint16_t* crow = p.C + (t.row0 + r) * p.Nout;
-    if (GATEUP) {
+    if constexpr (EPI == kEpiSwiglu) {
 #pragma unroll
       for (int pr = 0; pr < NB / 2; ++pr)
 #pragma unroll
@@ -218,9 +229,20 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& t,
         for (int g = 0; g < 4; ++g) {
           const int n = t.nt * BN + wn * TN + nb * 32 + 8 * g + 4 * (lane >> 5);
           if (n >= p.Nout) continue;
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = acc[mb][nb][4 * g + q];
+          if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBias) {
+            const float4 b = *reinterpret_cast<const float4*>(p.bias + (size_t)t.e * p.Nout + n);
+            v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+          }
+          if constexpr (EPI == kEpiBiasGelu) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = gelu(v[q]);
+          }
           uint2 o;
-          o.x = pack_bf16x2(acc[mb][nb][4 * g + 0], acc[mb][nb][4 * g + 1]);
-          o.y = pack_bf16x2(acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]);
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
           *reinterpret_cast<uint2*>(crow + n) = o;
         }
     }
@@ -462,9 +484,10 @@ __device__ __forceinline__ void ring_kloop_n(int nmb, f32x16_t (&acc)[R::MB][R::
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int S, bool GATEUP, bool FP8>
+template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_ring(GemmArgs p) {
+  constexpr bool GATEUP = EPI == kEpiSwiglu;
   using R = Ring<BM, BN, WM, WN, BK, S, FP8>;
   constexpr int MB = R::MB, NB = R::NB, TN = R::TN;
   constexpr int PWA = R::PWA, PWB = R::PWB, PW = R::PW;
@@ -563,7 +586,7 @@ grouped_gemm_ring(GemmArgs p) {
     // 32-row blocks of this wave that hold at least one row of the tile
     const int nmb = min(MB, max(0, (t.rows - wm * R::TM + 31) / 32));
     ring_kloop_n<R, MB, FP8, GATEUP>(nmb, acc, lds, nk, wm, wn, lane, dma);
-    store_tile<MB, NB, R::TM, R::TN, BN, GATEUP>(p, t, acc, wm, wn, lane);
+    store_tile<MB, NB, R::TM, R::TN, BN, EPI>(p, t, acc, wm, wn, lane);
   }
 }
 
@@ -623,9 +646,10 @@ __device__ __forceinline__ void stage_lstore(uint4* st, const uint4 (&ra)[NA],
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool GATEUP, bool FP8>
+template <int BM, int BN, int WM, int WN, int EPI, bool FP8>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_regs(GemmArgs p) {
+  constexpr bool GATEUP = EPI == kEpiSwiglu;
   constexpr int NT = 64 * WM * WN;                // threads
   constexpr int TM = BM / WM, TN = BN / WN;       // wave tile
   constexpr int MB = TM / 32, NB = TN / 32;       // 32x32 MFMA blocks per wave
@@ -716,7 +740,7 @@ grouped_gemm_regs(GemmArgs p) {
         mfma_step(acc, af, bfr);
       }
     }
-    store_tile<MB, NB, TM, TN, BN, GATEUP>(p, t, acc, wm, wn, lane);
+    store_tile<MB, NB, TM, TN, BN, EPI>(p, t, acc, wm, wn, lane);
   }
 }
 
@@ -737,24 +761,24 @@ int64_t grid_size(const Dims& d, int n_tiles, int occupancy) {
 // Column tiles per expert: a gate/up tile covers BN / 2 columns of h (BN / 2
 // gate rows and the matching up rows), a down tile BN columns of out_perm.
 template <int BN, bool GATEUP>
-GemmArgs with_tiles(GemmArgs a) {
+GemmArgs with_tiles(GemmArgs a) {  // (GATEUP: interleaved gate/up tile)
   const int cols = GATEUP ? BN / 2 : BN;
   a.n_tiles = (a.Nout + cols - 1) / cols;
   return a;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int S, bool GATEUP, bool FP8>
+template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8>
 hipError_t launch_ring(const Dims& d, const GemmArgs& a0, hipStream_t s) {
-  const GemmArgs a = with_tiles<BN, GATEUP>(a0);
-  hipLaunchKernelGGL((grouped_gemm_ring<BM, BN, WM, WN, BK, S, GATEUP, FP8>),
+  const GemmArgs a = with_tiles<BN, EPI == kEpiSwiglu>(a0);
+  hipLaunchKernelGGL((grouped_gemm_ring<BM, BN, WM, WN, BK, S, EPI, FP8>),
                      dim3((unsigned)grid_size<BM>(d, a.n_tiles, 1)), dim3(64 * WM * WN), 0, s, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, bool GATEUP, bool FP8>
+template <int BM, int BN, int WM, int WN, int EPI, bool FP8>
 hipError_t launch_regs(const Dims& d, const GemmArgs& a0, int occupancy, hipStream_t s) {
-  const GemmArgs a = with_tiles<BN, GATEUP>(a0);
-  hipLaunchKernelGGL((grouped_gemm_regs<BM, BN, WM, WN, GATEUP, FP8>),
+  const GemmArgs a = with_tiles<BN, EPI == kEpiSwiglu>(a0);
+  hipLaunchKernelGGL((grouped_gemm_regs<BM, BN, WM, WN, EPI, FP8>),
                      dim3((unsigned)grid_size<BM>(d, a.n_tiles, occupancy)), dim3(64 * WM * WN),
                      0, s, a);
   return hipGetLastError();
@@ -779,22 +803,19 @@ size_t ffn_ws_bytes(const Dims& d) { return align_up((size_t)d.R * d.F * 2); }
 
 namespace {
 
-template <bool FP8>
-hipError_t gateup(const Dims& d, const GemmArgs& a, hipStream_t s) {
-  switch (pick(d)) {
-    case Shape::Small: return launch_regs<32, 256, 1, 4, true, FP8>(d, a, 2, s);
-    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, FP8 ? 4 : 3, true, FP8>(d, a, s);
-    default: return launch_ring<256, 256, 2, 4, 32, 4, true, FP8>(d, a, s);
+// Tile shape by rows per expert (or as given), for any epilogue.
+template <int EPI, bool FP8>
+hipError_t launch_gemm(const Dims& d, const GemmArgs& a, hipStream_t s, Shape shape) {
+  switch (shape) {
+    case Shape::Small: return launch_regs<32, 256, 1, 4, EPI, FP8>(d, a, 2, s);
+    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, FP8 ? 4 : 3, EPI, FP8>(d, a, s);
+    default: return launch_ring<256, 256, 2, 4, 32, 4, EPI, FP8>(d, a, s);
   }
 }
 
-template <bool FP8>
-hipError_t down(const Dims& d, const GemmArgs& a, hipStream_t s) {
-  switch (pick(d)) {
-    case Shape::Small: return launch_regs<32, 256, 1, 4, false, FP8>(d, a, 2, s);
-    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, FP8 ? 4 : 3, false, FP8>(d, a, s);
-    default: return launch_ring<256, 256, 2, 4, 32, 4, false, FP8>(d, a, s);
-  }
+template <int EPI, bool FP8>
+hipError_t launch_gemm(const Dims& d, const GemmArgs& a, hipStream_t s) {
+  return launch_gemm<EPI, FP8>(d, a, s, pick(d));
 }
 
 }  // namespace
@@ -802,13 +823,13 @@ hipError_t down(const Dims& d, const GemmArgs& a, hipStream_t s) {
 hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                 const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                                 hipStream_t s) {
-  return gateup<false>(d, GemmArgs{x_perm, wg, wu, h, offsets, d.E, d.D, d.F, 0,
+  return launch_gemm<kEpiSwiglu, false>(d, GemmArgs{x_perm, wg, wu, h, offsets, d.E, d.D, d.F, 0,
                                    nullptr, nullptr}, s);
 }
 
 hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
                               const uint16_t* wd, uint16_t* out_perm, hipStream_t s) {
-  return down<false>(d, GemmArgs{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D,
+  return launch_gemm<kEpiStore, false>(d, GemmArgs{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D,
                                  0, nullptr, nullptr}, s);
 }
 
@@ -824,13 +845,13 @@ hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32
 hipError_t launch_expert_gateup_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                     const Fp8Weight& wg, const Fp8Weight& wu, uint16_t* h,
                                     hipStream_t s) {
-  return gateup<true>(d, GemmArgs{x_perm, wg.codes, wu.codes, h, offsets, d.E, d.D, d.F,
+  return launch_gemm<kEpiSwiglu, true>(d, GemmArgs{x_perm, wg.codes, wu.codes, h, offsets, d.E, d.D, d.F,
                                   0, wg.scales, wu.scales}, s);
 }
 
 hipError_t launch_expert_down_fp8(const Dims& d, const uint16_t* h, const int32_t* offsets,
                                   const Fp8Weight& wd, uint16_t* out_perm, hipStream_t s) {
-  return down<true>(d, GemmArgs{h, wd.codes, nullptr, out_perm, offsets, d.E, d.F, d.D,
+  return launch_gemm<kEpiStore, true>(d, GemmArgs{h, wd.codes, nullptr, out_perm, offsets, d.E, d.F, d.D,
                                 0, wd.scales, nullptr}, s);
 }
 
@@ -841,6 +862,62 @@ hipError_t launch_grouped_ffn_fp8(const Dims& d, const uint16_t* x_perm, const i
   hipError_t e = launch_expert_gateup_fp8(d, x_perm, offsets, wg, wu, h, s);
   if (e != hipSuccess) return e;
   return launch_expert_down_fp8(d, h, offsets, wd, out_perm, s);
+}
+
+hipError_t launch_expert_up_gelu(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                                 const uint16_t* w1, const float* b1, uint16_t* h,
+                                 hipStream_t s) {
+  return launch_gemm<kEpiBiasGelu, false>(
+      d, GemmArgs{x_perm, w1, nullptr, h, offsets, d.E, d.D, d.F, 0, nullptr, nullptr, b1}, s);
+}
+
+hipError_t launch_expert_down_bias(const Dims& d, const uint16_t* h, const int32_t* offsets,
+                                   const uint16_t* w2, const float* b2, uint16_t* out_perm,
+                                   hipStream_t s) {
+  return launch_gemm<kEpiBias, false>(
+      d, GemmArgs{h, w2, nullptr, out_perm, offsets, d.E, d.F, d.D, 0, nullptr, nullptr, b2}, s);
+}
+
+hipError_t launch_grouped_ffn_gelu(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
+                                   const uint16_t* w1, const float* b1, const uint16_t* w2,
+                                   const float* b2, uint16_t* out_perm, uint16_t* h, void* ws,
+                                   hipStream_t s) {
+  if (!h) h = static_cast<uint16_t*>(ws);
+  hipError_t e = launch_expert_up_gelu(d, x_perm, offsets, w1, b1, h, s);
+  if (e != hipSuccess) return e;
+  return launch_expert_down_bias(d, h, offsets, w2, b2, out_perm, s);
+}
+
+namespace {
+__global__ void write_offsets_kernel(int32_t* offsets2, int n) {
+  if (threadIdx.x == 0) {
+    offsets2[0] = 0;
+    offsets2[1] = n;
+  }
+}
+}  // namespace
+
+hipError_t launch_dense_gelu(int64_t N, int Kd, int Nout, const uint16_t* A, const uint16_t* W,
+                             const float* bias, uint16_t* C, int32_t* offsets2, hipStream_t s) {
+  hipLaunchKernelGGL(write_offsets_kernel, dim3(1), dim3(64), 0, s, offsets2, (int)N);
+  Dims d{};
+  d.N = N;
+  d.S = N;
+  d.R = N;
+  d.cap = 0;
+  d.D = Kd;
+  d.F = Nout;
+  d.E = 1;
+  d.K = 1;
+  d.padded = false;
+  // One group of N rows: the largest tile that still gives every compute unit
+  // a tile (128 x 256 when it gives at least half of them one).
+  const int64_t cols = (Nout + 255) / 256, cu = device_cu_count();
+  const Shape shape = ((N + 255) / 256) * cols >= cu       ? Shape::Large
+                      : ((N + 127) / 128) * cols * 2 >= cu ? Shape::Mid
+                                                           : Shape::Small;
+  return launch_gemm<kEpiBiasGelu, false>(
+      d, GemmArgs{A, W, nullptr, C, offsets2, 1, Kd, Nout, 0, nullptr, nullptr, bias}, s, shape);
 }
 
 }  // namespace moe

@@ -54,7 +54,7 @@ moe_status check_problem(const moe_problem* p, Dims* d) {
 
 struct ForwardWs {
   size_t logits, ids, weights, counts, offsets, row_token, slot_row, x_perm, out_perm, perm,
-      ffn, total;
+      ffn, feats, roff, total;
 };
 
 ForwardWs forward_layout(const Dims& d) {
@@ -76,6 +76,8 @@ ForwardWs forward_layout(const Dims& d) {
   w.out_perm = take((size_t)d.R * d.D * 2);
   w.perm = take(permute_ws_bytes(d));
   w.ffn = take(ffn_ws_bytes(d));
+  w.feats = take((size_t)d.N * (d.D / 4) * 2);   // MLP router: compressed features
+  w.roff = take(2 * 4);                          // MLP router: offsets {0, N} of its GEMM
   w.total = o;
   return w;
 }
@@ -88,20 +90,19 @@ inline moe_status hip_status(hipError_t e) {
   return MOE_ERR_HIP;
 }
 
-// The layer: route, permute, the grouped FFN given by `ffn`, combine.
-// weights_present / weights_aligned: the caller's checks of its expert weights.
-template <class Ffn>
-moe_status forward_impl(const moe_problem* p, const uint16_t* x, const float* w_router,
-                        const float* expert_bias, bool weights_present, bool weights_aligned,
-                        uint16_t* y, float* logits, int32_t* topk_ids, float* topk_weights,
-                        int32_t* expert_counts, int32_t* expert_offsets, void* ws,
-                        size_t ws_bytes, void* stream, Ffn ffn) {
+// The layer: the routing given by `route`, permute, the grouped FFN given by
+// `ffn`, combine.  weights_present / weights_aligned: the caller's checks of
+// its router and expert weights.
+template <class Route, class Ffn>
+moe_status forward_impl(const moe_problem* p, const uint16_t* x, bool weights_present,
+                        bool weights_aligned, uint16_t* y, float* logits, int32_t* topk_ids,
+                        float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
+                        void* ws, size_t ws_bytes, void* stream, Route route, Ffn ffn) {
   Dims d;
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
-  if (!x || !w_router || !y || !weights_present) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(y) || !weights_aligned)
-    return MOE_ERR_UNSUPPORTED;
+  if (!x || !y || !weights_present) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !weights_aligned) return MOE_ERR_UNSUPPORTED;
   const ForwardWs L = forward_layout(d);
   if (d.N > 0 && (!ws || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
@@ -118,9 +119,7 @@ moe_status forward_impl(const moe_problem* p, const uint16_t* x, const float* w_
   uint16_t* x_perm = reinterpret_cast<uint16_t*>(base + L.x_perm);
   uint16_t* out_perm = reinterpret_cast<uint16_t*>(base + L.out_perm);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(launch_router_gemm(d, x, w_router, logits, s));
-  if (st != MOE_OK) return st;
-  st = hip_status(launch_topk(d, logits, expert_bias, topk_ids, topk_weights, s));
+  st = hip_status(route(d, logits, topk_ids, topk_weights, base, L, s));
   if (st != MOE_OK) return st;
   st = hip_status(launch_permute(d, x, topk_ids, expert_counts, expert_offsets, row_token,
                                  slot_row, x_perm, base + L.perm, s));
@@ -128,6 +127,22 @@ moe_status forward_impl(const moe_problem* p, const uint16_t* x, const float* w_
   st = hip_status(ffn(d, x_perm, expert_offsets, out_perm, base + L.ffn, s));
   if (st != MOE_OK) return st;
   return hip_status(launch_combine(d, out_perm, slot_row, topk_weights, y, s));
+}
+
+// The MLP router: features = bf16(GELU(x W_proj^T + b_proj)) as a one-group
+// grouped GEMM, logits = features W_out^T by the router kernel, then top-K with
+// b_out as the per-expert bias.
+hipError_t launch_route_mlp(const Dims& d, const uint16_t* x, const uint16_t* w_proj,
+                            const float* b_proj, const float* w_out, const float* b_out,
+                            uint16_t* feats, int32_t* offsets2, float* logits, int32_t* ids,
+                            float* weights, hipStream_t s) {
+  hipError_t e = launch_dense_gelu(d.N, d.D, d.D / 4, x, w_proj, b_proj, feats, offsets2, s);
+  if (e != hipSuccess) return e;
+  Dims dr = d;
+  dr.D = d.D / 4;
+  e = launch_router_gemm(dr, feats, w_out, logits, s);
+  if (e != hipSuccess) return e;
+  return launch_topk(d, logits, b_out, ids, weights, s);
 }
 
 // Block-scaled FP8 weight stack: codes and scales present and 16-byte aligned.
@@ -300,10 +315,16 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                        const uint16_t* w_down, uint16_t* y, float* logits, int32_t* topk_ids,
                        float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
                        void* ws, size_t ws_bytes, void* stream) {
-  const bool present = w_gate && w_up && w_down;
-  const bool aligned = aligned16(w_gate) && aligned16(w_up) && aligned16(w_down);
-  return forward_impl(p, x, w_router, expert_bias, present, aligned, y, logits, topk_ids,
-                      topk_weights, expert_counts, expert_offsets, ws, ws_bytes, stream,
+  const bool present = w_router && w_gate && w_up && w_down;
+  const bool aligned = aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) &&
+                       aligned16(w_down);
+  return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
+                      expert_offsets, ws, ws_bytes, stream,
+                      [&](const Dims& d, float* lg, int32_t* ids, float* w, char*,
+                          const ForwardWs&, hipStream_t s) {
+                        const hipError_t e = launch_router_gemm(d, x, w_router, lg, s);
+                        return e != hipSuccess ? e : launch_topk(d, lg, expert_bias, ids, w, s);
+                      },
                       [&](const Dims& d, const uint16_t* xp, const int32_t* offs, uint16_t* op,
                           void* fws, hipStream_t s) {
                         return launch_grouped_ffn(d, xp, offs, w_gate, w_up, w_down, op, nullptr,
@@ -402,20 +423,131 @@ moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float*
                            const uint8_t* w_down_scales, uint16_t* y, float* logits,
                            int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
                            int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream) {
-  const bool present = fp8_present(w_gate_codes, w_gate_scales) &&
+  const bool present = w_router && fp8_present(w_gate_codes, w_gate_scales) &&
                        fp8_present(w_up_codes, w_up_scales) &&
                        fp8_present(w_down_codes, w_down_scales);
-  const bool aligned = fp8_aligned(w_gate_codes, w_gate_scales) &&
+  const bool aligned = aligned16(w_router) && fp8_aligned(w_gate_codes, w_gate_scales) &&
                        fp8_aligned(w_up_codes, w_up_scales) &&
                        fp8_aligned(w_down_codes, w_down_scales);
   const Fp8Weight wg{w_gate_codes, w_gate_scales}, wu{w_up_codes, w_up_scales},
       wd{w_down_codes, w_down_scales};
-  return forward_impl(p, x, w_router, expert_bias, present, aligned, y, logits, topk_ids,
-                      topk_weights, expert_counts, expert_offsets, ws, ws_bytes, stream,
+  return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
+                      expert_offsets, ws, ws_bytes, stream,
+                      [&](const Dims& d, float* lg, int32_t* ids, float* w, char*,
+                          const ForwardWs&, hipStream_t s) {
+                        const hipError_t e = launch_router_gemm(d, x, w_router, lg, s);
+                        return e != hipSuccess ? e : launch_topk(d, lg, expert_bias, ids, w, s);
+                      },
                       [&](const Dims& d, const uint16_t* xp, const int32_t* offs, uint16_t* op,
                           void* fws, hipStream_t s) {
                         return launch_grouped_ffn_fp8(d, xp, offs, wg, wu, wd, op, nullptr, fws,
                                                       s);
+                      });
+}
+
+moe_status moe_route_mlp(const moe_problem* p, const uint16_t* x, const uint16_t* w_proj,
+                         const float* b_proj, const float* w_out, const float* b_out,
+                         uint16_t* features, float* logits, int32_t* topk_ids,
+                         float* topk_weights, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !w_proj || !b_proj || !w_out || !logits || !topk_ids || !topk_weights)
+    return MOE_ERR_INVALID_ARG;
+  if (d.D % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_proj) || !aligned16(b_proj) || !aligned16(w_out) ||
+      (features && !aligned16(features)))
+    return MOE_ERR_UNSUPPORTED;
+  const ForwardWs L = forward_layout(d);
+  if (d.N > 0 && (!ws || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  char* base = static_cast<char*>(ws);
+  if (!features) features = reinterpret_cast<uint16_t*>(base + L.feats);
+  return hip_status(launch_route_mlp(d, x, w_proj, b_proj, w_out, b_out, features,
+                                     reinterpret_cast<int32_t*>(base + L.roff), logits, topk_ids,
+                                     topk_weights, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_up_gelu(const moe_problem* p, const uint16_t* x_perm,
+                              const int32_t* expert_offsets, const uint16_t* w1, const float* b1,
+                              uint16_t* h, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !w1 || !b1 || !h) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(b1) || !aligned16(h))
+    return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_up_gelu(d, x_perm, expert_offsets, w1, b1, h,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_down_bias(const moe_problem* p, const uint16_t* h,
+                                const int32_t* expert_offsets, const uint16_t* w2,
+                                const float* b2, uint16_t* out_perm, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!h || !expert_offsets || !w2 || !b2 || !out_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w2) || !aligned16(b2) || !aligned16(out_perm))
+    return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_down_bias(d, h, expert_offsets, w2, b2, out_perm,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_ffn_gelu(const moe_problem* p, const uint16_t* x_perm,
+                                const int32_t* expert_offsets, const uint16_t* w1,
+                                const float* b1, const uint16_t* w2, const float* b2,
+                                uint16_t* out_perm, uint16_t* h, void* ws, size_t ws_bytes,
+                                void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !w1 || !b1 || !w2 || !b2 || !out_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(b1) || !aligned16(w2) ||
+      !aligned16(b2) || !aligned16(out_perm) || (h && !aligned16(h)))
+    return MOE_ERR_UNSUPPORTED;
+  const size_t need = h ? 0 : ffn_ws_bytes(d);
+  if (d.N > 0 && need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_grouped_ffn_gelu(d, x_perm, expert_offsets, w1, b1, w2, b2, out_perm,
+                                            h, ws, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward_gelu(const moe_problem* p, const uint16_t* x, const uint16_t* w_proj,
+                            const float* b_proj, const float* w_out, const float* b_out,
+                            const uint16_t* w1, const float* b1, const uint16_t* w2,
+                            const float* b2, uint16_t* y, float* logits, int32_t* topk_ids,
+                            float* topk_weights, int32_t* expert_counts,
+                            int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  const bool present = w_proj && b_proj && w_out && w1 && b1 && w2 && b2;
+  const bool aligned = aligned16(w_proj) && aligned16(b_proj) && aligned16(w_out) &&
+                       aligned16(w1) && aligned16(b1) && aligned16(w2) && aligned16(b2);
+  if (present && aligned && x && y && d.D % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
+                      expert_offsets, ws, ws_bytes, stream,
+                      [&](const Dims& dd, float* lg, int32_t* ids, float* w, char* base,
+                          const ForwardWs& L, hipStream_t s) {
+                        return launch_route_mlp(dd, x, w_proj, b_proj, w_out, b_out,
+                                                reinterpret_cast<uint16_t*>(base + L.feats),
+                                                reinterpret_cast<int32_t*>(base + L.roff), lg,
+                                                ids, w, s);
+                      },
+                      [&](const Dims& dd, const uint16_t* xp, const int32_t* offs, uint16_t* op,
+                          void* fws, hipStream_t s) {
+                        return launch_grouped_ffn_gelu(dd, xp, offs, w1, b1, w2, b2, op, nullptr,
+                                                       fws, s);
                       });
 }
 

@@ -341,14 +341,17 @@ def forward(x_bits, w_router, bias, w_gate_bits, w_up_bits, w_down_bits,
                 x_perm=x_perm, h=h, out_perm=out_perm, y=y)
 
 
-def token_outputs(x_bits, topk_ids, topk_w, kept_mask, expert_weights):
+def token_outputs(x_bits, topk_ids, topk_w, kept_mask, expert_weights, rows_fn=None):
     """y for a subset of tokens, one token at a time (for large layers).
 
     x_bits [n, D]; topk_ids / topk_w / kept_mask [n, K]; ``expert_weights(e)``
-    returns (Wg, Wu, Wd) bf16 bit arrays of expert e.  Per token:
+    returns the weights of expert e as ``rows_fn`` takes them after the rows:
+    (Wg, Wu, Wd) bf16 bit arrays for the SwiGLU expert (default), (W1, b1,
+    W2, b2) with ``rows_fn=gelu_ffn_rows``.  Per token:
     y = bf16(sum_k w_k * out_k) with out_k the expert FFN of that token's row.
     Returns (y [n, D], out [n, K, D]) as float64 arrays of bf16 values.
     """
+    rows_fn = swiglu_rows if rows_fn is None else rows_fn
     xs = bf16_to_f64(x_bits)
     n, K = np.asarray(topk_ids).shape
     D = xs.shape[1]
@@ -359,9 +362,8 @@ def token_outputs(x_bits, topk_ids, topk_w, kept_mask, expert_weights):
             if kept_mask[t, k]:
                 need.setdefault(int(topk_ids[t, k]), []).append((t, k))
     for e, pairs in sorted(need.items()):
-        wg, wu, wd = expert_weights(e)
         rows = np.stack([xs[t] for t, _ in pairs])
-        _, o = swiglu_rows(rows, wg, wu, wd)
+        _, o = rows_fn(rows, *expert_weights(e))
         for j, (t, k) in enumerate(pairs):
             outs[t, k] = o[j]
     w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
@@ -602,18 +604,20 @@ def expert_ffn_gelu(x_perm_bits, offsets, w1_bits, b1, w2_bits, b2):
 
 
 def forward_gelu(x_bits, w_proj_bits, b_proj, w_out, b_out, w1_bits, b1, w2_bits, b2,
-                 K: int, cap: int | None = None, logits=None) -> dict:
+                 K: int, cap: int | None = None, logits=None,
+                 gating: str = GATING_SOFTMAX) -> dict:
     """The GELU-expert layer: MLP router, top-K with softmax over the K
-    selected (jsqmd.com 4.2), permutation, GELU experts, weighted combine.
-    If ``logits`` is given it replaces the router (selection on exactly the
-    fp32 logits another side produced)."""
+    selected (jsqmd.com 4.2; ``gating`` may also name the sigmoid variant),
+    permutation, GELU experts, weighted combine.  If ``logits`` is given it
+    replaces the router (selection on exactly the fp32 logits another side
+    produced)."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     E = np.asarray(w_out).shape[0]
     feats = None
     if logits is None:
         feats = mlp_router_features(x_bits, w_proj_bits, b_proj)
         logits = mlp_router_logits(feats, w_out)
-    ids, w = route_from_logits(logits, b_out, K, GATING_SOFTMAX)
+    ids, w = route_from_logits(logits, b_out, K, gating)
     counts, offsets, row_token, slot_row = permute(ids, E, cap)
     x_perm = gather_rows(x_bits, row_token)
     h, out_perm = expert_ffn_gelu(x_perm, offsets, w1_bits, b1, w2_bits, b2)

@@ -184,3 +184,54 @@ def check_sampled_outputs(L: Layer, y_gpu: torch.Tensor, tokens):
     y_ref, _ = O.token_outputs(x_bits, ids, w, kept, L.expert_bits)
     y = O.bf16_to_f64(bits(y_gpu)[tokens])
     assert_fp_close(y, y_ref, f"y[{len(tokens)} sampled tokens]")
+
+
+class GeluLayer:
+    """Inputs of the GELU-expert layer on the GPU plus every buffer of its staged path."""
+
+    def __init__(self, cfg: ms.MoEConfig, padded: bool = False):
+        self.cfg = cfg
+        self.inp = ms.make_gelu_inputs(cfg, device=DEV)
+        cap = cfg.capacity if padded else None
+        self.p = moe.problem(cfg.N, cfg.D, cfg.F, cfg.E, cfg.K, cfg.gating, cap)
+        self.R, self.cap = moe.permuted_rows(self.p)
+        N, D, E, K, F, R = cfg.N, cfg.D, cfg.E, cfg.K, cfg.F, self.R
+        z = lambda *s, dt=torch.float32: torch.empty(*s, dtype=dt, device=DEV)
+        self.feats = z(N, D // 4, dt=torch.bfloat16)
+        self.logits = z(N, E)
+        self.ids = z(N, K, dt=torch.int32)
+        self.w = z(N, K)
+        self.counts = z(E, dt=torch.int32)
+        self.offsets = z(E + 1, dt=torch.int32)
+        self.row_token = z(R, dt=torch.int32)
+        self.slot_row = z(N * K, dt=torch.int32)
+        self.x_perm = z(R, D, dt=torch.bfloat16)
+        self.h = z(R, F, dt=torch.bfloat16)
+        self.out_perm = z(R, D, dt=torch.bfloat16)
+        self.y = z(N, D, dt=torch.bfloat16)
+        self.ws = torch.empty(max(moe.workspace_size(self.p), 256), dtype=torch.uint8, device=DEV)
+
+    def staged(self):
+        i, p = self.inp, self.p
+        moe.route_mlp(p, i["x"], i["w_proj"], i["b_proj"], i["w_out"], i["b_out"], self.logits,
+                      self.ids, self.w, self.ws, features=self.feats)
+        moe.permute(p, i["x"], self.ids, self.counts, self.offsets, self.row_token,
+                    self.slot_row, self.x_perm, self.ws)
+        moe.expert_up_gelu(p, self.x_perm, self.offsets, i["w1"], i["b1"], self.h)
+        moe.expert_down_bias(p, self.h, self.offsets, i["w2"], i["b2"], self.out_perm)
+        moe.unpermute_combine(p, self.out_perm, self.slot_row, self.w, self.y)
+        torch.cuda.synchronize()
+
+    def forward(self, y_out):
+        i = self.inp
+        moe.forward_gelu(self.p, i["x"], i["w_proj"], i["b_proj"], i["w_out"], i["b_out"],
+                         i["w1"], i["b1"], i["w2"], i["b2"], y_out, self.ws)
+        torch.cuda.synchronize()
+
+    def host(self, name):
+        t = self.inp[name]
+        return bits(t) if t.dtype == torch.bfloat16 else np_(t)
+
+    def expert(self, e):
+        return (bits(self.inp["w1"][e]), np_(self.inp["b1"][e]), bits(self.inp["w2"][e]),
+                np_(self.inp["b2"][e]))

@@ -182,3 +182,41 @@ def test_fp8_argument_checks():
     assert fw(*bad, FAKE, need, None) == UNSUPPORTED
     assert fw(*args, FAKE, need - 1, None) == WORKSPACE
     assert fw(ctypes.byref(P(N=0)), *args[1:], None, 0, None) == OK
+
+
+def test_gelu_layer_argument_checks():
+    L = moe.lib
+    p = P(D=256)
+    bp = ctypes.byref(p)
+    need = moe.workspace_size(p)
+    r = L.moe_route_mlp
+    # x, w_proj, b_proj, w_out required; b_out optional
+    assert r(bp, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, need, None) == INVALID
+    assert r(bp, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, need, None) == INVALID
+    assert r(bp, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert r(ctypes.byref(P(D=192)), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE,
+             1 << 30, None) == UNSUPPORTED                              # D % 256 != 0
+    assert r(bp, FAKE + 2, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, need, None) \
+        == UNSUPPORTED
+    assert r(ctypes.byref(P(N=0, D=256)), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+             None, 0, None) == OK
+    u = L.moe_expert_up_gelu
+    assert u(bp, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID         # b1 required
+    assert u(bp, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == UNSUPPORTED
+    d = L.moe_expert_down_bias
+    assert d(bp, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
+    f = L.moe_grouped_ffn_gelu
+    assert f(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == WORKSPACE
+    assert f(bp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == INVALID
+    fw = L.moe_forward_gelu
+    args = [bp, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE] + [None] * 5
+    assert fw(*args, FAKE, need - 1, None) == WORKSPACE
+    bad = list(args)
+    bad[9] = None                                                       # b2 missing
+    assert fw(*bad, FAKE, need, None) == INVALID
+    bad = list(args)
+    bad[7] = FAKE + 8                                                   # b1 misaligned
+    assert fw(*bad, FAKE, need, None) == UNSUPPORTED
+    args192 = [ctypes.byref(P(D=192))] + args[1:]
+    assert fw(*args192, FAKE, 1 << 30, None) == UNSUPPORTED             # D % 256 != 0
+    assert fw(ctypes.byref(P(N=0, D=256)), *args[1:], None, 0, None) == OK

@@ -647,3 +647,16 @@ def test_gelu_layer_sparse_equals_dense(K, cap):
                                              t["b2"][e])[1][0] for e in range(E)])
         seg = np.repeat(np.arange(E), c)
         assert np.array_equal(res["out_perm"][pad], zero_row[seg[pad]])
+
+
+def test_token_outputs_gelu_matches_forward_gelu():
+    N, D, E, K, F = 20, 64, 5, 2, 128
+    cfg, t = _gelu_layer(N, D, E, K, F, seed=74)
+    res = O.forward_gelu(t["x"], t["w_proj"], t["b_proj"], t["w_out"], t["b_out"], t["w1"],
+                         t["b1"], t["w2"], t["b2"], K)
+    tok = np.array([0, 3, 7, 19])
+    y, _ = O.token_outputs(t["x"][tok], res["topk_ids"][tok], res["topk_weights"][tok],
+                           np.ones((len(tok), K), dtype=bool),
+                           lambda e: (t["w1"][e], t["b1"][e], t["w2"][e], t["b2"][e]),
+                           rows_fn=O.gelu_ffn_rows)
+    assert np.array_equal(y, res["y"][tok])

@@ -60,6 +60,9 @@ def main():
                     help="tiny | mixtral | deepseek_v3 | qwen3_decode | hot_skew | gelu_mlp | "
                          "gelu_tiny")
     ap.add_argument("--padded", action="store_true", help="capacity-padded layout (hot_skew)")
+    ap.add_argument("--fused", action="store_true",
+                    help="the expert FFN as one persistent launch (moe_fused_ffn; rows gathered "
+                         "from x, no permuted copy)")
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
     ap.add_argument("--cpu-tokens", type=int, default=192,
@@ -73,7 +76,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              f"(this build has no multi-GPU path)", file=sys.stderr)
+              f"(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -89,6 +92,11 @@ def main():
     if args.padded and cap is None:
         raise SystemExit(f"{cfg.name} has no capacity factor")
     gelu = cfg.expert == "gelu"
+    if args.fused:
+        raise SystemExit("--fused: the fused FFN launch is switched off in the library "
+                         "(moe_fused_ffn returns MOE_ERR_UNSUPPORTED)")
+    if args.fused and (gelu or args.weights != "bf16" or args.padded):
+        raise SystemExit("--fused runs the SwiGLU layer, bf16 weights, contiguous layout")
     if gelu and args.weights != "bf16":
         raise SystemExit("the GELU-expert layer runs with bf16 weights")
     t0 = time.time()
@@ -140,9 +148,22 @@ def main():
             ev[2].record(stream)
         moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
 
+    def step_fused(ev=None):
+        moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
+        moe.permute(p, x, ids, counts, offsets, row_token, slot_row, None, ws, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        moe.fused_ffn(p, x, row_token, offsets, wg, wu, wd, out_perm, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+            ev[2].record(stream)
+        moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
+
     def step(ev=None):
         if gelu:
             return step_gelu(ev)
+        if args.fused:
+            return step_fused(ev)
         moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=stream)
         if ev is not None:
@@ -209,8 +230,23 @@ def main():
                        if not capv else None)
     roof["kernel"] = ("grouped up GEMM + bias + GELU" if gelu
                       else "grouped gate/up GEMM + SwiGLU")
+    if args.fused:
+        # the one fused launch: gate/up, SwiGLU and down of every expert
+        f_flops = 6.0 * D * F * kept
+        f_bytes = 3.0 * touched * F * D * 2 + kept * D * 2 * 2 + kept * F * 2 * 2
+        t_m, t_h = f_flops / (PEAK_BF16_TFLOPS * 1e12), f_bytes / (PEAK_HBM_GBPS * 1e9)
+        if t_m >= t_h:
+            roof = {"bound": "mfma", "achieved": f_flops / (gateup_ms * 1e-3) / 1e12,
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        else:
+            roof = {"bound": "hbm", "achieved": f_bytes / (gateup_ms * 1e-3) / 1e9,
+                    "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = None
+        roof["kernel"] = "fused expert FFN (gate/up + SwiGLU + down, one launch)"
+        roof["algorithmic"] = {"flop": f_flops, "bytes": f_bytes}
     roof["avg_ms"] = gateup_ms
-    roof["algorithmic"] = {"flop": gu_flops, "bytes": gu_bytes}
+    roof.setdefault("algorithmic", {"flop": gu_flops, "bytes": gu_bytes})
     line = {
         "metric": "MoE-layer tokens/sec + TFLOPS (% bf16 MFMA peak) / HBM GB/s (% peak), 1 GPU",
         "value": N / (ms_step * 1e-3),
@@ -230,7 +266,8 @@ def main():
                    "expert_weights": ("fp8 e4m3, power-of-two scale per 32 values"
                                       if fp8 else "bf16"),
                    "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
-                              else "SwiGLU")},
+                              else "SwiGLU"),
+                   "ffn_launch": "fused (one persistent launch)" if args.fused else "two grouped GEMMs"},
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "weight_stream_gbps": weight_bytes / (ms_step * 1e-3) / 1e9,

@@ -129,7 +129,8 @@ moe_status moe_route(const moe_problem* p, const uint16_t* x, const float* w_rou
  *   row_token      [R] int32 out: token of each row, -1 for padding rows.
  *   slot_row       [N*K] int32 out: row of each slot, -1 if dropped.
  *   x_perm         [R, D] bf16 out: x_perm[r] = x[row_token[r]], padding
- *                  rows zero.
+ *                  rows zero; or NULL: only the routing tables are written
+ *                  (for moe_fused_ffn, which gathers from x itself).
  * Workspace: moe_workspace_size bytes suffice. */
 moe_status moe_permute(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
@@ -188,6 +189,44 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                        const uint16_t* w_down, uint16_t* y, float* logits, int32_t* topk_ids,
                        float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ fused FFN */
+/* NOT AVAILABLE IN THIS BUILD: after their argument checks, moe_fused_ffn and
+ * moe_forward_fused return MOE_ERR_UNSUPPORTED (their persistent launch did
+ * not complete on MI355X and is switched off until the cause is found).  The
+ * contract below is the one they are built to. */
+/* The whole expert FFN as one persistent launch (the single-kernel MoE of
+ * "MoE 推理完整机制" (zoe.im) 第四层, DeepGEMM & MegaMoE Kernel: workgroups
+ * take gate/up and down tiles of every expert from one work list).  Same
+ * results as moe_grouped_ffn on x_perm = x[row_token] (bit for bit), but the
+ * gate/up tiles gather their rows from x through row_token, so no permuted
+ * copy of x exists, and down tiles of an expert's rows start as soon as that
+ * row range's h is complete.  Contiguous layout only (MOE_ERR_UNSUPPORTED
+ * for a padded problem) and N * D * 2 < 2^32 bytes of x.
+ *   x [N, D] bf16; row_token [R] int32 and expert_offsets [E+1] int32 as
+ *   written by moe_permute; weights as moe_grouped_ffn; out_perm [R, D] out.
+ * Workspace: moe_workspace_size(p) bytes suffice (it holds h and the
+ * launch's counters).  A wait inside the launch is bounded: if one ever ran
+ * past its bound the results are wrong and the int32 error word at byte
+ * offset moe_fused_error_offset(p, 0, &off) of the workspace is nonzero after
+ * the call completes (zero otherwise). */
+moe_status moe_fused_ffn(const moe_problem* p, const uint16_t* x, const int32_t* row_token,
+                         const int32_t* expert_offsets, const uint16_t* w_gate,
+                         const uint16_t* w_up, const uint16_t* w_down, uint16_t* out_perm,
+                         void* ws, size_t ws_bytes, void* stream);
+/* moe_forward with the fused FFN: moe_route, moe_permute (routing tables only,
+ * no x_perm), moe_fused_ffn and moe_unpermute_combine.  Arguments as
+ * moe_forward; contiguous layout only.  Its error word is at
+ * moe_fused_error_offset(p, 1, &off). */
+moe_status moe_forward_fused(const moe_problem* p, const uint16_t* x, const float* w_router,
+                             const float* expert_bias, const uint16_t* w_gate,
+                             const uint16_t* w_up, const uint16_t* w_down, uint16_t* y,
+                             float* logits, int32_t* topk_ids, float* topk_weights,
+                             int32_t* expert_counts, int32_t* expert_offsets, void* ws,
+                             size_t ws_bytes, void* stream);
+/* Host only: byte offset of the fused launch's error word in the workspace of
+ * moe_fused_ffn (whole_layer = 0) or moe_forward_fused (whole_layer = 1). */
+moe_status moe_fused_error_offset(const moe_problem* p, int32_t whole_layer, size_t* offset);
 
 /* ------------------------------------------- GELU experts and the MLP router */
 /* The second MoE layer of "MoE工程实战" (jsqmd.com): a router that first

@@ -21,7 +21,10 @@ from ._lib import (  # noqa: F401
     expert_up_gelu,
     forward,
     forward_fp8,
+    forward_fused,
     forward_gelu,
+    fused_error_offset,
+    fused_ffn,
     grouped_ffn,
     grouped_ffn_fp8,
     grouped_ffn_gelu,

@@ -68,6 +68,12 @@ def _load():
     L.moe_unpermute_combine.argtypes = [P, vp, vp, vp, vp, vp]
     L.moe_forward.restype = ctypes.c_int
     L.moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_fused_ffn.restype = ctypes.c_int
+    L.moe_fused_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_forward_fused.restype = ctypes.c_int
+    L.moe_forward_fused.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_fused_error_offset.restype = ctypes.c_int
+    L.moe_fused_error_offset.argtypes = [P, ctypes.c_int32, ctypes.POINTER(sz)]
     L.moe_route_mlp.restype = ctypes.c_int
     L.moe_route_mlp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_up_gelu.restype = ctypes.c_int
@@ -283,3 +289,29 @@ def forward_gelu(p, x, w_proj, b_proj, w_out, b_out, w1, b1, w2, b2, y, ws, logi
                                 _ptr(b2), _ptr(y), _ptr(logits), _ptr(topk_ids),
                                 _ptr(topk_weights), _ptr(counts), _ptr(offsets), _ptr(ws),
                                 _nbytes(ws), _stream(stream)))
+
+
+# The fused FFN (one persistent launch, rows gathered from x).
+
+def fused_ffn(p, x, row_token, offsets, w_gate, w_up, w_down, out_perm, ws, stream=None):
+    _check("moe_fused_ffn", lib.moe_fused_ffn(ctypes.byref(p), _ptr(x), _ptr(row_token),
+                                              _ptr(offsets), _ptr(w_gate), _ptr(w_up),
+                                              _ptr(w_down), _ptr(out_perm), _ptr(ws), _nbytes(ws),
+                                              _stream(stream)))
+
+
+def forward_fused(p, x, w_router, bias, w_gate, w_up, w_down, y, ws, logits=None, topk_ids=None,
+                  topk_weights=None, counts=None, offsets=None, stream=None):
+    _check("moe_forward_fused",
+           lib.moe_forward_fused(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
+                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(logits),
+                                 _ptr(topk_ids), _ptr(topk_weights), _ptr(counts), _ptr(offsets),
+                                 _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def fused_error_offset(p, whole_layer: bool) -> int:
+    n = ctypes.c_size_t()
+    _check("moe_fused_error_offset", lib.moe_fused_error_offset(ctypes.byref(p),
+                                                                1 if whole_layer else 0,
+                                                                ctypes.byref(n)))
+    return n.value

@@ -55,7 +55,7 @@ hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, 
 hipError_t launch_topk(const Dims& d, const float* logits, const float* bias, int32_t* ids,
                        float* weights, hipStream_t s);
 
-// permute.hip
+// permute.hip (x_perm NULL: the routing tables only, no row copy)
 size_t permute_ws_bytes(const Dims& d);
 hipError_t launch_permute(const Dims& d, const uint16_t* x, const int32_t* ids, int32_t* counts,
                           int32_t* offsets, int32_t* row_token, int32_t* slot_row,
@@ -102,6 +102,15 @@ hipError_t launch_grouped_ffn_gelu(const Dims& d, const uint16_t* x_perm, const 
 // C[N, Nout] = bf16(GELU(A W^T + bias)); offsets2: 2 int32 of device scratch.
 hipError_t launch_dense_gelu(int64_t N, int Kd, int Nout, const uint16_t* A, const uint16_t* W,
                              const float* bias, uint16_t* C, int32_t* offsets2, hipStream_t s);
+
+// The fused FFN: one persistent launch for gate/up, SwiGLU and down, A rows of
+// gate/up gathered from x by row_token (contiguous layout).  Workspace: h and
+// the launch's counters; *err receives the device address of its error word.
+size_t fused_ws_bytes(const Dims& d);
+size_t fused_err_offset(const Dims& d);
+hipError_t launch_fused_ffn(const Dims& d, const uint16_t* x, const int32_t* row_token,
+                            const int32_t* offsets, const uint16_t* wg, const uint16_t* wu,
+                            const uint16_t* wd, uint16_t* out_perm, void* ws, hipStream_t s);
 
 // quant.hip
 hipError_t launch_quantize_fp8(int64_t rows, int cols, const uint16_t* w, uint8_t* codes,

@@ -63,6 +63,7 @@ struct GemmArgs {
   const uint8_t* S0;        // FP8 only: scales of B0, [E, Nout/32, Kd/32, 32]
   const uint8_t* S1;        // FP8 only: scales of B1
   const float* bias;        // bias epilogues: [E, Nout] fp32
+  const int32_t* gather;    // ring kernels: A row r is A[gather[r]] (NULL: A[r])
 };
 
 // Epilogues: what a tile writes to C.
@@ -151,6 +152,7 @@ struct Tile {
   int e, nt;
   int64_t row0;
   int rows;
+  int mtg;      // row tile over all experts: mstart[e] + row tile within the expert
 };
 template <int BM>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* mstart, int l) {
@@ -175,6 +177,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* ms
   const int b0 = (int)((int64_t)mt * nbk / mt_e), b1 = (int)((int64_t)(mt + 1) * nbk / mt_e);
   t.row0 = (int64_t)seg0 + 32 * b0;
   t.rows = min(32 * (b1 - b0), m - 32 * b0);
+  t.mtg = __builtin_amdgcn_readfirstlane(mstart[t.e]) + mt;
   return t;
 }
 
@@ -321,7 +324,17 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // the pragma); nothing else in these kernels reads or writes it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// UNIFORM: the caller cannot show the compiler that base is wave-uniform
+// (it is); read it from the first lane so that it is a scalar operand.
+template <bool UNIFORM = false>
 __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* base, uint32_t voff) {
+  if constexpr (UNIFORM) {
+    // readfirstlane returns int: go through uint32_t, which zero-extends
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    base = reinterpret_cast<const void*>((uint64_t)lo | ((uint64_t)hi << 32));
+  }
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                ::"s"(lds_addr), "v"(voff), "s"(base)
                : "memory", "m0");
@@ -484,110 +497,211 @@ __device__ __forceinline__ void ring_kloop_n(int nmb, f32x16_t (&acc)[R::MB][R::
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8>
-__global__ void __launch_bounds__(64 * WM * WN)
-grouped_gemm_ring(GemmArgs p) {
+// One tile of the ring kernel: its operands through the LDS ring, the k loop
+// and the epilogue.  Every wave of the workgroup takes part; on return each
+// wave has issued its stores of the tile.
+template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8, bool UNIFORM = false>
+__device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
+                                          uint4 (*lds)[Ring<BM, BN, WM, WN, BK, S, FP8>::STAGE_U4],
+                                          uint32_t lds_addr, int wave, int lane) {
   constexpr bool GATEUP = EPI == kEpiSwiglu;
   using R = Ring<BM, BN, WM, WN, BK, S, FP8>;
-  constexpr int MB = R::MB, NB = R::NB, TN = R::TN;
+  constexpr int MB = R::MB, NB = R::NB;
   constexpr int PWA = R::PWA, PWB = R::PWB, PW = R::PW;
-  __shared__ uint4 lds[S][R::STAGE_U4];
-  __shared__ int32_t mstart[1025];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   // DMA lane roles: lane -> (row in its instruction's group, LDS chunk)
   const int lra = lane / R::CHA, lca = lane % R::CHA;
   const int lrb = lane / R::CHB, lcb = lane % R::CHB;
+  const int nk = p.Kd / BK;
+  const size_t wmat = (size_t)p.Nout * p.Kd;     // elements of one expert's matrix
+  // DMA sources: instruction j moves 1 KB into LDS at byte ldso[j] of the
+  // stage from base[j] + off[j] (+ the per-stage advance); the lane writing
+  // LDS chunk c of a row fetches global chunk c ^ swizzle(row), which
+  // realises the swizzle.  Instructions [0, PWA) carry A rows, [PWA,
+  // PWA + PWB) B rows and, for FP8, the last one (lanes < LS only) scales.
+  const void* base[PW];
+  uint32_t off[PW], ldso[PW];
+#pragma unroll
+  for (int j = 0; j < PWA; ++j) {
+    const int q = wave * PWA + j;
+    const int trow = q * R::RPIA + lra;
+    const int row = min(trow, t.rows - 1);
+    // gathered A: row r of the tile is row gather[row0 + r] of A
+    const uint32_t src = p.gather ? (uint32_t)p.gather[t.row0 + row] : (uint32_t)row;
+    base[j] = p.gather ? p.A : p.A + t.row0 * p.Kd;
+    off[j] = (src * p.Kd + (uint32_t)(lca ^ swz<BK>(trow)) * 8) * 2u;
+    ldso[j] = q * 1024;
+  }
+#pragma unroll
+  for (int jb = 0; jb < PWB; ++jb) {
+    const int q = wave * PWB + jb;
+    const int g0 = q * R::RPIB, trow = g0 + lrb;
+    bool up;
+    const int wrow = min(weight_row<BN, GATEUP>(t.nt, g0, up) + lrb, p.Nout - 1);
+    const char* b = static_cast<const char*>(up ? p.B1 : p.B0);
+    if (FP8) {
+      base[PWA + jb] = b + (size_t)t.e * wmat;
+      off[PWA + jb] = (uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz_rows<R::BRB>(trow)) * 16;
+    } else {
+      base[PWA + jb] = b + (size_t)t.e * wmat * 2;
+      off[PWA + jb] = ((uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz<BK>(trow)) * 8) * 2u;
+    }
+    ldso[PWA + jb] = R::A_U4 * 16 + q * 1024;
+  }
+  if constexpr (FP8) {
+    const int lam = min(lane, R::LS - 1);
+    const int half = lam & 1, kbl = (lam >> 1) % R::KB, i = (lam >> 1) / R::KB;
+    int m = 0, rg;
+    if (GATEUP) {
+      m = wave / (R::NW / 2);
+      rg = t.nt * (BN / 64) + (wave % (R::NW / 2)) * R::GPW + i;
+    } else {
+      rg = t.nt * (BN / 32) + wave * R::GPW + i;
+    }
+    rg = min(rg, p.Nout / 32 - 1);
+    base[PW - 1] = (m ? p.S1 : p.S0) + (size_t)t.e * (wmat / 32);
+    off[PW - 1] = ((uint32_t)rg * (uint32_t)(p.Kd / 32) + kbl) * 32 + half * 16;
+    ldso[PW - 1] = (R::A_U4 + R::B_U4) * 16 + wave * R::LS * 16;
+  }
+  // lds_addr: LDS byte address of lds[0][0] (taken where the array is
+  // declared, so no generic-pointer conversion is needed here)
+  auto dma = [&](int s, int kt) {
+    const uint32_t l0 = lds_addr + (uint32_t)s * (R::STAGE_U4 * 16);
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const uint32_t adv = j < PWA ? BK * 2 : j < PWA + PWB ? R::BRB : R::KB * 32;
+      const uint32_t la = __builtin_amdgcn_readfirstlane(l0 + ldso[j]);
+      if (FP8 && j == PW - 1) {
+        if (lane < R::LS) lds_dma16<UNIFORM>(la, base[j], off[j] + (uint32_t)kt * adv);
+      } else {
+        lds_dma16<UNIFORM>(la, base[j], off[j] + (uint32_t)kt * adv);
+      }
+    }
+  };
 
+  f32x16_t acc[MB][NB];
+  zero(acc);
+  // every wave is past its last LDS read of the previous tile
+  wait_lgkmcnt0();
+  barrier();
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (s < nk) dma(s, s);
+  wait_stages<PW, S>(min(S - 1, nk - 1));
+  barrier();
+  // 32-row blocks of this wave that hold at least one row of the tile
+  const int nmb = min(MB, max(0, (t.rows - wm * R::TM + 31) / 32));
+  ring_kloop_n<R, MB, FP8, GATEUP>(nmb, acc, lds, nk, wm, wn, lane, dma);
+  store_tile<MB, NB, R::TM, R::TN, BN, EPI>(p, t, acc, wm, wn, lane);
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8>
+__global__ void __launch_bounds__(64 * WM * WN)
+grouped_gemm_ring(GemmArgs p) {
+  using R = Ring<BM, BN, WM, WN, BK, S, FP8>;
+  __shared__ uint4 lds[S][R::STAGE_U4];
+  __shared__ int32_t mstart[1025];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0];
   if (wave == 0) build_work_list<BM>(p, mstart, lane);
   __syncthreads();
   const int total = p.n_tiles * mstart[p.E];
   const int xcd = blockIdx.x & 7, P8 = gridDim.x >> 3, j0 = blockIdx.x >> 3;
   const int begin = (int)((int64_t)total * xcd / 8);
   const int end = (int)((int64_t)total * (xcd + 1) / 8);
-  const int nk = p.Kd / BK;
-  const size_t wmat = (size_t)p.Nout * p.Kd;     // elements of one expert's matrix
-  (void)TN;
+  for (int l = begin + j0; l < end; l += P8)
+    ring_tile<BM, BN, WM, WN, BK, S, EPI, FP8>(p, decode_tile<BM>(p, mstart, l), lds, lds_addr,
+                                               wave, lane);
+}
 
-  for (int l = begin + j0; l < end; l += P8) {
-    const Tile t = decode_tile<BM>(p, mstart, l);
-    // DMA sources: instruction j moves 1 KB into LDS at byte ldso[j] of the
-    // stage from base[j] + off[j] (+ the per-stage advance); the lane writing
-    // LDS chunk c of a row fetches global chunk c ^ swizzle(row), which
-    // realises the swizzle.  Instructions [0, PWA) carry A rows, [PWA,
-    // PWA + PWB) B rows and, for FP8, the last one (lanes < LS only) scales.
-    const void* base[PW];
-    uint32_t off[PW], ldso[PW];
-#pragma unroll
-    for (int j = 0; j < PWA; ++j) {
-      const int q = wave * PWA + j;
-      const int trow = q * R::RPIA + lra;
-      base[j] = p.A + t.row0 * p.Kd;
-      off[j] = ((uint32_t)min(trow, t.rows - 1) * p.Kd + (uint32_t)(lca ^ swz<BK>(trow)) * 8) * 2u;
-      ldso[j] = q * 1024;
-    }
-#pragma unroll
-    for (int jb = 0; jb < PWB; ++jb) {
-      const int q = wave * PWB + jb;
-      const int g0 = q * R::RPIB, trow = g0 + lrb;
-      bool up;
-      const int wrow = min(weight_row<BN, GATEUP>(t.nt, g0, up) + lrb, p.Nout - 1);
-      const char* b = static_cast<const char*>(up ? p.B1 : p.B0);
-      if (FP8) {
-        base[PWA + jb] = b + (size_t)t.e * wmat;
-        off[PWA + jb] = (uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz_rows<R::BRB>(trow)) * 16;
-      } else {
-        base[PWA + jb] = b + (size_t)t.e * wmat * 2;
-        off[PWA + jb] = ((uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz<BK>(trow)) * 8) * 2u;
-      }
-      ldso[PWA + jb] = R::A_U4 * 16 + q * 1024;
-    }
-    if constexpr (FP8) {
-      const int lam = min(lane, R::LS - 1);
-      const int half = lam & 1, kbl = (lam >> 1) % R::KB, i = (lam >> 1) / R::KB;
-      int m = 0, rg;
-      if (GATEUP) {
-        m = wave / (R::NW / 2);
-        rg = t.nt * (BN / 64) + (wave % (R::NW / 2)) * R::GPW + i;
-      } else {
-        rg = t.nt * (BN / 32) + wave * R::GPW + i;
-      }
-      rg = min(rg, p.Nout / 32 - 1);
-      base[PW - 1] = (m ? p.S1 : p.S0) + (size_t)t.e * (wmat / 32);
-      off[PW - 1] = ((uint32_t)rg * (uint32_t)(p.Kd / 32) + kbl) * 32 + half * 16;
-      ldso[PW - 1] = (R::A_U4 + R::B_U4) * 16 + wave * R::LS * 16;
-    }
-    auto dma = [&](int s, int kt) {
-      const uint32_t l0 = (uint32_t)(uintptr_t)(lds_void_t*)&lds[s][0];
-#pragma unroll
-      for (int j = 0; j < PW; ++j) {
-        const uint32_t adv = j < PWA ? BK * 2 : j < PWA + PWB ? R::BRB : R::KB * 32;
-        const uint32_t la = __builtin_amdgcn_readfirstlane(l0 + ldso[j]);
-        if (FP8 && j == PW - 1) {
-          if (lane < R::LS) lds_dma16(la, base[j], off[j] + (uint32_t)kt * adv);
-        } else {
-          lds_dma16(la, base[j], off[j] + (uint32_t)kt * adv);
+// ------------------------------------------------------------ fused FFN
+//
+// The whole expert FFN in one persistent launch ("MoE 推理完整机制" (zoe.im),
+// 第四层: one kernel, compute units handed to experts dynamically, any number
+// of rows per expert).  The work list is every gate/up tile, then every down
+// tile; workgroups take tiles in list order from one ticket counter.  A
+// gate/up tile gathers its A rows straight from x through row_token (no
+// permuted copy of x), writes its h columns and counts itself finished for
+// its row tile; a down tile waits until every gate/up tile of its row tile
+// has been counted.  Every tile a down tile waits for has a smaller ticket,
+// so it was claimed by a running workgroup that waits for nothing: the launch
+// always drains.  A wait is still bounded: after kWaitTicks of the 100 MHz
+// real-time counter it sets the error word and goes on (the results are then
+// wrong, and the caller can read the word).
+//
+// Ordering: a gate/up tile's waves wait for their h stores, then one lane
+// makes them visible device-wide (agent-scope release) before counting the
+// tile.  A waiting lane polls the counter with plain device-coherent loads
+// (an acquire per poll would invalidate this XCD's caches over and over,
+// starving the tiles being waited for) and acquires once when it is done.
+
+struct FusedArgs {
+  GemmArgs gu;       // gate/up: A = x gathered by row_token, C = h
+  GemmArgs dn;       // down: A = h, C = out_perm
+  int32_t* ticket;   // [1], zero at launch
+  int32_t* done;     // [row tiles], zero at launch: finished gate/up tiles per row tile
+  int32_t* err;      // [1], zero at launch; nonzero after a wait ran past its bound
+};
+
+constexpr uint64_t kWaitTicks = 5000000;   // 50 ms of the 100 MHz real-time counter
+
+template <int BM, int BN, int WM, int WN, int BK, int S, bool FP8>
+__global__ void __launch_bounds__(64 * WM * WN)
+grouped_ffn_fused(FusedArgs f) {
+  using R = Ring<BM, BN, WM, WN, BK, S, FP8>;
+  __shared__ uint4 lds[S][R::STAGE_U4];
+  __shared__ int32_t mstart[1025];
+  __shared__ int32_t ticket;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0];
+  if (wave == 0) build_work_list<BM>(f.gu, mstart, lane);
+  __syncthreads();
+  const int M = mstart[f.gu.E];
+  const int T1 = f.gu.n_tiles * M, T = T1 + f.dn.n_tiles * M;
+  for (;;) {
+    if (tid == 0) ticket = __hip_atomic_fetch_add(f.ticket, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int l = __builtin_amdgcn_readfirstlane(ticket);
+    __syncthreads();
+    if (l >= T) break;
+    if (l < T1) {
+      const Tile t = decode_tile<BM>(f.gu, mstart, l);
+      ring_tile<BM, BN, WM, WN, BK, S, kEpiSwiglu, FP8, true>(f.gu, t, lds, lds_addr, wave,
+                                                              lane);
+      // every wave's h stores have completed, then they are made visible
+      // device-wide and the tile is counted
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(f.done + t.mtg, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const Tile t = decode_tile<BM>(f.dn, mstart, l - T1);
+      if (tid == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(f.done + t.mtg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               f.gu.n_tiles) {
+          __builtin_amdgcn_s_sleep(4);
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            __hip_atomic_fetch_or(f.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
-    };
-
-    f32x16_t acc[MB][NB];
-    zero(acc);
-    // every wave is past its last LDS read of the previous tile
-    wait_lgkmcnt0();
-    barrier();
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-      if (s < nk) dma(s, s);
-    wait_stages<PW, S>(min(S - 1, nk - 1));
-    barrier();
-    // 32-row blocks of this wave that hold at least one row of the tile
-    const int nmb = min(MB, max(0, (t.rows - wm * R::TM + 31) / 32));
-    ring_kloop_n<R, MB, FP8, GATEUP>(nmb, acc, lds, nk, wm, wn, lane, dma);
-    store_tile<MB, NB, R::TM, R::TN, BN, EPI>(p, t, acc, wm, wn, lane);
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      ring_tile<BM, BN, WM, WN, BK, S, kEpiStore, FP8, true>(f.dn, t, lds, lds_addr, wave, lane);
+    }
   }
+}
+
+// Zeroes the fused launch's ticket, error word and row-tile counters.
+__global__ void fused_reset_kernel(int32_t* words, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    words[i] = 0;
 }
 
 // ------------------------------------------------------------ register-staged
@@ -918,6 +1032,56 @@ hipError_t launch_dense_gelu(int64_t N, int Kd, int Nout, const uint16_t* A, con
                                                            : Shape::Small;
   return launch_gemm<kEpiBiasGelu, false>(
       d, GemmArgs{A, W, nullptr, C, offsets2, 1, Kd, Nout, 0, nullptr, nullptr, bias}, s, shape);
+}
+
+namespace {
+
+template <int BM, int BN, int WM, int WN, int BK, int S>
+hipError_t launch_fused(const Dims& d, const FusedArgs& f0, hipStream_t s) {
+  FusedArgs f = f0;
+  f.gu = with_tiles<BN, true>(f.gu);
+  f.dn = with_tiles<BN, false>(f.dn);
+  const int64_t mt_max = (d.R + BM - 1) / BM + d.E;    // row tiles, upper bound
+  const int words = (int)(2 + mt_max);
+  hipLaunchKernelGGL(fused_reset_kernel, dim3((unsigned)((words + 255) / 256 < 64 ? (words + 255) / 256 : 64)),
+                     dim3(256), 0, s, f.ticket, words);
+  int64_t g = device_cu_count();
+  const int64_t work = mt_max * (f.gu.n_tiles + f.dn.n_tiles);
+  if (g > work) g = work;
+  hipLaunchKernelGGL((grouped_ffn_fused<BM, BN, WM, WN, BK, S, false>), dim3((unsigned)g),
+                     dim3(64 * WM * WN), 0, s, f);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Workspace of the fused FFN: h [R, F] bf16, then the ticket, the error word
+// and one counter per row tile (row tiles of 32 rows bound those of every tile
+// shape).
+size_t fused_ws_bytes(const Dims& d) {
+  return align_up((size_t)d.R * d.F * 2) + align_up((size_t)(2 + d.R / 32 + 1 + d.E) * 4);
+}
+
+size_t fused_err_offset(const Dims& d) { return align_up((size_t)d.R * d.F * 2) + 4; }
+
+hipError_t launch_fused_ffn(const Dims& d, const uint16_t* x, const int32_t* row_token,
+                            const int32_t* offsets, const uint16_t* wg, const uint16_t* wu,
+                            const uint16_t* wd, uint16_t* out_perm, void* ws, hipStream_t s) {
+  uint16_t* h = static_cast<uint16_t*>(ws);
+  int32_t* words = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                              align_up((size_t)d.R * d.F * 2));
+  FusedArgs f;
+  f.gu = GemmArgs{x, wg, wu, h, offsets, d.E, d.D, d.F, 0, nullptr, nullptr, nullptr, row_token};
+  f.dn = GemmArgs{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D, 0, nullptr, nullptr, nullptr,
+                  nullptr};
+  f.ticket = words;
+  f.err = words + 1;
+  f.done = words + 2;
+  switch (pick(d)) {
+    case Shape::Small: return launch_fused<32, 256, 1, 4, 64, 4>(d, f, s);
+    case Shape::Mid: return launch_fused<128, 256, 2, 4, 64, 3>(d, f, s);
+    default: return launch_fused<256, 256, 2, 4, 32, 4>(d, f, s);
+  }
 }
 
 }  // namespace moe

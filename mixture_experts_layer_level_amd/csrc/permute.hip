@@ -249,6 +249,7 @@ hipError_t launch_permute(const Dims& d, const uint16_t* x, const int32_t* ids, 
                        d.E, d.K, nbits, d.cap, (int)d.padded, ids, table, offsets, slot_row,
                        row_token);
   }
+  if (!x_perm) return hipGetLastError();      // routing tables only
   const int64_t items = d.N * (d.D / 8);
   const int64_t blocks = std::min<int64_t>((items + 255) / 256, 1 << 20);
   hipLaunchKernelGGL(perm_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, d.N, d.D, d.K, x,

@@ -109,6 +109,8 @@ def test_staged_argument_errors():
     # permute: workspace checked
     assert L.moe_permute(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0) == WORKSPACE
     assert L.moe_permute(bp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 0) == INVALID
+    assert L.moe_permute(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, 1 << 20, 0) \
+        == UNSUPPORTED                                                # misaligned x_perm
     # grouped FFN: workspace needed only without h
     assert L.moe_grouped_ffn(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, 0) == WORKSPACE
     assert L.moe_grouped_ffn(bp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 0, 0) == INVALID
@@ -220,3 +222,42 @@ def test_gelu_layer_argument_checks():
     args192 = [ctypes.byref(P(D=192))] + args[1:]
     assert fw(*args192, FAKE, 1 << 30, None) == UNSUPPORTED             # D % 256 != 0
     assert fw(ctypes.byref(P(N=0, D=256)), *args[1:], None, 0, None) == OK
+
+
+def test_fused_argument_checks():
+    L = moe.lib
+    p = P()
+    bp = ctypes.byref(p)
+    need = moe.workspace_size(p)
+    f = L.moe_fused_ffn
+    assert f(bp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == INVALID
+    assert f(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == WORKSPACE
+    assert f(ctypes.byref(P(cn=5, cd=4)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
+             None) == UNSUPPORTED                                     # padded layout
+    assert f(bp, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == UNSUPPORTED
+    assert f(ctypes.byref(P(N=0)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == OK
+    fw = L.moe_forward_fused
+    args = [bp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE] + [None] * 5
+    assert fw(*args, FAKE, need - 1, None) == WORKSPACE
+    assert fw(*([bp, FAKE, None] + args[3:]), FAKE, need, None) == INVALID   # no router weights
+    assert fw(*([ctypes.byref(P(cn=5, cd=4))] + args[1:]), FAKE, 1 << 30, None) == UNSUPPORTED
+    assert fw(*([ctypes.byref(P(N=1 << 20, D=4096))] + args[1:]), FAKE, 1 << 62, None) \
+        == UNSUPPORTED                                                # x of 8 GiB
+    assert fw(*([ctypes.byref(P(N=0))] + args[1:]), None, 0, None) == OK
+    n = ctypes.c_size_t()
+    assert L.moe_fused_error_offset(bp, 0, ctypes.byref(n)) == OK
+    n1 = ctypes.c_size_t()
+    assert L.moe_fused_error_offset(bp, 1, ctypes.byref(n1)) == OK
+    assert n.value % 4 == 0 and n1.value > n.value and n1.value + 4 <= need
+    assert L.moe_fused_error_offset(bp, 0, None) == INVALID
+
+
+def test_fused_entry_points_are_switched_off():
+    """The fused FFN is switched off: valid arguments give UNSUPPORTED (the
+    argument checks still run first, see test_fused_argument_checks)."""
+    p = P()
+    need = moe.workspace_size(p)
+    assert moe.lib.moe_fused_ffn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 need, None) == UNSUPPORTED
+    assert moe.lib.moe_forward_fused(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                     None, None, None, None, None, FAKE, need, None) == UNSUPPORTED

@@ -92,9 +92,6 @@ def main():
     if args.padded and cap is None:
         raise SystemExit(f"{cfg.name} has no capacity factor")
     gelu = cfg.expert == "gelu"
-    if args.fused:
-        raise SystemExit("--fused: the fused FFN launch is switched off in the library "
-                         "(moe_fused_ffn returns MOE_ERR_UNSUPPORTED)")
     if args.fused and (gelu or args.weights != "bf16" or args.padded):
         raise SystemExit("--fused runs the SwiGLU layer, bf16 weights, contiguous layout")
     if gelu and args.weights != "bf16":

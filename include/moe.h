@@ -191,10 +191,6 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                        void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------ fused FFN */
-/* NOT AVAILABLE IN THIS BUILD: after their argument checks, moe_fused_ffn and
- * moe_forward_fused return MOE_ERR_UNSUPPORTED (their persistent launch did
- * not complete on MI355X and is switched off until the cause is found).  The
- * contract below is the one they are built to. */
 /* The whole expert FFN as one persistent launch (the single-kernel MoE of
  * "MoE 推理完整机制" (zoe.im) 第四层, DeepGEMM & MegaMoE Kernel: workgroups
  * take gate/up and down tiles of every expert from one work list).  Same

@@ -606,7 +606,7 @@ grouped_gemm_ring(GemmArgs p) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0];
   if (wave == 0) build_work_list<BM>(p, mstart, lane);
   __syncthreads();
-  const int total = p.n_tiles * mstart[p.E];
+  const int total = p.n_tiles * __builtin_amdgcn_readfirstlane(mstart[p.E]);
   const int xcd = blockIdx.x & 7, P8 = gridDim.x >> 3, j0 = blockIdx.x >> 3;
   const int begin = (int)((int64_t)total * xcd / 8);
   const int end = (int)((int64_t)total * (xcd + 1) / 8);
@@ -630,17 +630,18 @@ grouped_gemm_ring(GemmArgs p) {
 // real-time counter it sets the error word and goes on (the results are then
 // wrong, and the caller can read the word).
 //
-// Ordering: a gate/up tile's waves wait for their h stores, then one lane
-// makes them visible device-wide (agent-scope release) before counting the
-// tile.  A waiting lane polls the counter with plain device-coherent loads
-// (an acquire per poll would invalidate this XCD's caches over and over,
-// starving the tiles being waited for) and acquires once when it is done.
+// Ordering: each wave of a gate/up tile makes its h stores visible
+// device-wide (agent-scope release fence: its stores complete and this XCD's
+// L2 is written back) and then adds its count to the row tile; each wave of a
+// down tile polls that count with plain device-coherent loads (an acquire per
+// poll would invalidate this XCD's caches over and over, starving the tiles
+// being waited for) and acquires once when it is complete.
 
 struct FusedArgs {
   GemmArgs gu;       // gate/up: A = x gathered by row_token, C = h
   GemmArgs dn;       // down: A = h, C = out_perm
   int32_t* ticket;   // [1], zero at launch
-  int32_t* done;     // [row tiles], zero at launch: finished gate/up tiles per row tile
+  int32_t* done;     // [row tiles], zero at launch: finished gate/up waves per row tile
   int32_t* err;      // [1], zero at launch; nonzero after a wait ran past its bound
 };
 
@@ -658,11 +659,21 @@ grouped_ffn_fused(FusedArgs f) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0];
   if (wave == 0) build_work_list<BM>(f.gu, mstart, lane);
   __syncthreads();
-  const int M = mstart[f.gu.E];
+  // No branch on the loop's path may depend on the lane (or look as if it
+  // did): with an "if (tid == 0)" at the loop head and another after the
+  // tile, the compiler merges the two across the back edge, and the lanes
+  // other than thread 0 then go round an inner loop that skips the ticket
+  // fetch while thread 0 waits for them to leave it, so the workgroup repeats
+  // one tile for ever.  Hence scalar loop bounds, and atomics that a whole
+  // wave executes (lane 0 adds 1, the others 0).
+  const int M = __builtin_amdgcn_readfirstlane(mstart[f.gu.E]);
   const int T1 = f.gu.n_tiles * M, T = T1 + f.dn.n_tiles * M;
+  const int need = f.gu.n_tiles * WM * WN;     // every wave of a gate/up tile counts once
+  const int one = lane == 0 ? 1 : 0;
   for (;;) {
-    if (tid == 0) ticket = __hip_atomic_fetch_add(f.ticket, 1, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
+    if (wave == 0)
+      ticket = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_fetch_add(f.ticket, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     __syncthreads();
     const int l = __builtin_amdgcn_readfirstlane(ticket);
     __syncthreads();
@@ -671,28 +682,25 @@ grouped_ffn_fused(FusedArgs f) {
       const Tile t = decode_tile<BM>(f.gu, mstart, l);
       ring_tile<BM, BN, WM, WN, BK, S, kEpiSwiglu, FP8, true>(f.gu, t, lds, lds_addr, wave,
                                                               lane);
-      // every wave's h stores have completed, then they are made visible
-      // device-wide and the tile is counted
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __syncthreads();
-      if (tid == 0)
-        __hip_atomic_fetch_add(f.done + t.mtg, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      // each wave publishes its own h stores (agent-scope release fence,
+      // then its count on the row tile)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(f.done + t.mtg, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       const Tile t = decode_tile<BM>(f.dn, mstart, l - T1);
-      if (tid == 0) {
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (__hip_atomic_load(f.done + t.mtg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               f.gu.n_tiles) {
-          __builtin_amdgcn_s_sleep(4);
-          if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-            __hip_atomic_fetch_or(f.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
+      // each wave waits for the row tile's counts itself, then acquires
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      for (;;) {
+        const int c = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(f.done + t.mtg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (c >= need) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+          __hip_atomic_fetch_or(f.err, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __builtin_amdgcn_s_sleep(4);
       }
-      __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       ring_tile<BM, BN, WM, WN, BK, S, kEpiStore, FP8, true>(f.dn, t, lds, lds_addr, wave, lane);
     }
   }
@@ -786,7 +794,7 @@ grouped_gemm_regs(GemmArgs p) {
 
   if (wave == 0) build_work_list<BM>(p, mstart, lane);
   __syncthreads();
-  const int total = p.n_tiles * mstart[p.E];
+  const int total = p.n_tiles * __builtin_amdgcn_readfirstlane(mstart[p.E]);
   const int xcd = blockIdx.x & 7, P8 = gridDim.x >> 3, j0 = blockIdx.x >> 3;
   const int begin = (int)((int64_t)total * xcd / 8);
   const int end = (int)((int64_t)total * (xcd + 1) / 8);

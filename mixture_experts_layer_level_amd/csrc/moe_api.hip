@@ -14,10 +14,6 @@ std::atomic<int> g_cu_count[kMaxDevices];
 
 inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// The fused FFN launch is switched off: on MI355X its launch did not complete
-// (it ran past every test's time limit) for a cause not yet found; both fused
-// entry points check their arguments and then return MOE_ERR_UNSUPPORTED.
-constexpr bool kFusedEnabled = false;
 
 moe_status check_problem(const moe_problem* p, Dims* d) {
   if (!p) return MOE_ERR_INVALID_ARG;
@@ -582,7 +578,6 @@ moe_status moe_fused_ffn(const moe_problem* p, const uint16_t* x, const int32_t*
   if (d.N > 0 && (!ws || ws_bytes < fused_ws_bytes(d))) return MOE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
   if (d.N == 0) return MOE_OK;
-  if (!kFusedEnabled) return MOE_ERR_UNSUPPORTED;
   (void)hipGetLastError();  // report only this call's launch errors
   return hip_status(launch_fused_ffn(d, x, row_token, expert_offsets, w_gate, w_up, w_down,
                                      out_perm, ws, static_cast<hipStream_t>(stream)));
@@ -606,7 +601,6 @@ moe_status moe_forward_fused(const moe_problem* p, const uint16_t* x, const floa
   if (d.N > 0 && (!ws || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MOE_ERR_UNSUPPORTED;
   if (d.N == 0) return MOE_OK;
-  if (!kFusedEnabled) return MOE_ERR_UNSUPPORTED;
   (void)hipGetLastError();  // report only this call's launch errors
   char* base = static_cast<char*>(ws);
   if (!logits) logits = reinterpret_cast<float*>(base + L.logits);

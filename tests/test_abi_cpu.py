@@ -251,13 +251,3 @@ def test_fused_argument_checks():
     assert n.value % 4 == 0 and n1.value > n.value and n1.value + 4 <= need
     assert L.moe_fused_error_offset(bp, 0, None) == INVALID
 
-
-def test_fused_entry_points_are_switched_off():
-    """The fused FFN is switched off: valid arguments give UNSUPPORTED (the
-    argument checks still run first, see test_fused_argument_checks)."""
-    p = P()
-    need = moe.workspace_size(p)
-    assert moe.lib.moe_fused_ffn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                 need, None) == UNSUPPORTED
-    assert moe.lib.moe_forward_fused(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
-                                     None, None, None, None, None, FAKE, need, None) == UNSUPPORTED

@@ -9,10 +9,7 @@ import torch
 import moe_synth as ms
 from oracle import moe_oracle as O
 
-pytestmark = [pytest.mark.gpu,
-              pytest.mark.skip(reason="the fused FFN launch is switched off: on MI355X it did "
-                                      "not complete within the test time limit (cause not found "
-                                      "yet); the entry points return MOE_ERR_UNSUPPORTED")]
+pytestmark = pytest.mark.gpu
 
 from gpu_layer import (DEV, SMALL, Layer, assert_fp_close, bits, check_permutation,  # noqa: E402
                        np_, sample_tokens, check_sampled_outputs)

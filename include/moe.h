@@ -193,7 +193,7 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
 /* ------------------------------------------------------------ fused FFN */
 /* The whole expert FFN as one persistent launch (the single-kernel MoE of
  * "MoE 推理完整机制" (zoe.im) 第四层, DeepGEMM & MegaMoE Kernel: workgroups
- * take gate/up and down tiles of every expert from one work list).  Same
+ * claim the gate/up tiles, then the down tiles, of every expert at run time).  Same
  * results as moe_grouped_ffn on x_perm = x[row_token] (bit for bit), but the
  * gate/up tiles gather their rows from x through row_token, so no permuted
  * copy of x exists, and down tiles of an expert's rows start as soon as that

@@ -619,32 +619,42 @@ grouped_gemm_ring(GemmArgs p) {
 //
 // The whole expert FFN in one persistent launch ("MoE 推理完整机制" (zoe.im),
 // 第四层: one kernel, compute units handed to experts dynamically, any number
-// of rows per expert).  The work list is every gate/up tile, then every down
-// tile; workgroups take tiles in list order from one ticket counter.  A
+// of rows per expert).  There are two work lists in the grouped GEMM's tile
+// order: every gate/up tile, then every down tile.  Each list is cut into
+// eight contiguous parts, one per XCD, each with its own claim counter, so
+// that the row tiles sharing a weight panel run on one XCD and meet in its L2
+// (as in the grouped GEMM).  A workgroup claims tiles from its XCD's part of
+// the gate/up list, then from the other XCDs' parts, and only when every
+// gate/up tile is claimed does it turn to the down list (own part first).  A
 // gate/up tile gathers its A rows straight from x through row_token (no
 // permuted copy of x), writes its h columns and counts itself finished for
 // its row tile; a down tile waits until every gate/up tile of its row tile
-// has been counted.  Every tile a down tile waits for has a smaller ticket,
-// so it was claimed by a running workgroup that waits for nothing: the launch
-// always drains.  A wait is still bounded: after kWaitTicks of the 100 MHz
-// real-time counter it sets the error word and goes on (the results are then
-// wrong, and the caller can read the word).
+// has been counted.  Every tile a down tile waits for was claimed before by
+// a running workgroup that waits for nothing, so the launch always drains.
+// A wait is still bounded: after kWaitTicks of the 100 MHz real-time counter
+// it sets the error word and goes on (the results are then wrong, and the
+// caller can read the word).
 //
-// Ordering: each wave of a gate/up tile makes its h stores visible
-// device-wide (agent-scope release fence: its stores complete and this XCD's
-// L2 is written back) and then adds its count to the row tile; each wave of a
-// down tile polls that count with plain device-coherent loads (an acquire per
-// poll would invalidate this XCD's caches over and over, starving the tiles
-// being waited for) and acquires once when it is complete.
+// Ordering: every wave of a gate/up tile waits until its h stores have
+// completed (they are then in this XCD's L2); after a barrier, wave 0 writes
+// the L2 back (agent-scope release fence) and adds 1 to the row tile's count.
+// In a down tile, wave 0 polls that count with plain device-coherent loads (an
+// acquire per poll would invalidate this XCD's caches over and over, starving
+// the tiles being waited for), then acquires once (invalidating this CU's L1
+// and this XCD's L2) and waits for that to finish before a barrier releases
+// the other waves' loads.  One write-back and one invalidation per tile: done
+// by every wave, they took a third of the launch's time.
 
 struct FusedArgs {
   GemmArgs gu;       // gate/up: A = x gathered by row_token, C = h
   GemmArgs dn;       // down: A = h, C = out_perm
-  int32_t* ticket;   // [1], zero at launch
-  int32_t* done;     // [row tiles], zero at launch: finished gate/up waves per row tile
+  int32_t* claim;    // [16], zero at launch: tiles claimed from each XCD's part of the
+                     // gate/up list [0, 8), then of the down list [8, 16)
   int32_t* err;      // [1], zero at launch; nonzero after a wait ran past its bound
+  int32_t* done;     // [row tiles], zero at launch: finished gate/up tiles per row tile
 };
 
+constexpr int kFusedWords = 17;            // claim counters and the error word
 constexpr uint64_t kWaitTicks = 5000000;   // 50 ms of the 100 MHz real-time counter
 
 template <int BM, int BN, int WM, int WN, int BK, int S, bool FP8>
@@ -662,18 +672,35 @@ grouped_ffn_fused(FusedArgs f) {
   // No branch on the loop's path may depend on the lane (or look as if it
   // did): with an "if (tid == 0)" at the loop head and another after the
   // tile, the compiler merges the two across the back edge, and the lanes
-  // other than thread 0 then go round an inner loop that skips the ticket
-  // fetch while thread 0 waits for them to leave it, so the workgroup repeats
-  // one tile for ever.  Hence scalar loop bounds, and atomics that a whole
-  // wave executes (lane 0 adds 1, the others 0).
+  // other than thread 0 then go round an inner loop that skips the claim
+  // while thread 0 waits for them to leave it, so the workgroup repeats one
+  // tile for ever.  Hence scalar loop bounds, and atomics that a whole wave
+  // executes (lane 0 adds 1, the others 0).
   const int M = __builtin_amdgcn_readfirstlane(mstart[f.gu.E]);
   const int T1 = f.gu.n_tiles * M, T = T1 + f.dn.n_tiles * M;
-  const int need = f.gu.n_tiles * WM * WN;     // every wave of a gate/up tile counts once
+  const int need = f.gu.n_tiles;               // gate/up tiles per row tile
   const int one = lane == 0 ? 1 : 0;
+  const int xcd = blockIdx.x & 7;
+  int list = 0, step = 0;                      // wave 0: list and XCD part being claimed from
   for (;;) {
-    if (wave == 0)
-      ticket = __builtin_amdgcn_readfirstlane(
-          __hip_atomic_fetch_add(f.ticket, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (wave == 0) {
+      int got = T;
+      while (list < 2) {
+        const int n = list ? T - T1 : T1, x = (xcd + step) & 7;
+        const int b = (int)((int64_t)n * x / 8), e = (int)((int64_t)n * (x + 1) / 8);
+        const int c = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
+            f.claim + 8 * list + x, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (b + c < e) {
+          got = (list ? T1 : 0) + b + c;
+          break;
+        }
+        if (++step == 8) {
+          step = 0;
+          ++list;
+        }
+      }
+      ticket = got;
+    }
     __syncthreads();
     const int l = __builtin_amdgcn_readfirstlane(ticket);
     __syncthreads();
@@ -682,31 +709,40 @@ grouped_ffn_fused(FusedArgs f) {
       const Tile t = decode_tile<BM>(f.gu, mstart, l);
       ring_tile<BM, BN, WM, WN, BK, S, kEpiSwiglu, FP8, true>(f.gu, t, lds, lds_addr, wave,
                                                               lane);
-      // each wave publishes its own h stores (agent-scope release fence,
-      // then its count on the row tile)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_fetch_add(f.done + t.mtg, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // every wave's h stores have reached this XCD's L2; wave 0 writes the
+      // L2 back (agent-scope release) and counts the tile
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (wave == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(f.done + t.mtg, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     } else {
       const Tile t = decode_tile<BM>(f.dn, mstart, l - T1);
-      // each wave waits for the row tile's counts itself, then acquires
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      for (;;) {
-        const int c = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(f.done + t.mtg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (c >= need) break;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-          __hip_atomic_fetch_or(f.err, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
+      // wave 0 waits for the row tile's count, then invalidates this CU's L1
+      // and this XCD's L2 (agent-scope acquire) before the other waves load
+      if (wave == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+          const int c = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(f.done + t.mtg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          if (c >= need) break;
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            __hip_atomic_fetch_or(f.err, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
         }
-        __builtin_amdgcn_s_sleep(4);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        wait_vmcnt<0>();
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
       ring_tile<BM, BN, WM, WN, BK, S, kEpiStore, FP8, true>(f.dn, t, lds, lds_addr, wave, lane);
     }
   }
 }
 
-// Zeroes the fused launch's ticket, error word and row-tile counters.
+// Zeroes the fused launch's claim counters, error word and row-tile counters.
 __global__ void fused_reset_kernel(int32_t* words, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
     words[i] = 0;
@@ -1050,9 +1086,10 @@ hipError_t launch_fused(const Dims& d, const FusedArgs& f0, hipStream_t s) {
   f.gu = with_tiles<BN, true>(f.gu);
   f.dn = with_tiles<BN, false>(f.dn);
   const int64_t mt_max = (d.R + BM - 1) / BM + d.E;    // row tiles, upper bound
-  const int words = (int)(2 + mt_max);
-  hipLaunchKernelGGL(fused_reset_kernel, dim3((unsigned)((words + 255) / 256 < 64 ? (words + 255) / 256 : 64)),
-                     dim3(256), 0, s, f.ticket, words);
+  const int words = (int)(kFusedWords + mt_max);
+  hipLaunchKernelGGL(fused_reset_kernel,
+                     dim3((unsigned)((words + 255) / 256 < 64 ? (words + 255) / 256 : 64)),
+                     dim3(256), 0, s, f.claim, words);
   int64_t g = device_cu_count();
   const int64_t work = mt_max * (f.gu.n_tiles + f.dn.n_tiles);
   if (g > work) g = work;
@@ -1063,14 +1100,15 @@ hipError_t launch_fused(const Dims& d, const FusedArgs& f0, hipStream_t s) {
 
 }  // namespace
 
-// Workspace of the fused FFN: h [R, F] bf16, then the ticket, the error word
-// and one counter per row tile (row tiles of 32 rows bound those of every tile
-// shape).
+// Workspace of the fused FFN: h [R, F] bf16, then the 16 claim counters, the
+// error word and one counter per row tile (row tiles of 32 rows bound those
+// of every tile shape).
 size_t fused_ws_bytes(const Dims& d) {
-  return align_up((size_t)d.R * d.F * 2) + align_up((size_t)(2 + d.R / 32 + 1 + d.E) * 4);
+  return align_up((size_t)d.R * d.F * 2) +
+         align_up((size_t)(kFusedWords + d.R / 32 + 1 + d.E) * 4);
 }
 
-size_t fused_err_offset(const Dims& d) { return align_up((size_t)d.R * d.F * 2) + 4; }
+size_t fused_err_offset(const Dims& d) { return align_up((size_t)d.R * d.F * 2) + 16 * 4; }
 
 hipError_t launch_fused_ffn(const Dims& d, const uint16_t* x, const int32_t* row_token,
                             const int32_t* offsets, const uint16_t* wg, const uint16_t* wu,
@@ -1082,9 +1120,9 @@ hipError_t launch_fused_ffn(const Dims& d, const uint16_t* x, const int32_t* row
   f.gu = GemmArgs{x, wg, wu, h, offsets, d.E, d.D, d.F, 0, nullptr, nullptr, nullptr, row_token};
   f.dn = GemmArgs{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D, 0, nullptr, nullptr, nullptr,
                   nullptr};
-  f.ticket = words;
-  f.err = words + 1;
-  f.done = words + 2;
+  f.claim = words;
+  f.err = words + 16;
+  f.done = words + kFusedWords;
   switch (pick(d)) {
     case Shape::Small: return launch_fused<32, 256, 1, 4, 64, 4>(d, f, s);
     case Shape::Mid: return launch_fused<128, 256, 2, 4, 64, 3>(d, f, s);

@@ -65,8 +65,10 @@ def main():
                          "from x, no permuted copy)")
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
-    ap.add_argument("--cpu-tokens", type=int, default=192,
-                    help="tokens of the CPU-oracle sample (0 = skip the CPU baseline)")
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens of the CPU-oracle sample, at most the workload's N (0 = skip "
+                         "the CPU baseline); the oracle's fixed cost (weights to float64) "
+                         "dominates small samples")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, three "
                          "times (the reference kernel for HBM byte counters), then exit")
@@ -239,7 +241,7 @@ def main():
             roof = {"bound": "hbm", "achieved": f_bytes / (gateup_ms * 1e-3) / 1e9,
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] / roof["peak"]
-        roof["traffic"] = None
+        roof["traffic"] = measured_traffic(args.config + "_fused")
         roof["kernel"] = "fused expert FFN (gate/up + SwiGLU + down, one launch)"
         roof["algorithmic"] = {"flop": f_flops, "bytes": f_bytes}
     roof["avg_ms"] = gateup_ms

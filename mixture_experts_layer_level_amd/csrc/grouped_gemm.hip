@@ -14,8 +14,10 @@
 // Work list: expert e contributes ceil(m_e / BM) row tiles (m_e from
 // expert_offsets, read on the device); every workgroup prefix-sums them into
 // LDS at start-up, so no host synchronisation and no plan pass are needed.
-// Tiles are ordered expert-major, then column panel, then row tile, so
-// consecutive tiles share a weight panel.  The grid is persistent (a multiple
+// Tiles are ordered expert-major; within an expert, row tiles go in bands of
+// up to eight, and a band runs panel by panel with the row tile fastest, so
+// consecutive tiles share a weight panel and nearby ones share A rows.  The
+// grid is persistent (a multiple
 // of 8 workgroups); workgroup b runs on XCD b % 8 and each XCD walks its own
 // contiguous eighth of the list, so the row tiles that share a weight panel
 // meet in the same L2.
@@ -146,6 +148,8 @@ __device__ __forceinline__ void build_work_list(const GemmArgs& p, int32_t* msta
   if (lane == 63) mstart[p.E] = incl;
 }
 
+constexpr int kBand = 8;   // row tiles per band (see decode_tile)
+
 // Tile l -> (expert, column panel, first row, valid rows); all
 // workgroup-uniform, kept in scalar registers.
 struct Tile {
@@ -164,9 +168,16 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* ms
   Tile t;
   t.e = __builtin_amdgcn_readfirstlane(lo);
   const int mt_e = __builtin_amdgcn_readfirstlane(mstart[t.e + 1] - mstart[t.e]);
+  // Within an expert, row tiles go in bands of kBand and each band runs
+  // panel by panel: the tiles an XCD runs at once then share both their A
+  // rows and their weight panels in its L2 (with one band per expert, an
+  // expert of many row tiles ran one panel over all of them and re-read its
+  // A rows from HBM for every panel).
   const int idx = l - p.n_tiles * __builtin_amdgcn_readfirstlane(mstart[t.e]);
-  t.nt = idx / mt_e;
-  const int mt = idx % mt_e;
+  const int band = idx / (kBand * p.n_tiles), mt0 = band * kBand;
+  const int gb = min(kBand, mt_e - mt0), within = idx - band * kBand * p.n_tiles;
+  t.nt = within / gb;
+  const int mt = mt0 + within % gb;
   const int seg0 = __builtin_amdgcn_readfirstlane(p.offsets[t.e]);
   const int seg1 = __builtin_amdgcn_readfirstlane(p.offsets[t.e + 1]);
   // The expert's ceil(m / 32) row blocks are spread evenly over its mt_e row
@@ -368,18 +379,18 @@ struct Ring {
 };
 
 // Wait until at most n stages of this wave's DMA are still outstanding
-// (n is clamped to the supported values; waiting for more is always safe).
-template <int PW, int S>
-__device__ __forceinline__ void wait_stages(int n) {
-  if constexpr (S >= 4) {
-    if (n >= 3) { wait_vmcnt<3 * PW>(); return; }
+// (n is clamped to [0, N]; waiting for more is always safe).
+template <int PW, int N>
+__device__ __forceinline__ void wait_upto(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) { wait_vmcnt<N * PW>(); return; }
+    wait_upto<PW, N - 1>(n);
   }
-  if constexpr (S >= 3) {
-    if (n >= 2) { wait_vmcnt<2 * PW>(); return; }
-  }
-  if (n >= 1) { wait_vmcnt<PW>(); return; }
-  wait_vmcnt<0>();
 }
+template <int PW, int S>
+__device__ __forceinline__ void wait_stages(int n) { wait_upto<PW, S - 1>(n); }
 
 // FP8 scale area of a stage: wave w fetches LS 16-byte units, unit
 // (i * KB + kbl) * 2 + half holding rows 16*half .. 16*half+15 of its i-th
@@ -943,7 +954,9 @@ hipError_t launch_regs(const Dims& d, const GemmArgs& a0, int occupancy, hipStre
 }
 
 // Tile shape by the average number of rows per expert (R / E):
-//   <= 48  : 32 x 256 register-staged tiles (decode: the weight stream rules)
+//   <= 48  : 32 x 256 tiles (decode: the weight stream rules), 4 waves; an
+//            LDS-DMA ring of 64-deep stages (4, or 6 with FP8 weights) when
+//            k >= 1024, else register-staged
 //   <= 384 : 128 x 256 tiles, 8 waves (64 x 64 each), 64-deep stages, 3-stage ring
 //            (4 stages with FP8 weights, whose stages are a third smaller)
 //   else   : 256 x 256 tiles, 8 waves, 32-deep stages, 4-stage ring
@@ -965,7 +978,11 @@ namespace {
 template <int EPI, bool FP8>
 hipError_t launch_gemm(const Dims& d, const GemmArgs& a, hipStream_t s, Shape shape) {
   switch (shape) {
-    case Shape::Small: return launch_regs<32, 256, 1, 4, EPI, FP8>(d, a, 2, s);
+    case Shape::Small:
+      // the weight stream rules: a deep LDS-DMA ring (over 100 KB in flight
+      // per CU) when k is long enough to fill it, else register staging
+      if (a.Kd >= 1024) return launch_ring<32, 256, 1, 4, 64, FP8 ? 6 : 4, EPI, FP8>(d, a, s);
+      return launch_regs<32, 256, 1, 4, EPI, FP8>(d, a, 2, s);
     case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, FP8 ? 4 : 3, EPI, FP8>(d, a, s);
     default: return launch_ring<256, 256, 2, 4, 32, 4, EPI, FP8>(d, a, s);
   }

@@ -117,9 +117,16 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 // Work list prologue (wave 0): mstart[e] = row tiles of experts before e,
-// mstart[E] = all row tiles.
+// mstart[E] = all row tiles.  Expert e gets at least ceil(m_e / BM) row tiles.
+// With grid > 0 (a launch of grid workgroups that each take every grid-th
+// tile), spare tiles that would leave the last round partly empty are handed
+// out as extra row tiles, one at a time, to the expert with the most 32-row
+// blocks per row tile (never more row tiles than blocks): every workgroup then
+// runs the same number of tiles, each with fewer rows.  A tile's results do
+// not depend on its rows, so this changes no bit of the output.
 template <int BM>
-__device__ __forceinline__ void build_work_list(const GemmArgs& p, int32_t* mstart, int lane) {
+__device__ __forceinline__ void build_work_list(const GemmArgs& p, int32_t* mstart, int lane,
+                                                int grid) {
   const int per = (p.E + 63) / 64;
   const int e0 = lane * per;
   int local = 0;
@@ -127,8 +134,49 @@ __device__ __forceinline__ void build_work_list(const GemmArgs& p, int32_t* msta
     const int e = e0 + i;
     if (e < p.E) {
       const int m = p.offsets[e + 1] - p.offsets[e];
-      local += m > 0 ? (m + BM - 1) / BM : 0;
+      const int mt = m > 0 ? (m + BM - 1) / BM : 0;
+      mstart[e] = mt;
+      local += mt;
     }
+  }
+  if (grid > 0) {
+    int total = local;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) total += __shfl_xor(total, d, 64);
+    const int64_t t0 = (int64_t)total * p.n_tiles;
+    const int64_t rounds = (t0 + grid - 1) / grid;
+    for (int64_t extra = (rounds * grid - t0) / p.n_tiles; extra > 0; --extra) {
+      // this lane's candidate: most blocks per row tile, lower expert on ties
+      int bb = 0, bt = 1, be = -1;
+      for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < p.E) {
+          const int nb = (p.offsets[e + 1] - p.offsets[e] + 31) / 32, mt = mstart[e];
+          if (mt > 0 && mt < nb && (int64_t)nb * bt > (int64_t)bb * mt) {
+            bb = nb;
+            bt = mt;
+            be = e;
+          }
+        }
+      }
+      // the wave's best (a total order: ratio, then expert id)
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+        const int ob = __shfl_xor(bb, d, 64), ot = __shfl_xor(bt, d, 64);
+        const int oe = __shfl_xor(be, d, 64);
+        const int64_t l = (int64_t)ob * bt, r = (int64_t)bb * ot;
+        if (oe >= 0 && (be < 0 || l > r || (l == r && oe < be))) {
+          bb = ob;
+          bt = ot;
+          be = oe;
+        }
+      }
+      if (be < 0) break;                       // every expert has one block per tile
+      if (be >= e0 && be < e0 + per) mstart[be] += 1;
+    }
+    local = 0;
+    for (int i = 0; i < per; ++i)
+      if (e0 + i < p.E) local += mstart[e0 + i];
   }
   int incl = local;
 #pragma unroll
@@ -140,9 +188,9 @@ __device__ __forceinline__ void build_work_list(const GemmArgs& p, int32_t* msta
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e < p.E) {
+      const int mt = mstart[e];
       mstart[e] = run;
-      const int m = p.offsets[e + 1] - p.offsets[e];
-      run += m > 0 ? (m + BM - 1) / BM : 0;
+      run += mt;
     }
   }
   if (lane == 63) mstart[p.E] = incl;
@@ -615,7 +663,7 @@ grouped_gemm_ring(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0];
-  if (wave == 0) build_work_list<BM>(p, mstart, lane);
+  if (wave == 0) build_work_list<BM>(p, mstart, lane, gridDim.x);
   __syncthreads();
   const int total = p.n_tiles * __builtin_amdgcn_readfirstlane(mstart[p.E]);
   const int xcd = blockIdx.x & 7, P8 = gridDim.x >> 3, j0 = blockIdx.x >> 3;
@@ -678,7 +726,7 @@ grouped_ffn_fused(FusedArgs f) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0];
-  if (wave == 0) build_work_list<BM>(f.gu, mstart, lane);
+  if (wave == 0) build_work_list<BM>(f.gu, mstart, lane, 0);   // one row split for both lists
   __syncthreads();
   // No branch on the loop's path may depend on the lane (or look as if it
   // did): with an "if (tid == 0)" at the loop head and another after the
@@ -839,7 +887,7 @@ grouped_gemm_regs(GemmArgs p) {
   const int lrow = tid / RCH, lchunk = tid % RCH;   // bf16 loader mapping
   const int qrow = tid / QCH, qchunk = tid % QCH;   // FP8 weight loader mapping
 
-  if (wave == 0) build_work_list<BM>(p, mstart, lane);
+  if (wave == 0) build_work_list<BM>(p, mstart, lane, gridDim.x);
   __syncthreads();
   const int total = p.n_tiles * __builtin_amdgcn_readfirstlane(mstart[p.E]);
   const int xcd = blockIdx.x & 7, P8 = gridDim.x >> 3, j0 = blockIdx.x >> 3;

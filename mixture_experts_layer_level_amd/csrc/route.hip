@@ -29,33 +29,32 @@ namespace {
 // is no LDS staging; the S partial tiles are summed through LDS in
 // wave order, so the result does not depend on scheduling.
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t rne_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16, round to nearest even (one
+// v_cvt_pk_bf16_f32), and the bf16 values back as fp32.
+__device__ __forceinline__ uint32_t rne_pk(f32x2_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ f32x2_t unpk(uint32_t b) {
+  return f32x2_t{__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u)};
 }
 
-// Split 8 fp32 weights into the hi / mid / lo bf16 vectors.
+// Split 8 fp32 weights into the hi / mid / lo bf16 vectors: hi = bf16(w),
+// mid = bf16(w - hi) (w - hi is exact), lo = w - hi - mid (exact, at most 8
+// significant bits, so its top 16 bits are the value).
 __device__ __forceinline__ void split3(const float4& a, const float4& b, bf16x8_t& hi,
                                        bf16x8_t& mid, bf16x8_t& lo) {
-  const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const f32x2_t w[4] = {{a.x, a.y}, {a.z, a.w}, {b.x, b.y}, {b.z, b.w}};
   uint32_t h[4], m[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t hb[2], mb[2], lb[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float v = w[2 * i + j];
-      hb[j] = rne_bf16(v);
-      const float r1 = v - __uint_as_float(hb[j] << 16);      // exact
-      mb[j] = rne_bf16(r1);
-      const float r2 = r1 - __uint_as_float(mb[j] << 16);     // exact, fits bf16
-      lb[j] = __float_as_uint(r2) >> 16;
-    }
-    h[i] = hb[0] | (hb[1] << 16);
-    m[i] = mb[0] | (mb[1] << 16);
-    l[i] = lb[0] | (lb[1] << 16);
+    h[i] = rne_pk(w[i]);
+    const f32x2_t r1 = w[i] - unpk(h[i]);
+    m[i] = rne_pk(r1);
+    const f32x2_t r2 = r1 - unpk(m[i]);
+    l[i] = (__float_as_uint(r2.x) >> 16) | (__float_as_uint(r2.y) & 0xffff0000u);
   }
   hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
   mid = __builtin_bit_cast(bf16x8_t, make_uint4(m[0], m[1], m[2], m[3]));
@@ -74,8 +73,17 @@ router_mfma_kernel(int64_t N, int D, int E, int vec4, const uint16_t* __restrict
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int S = blockDim.x >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * WT;
-  const int e0 = blockIdx.y * WT;
+  // This workgroup's tile.  Tiles are numbered token tile by token tile (the
+  // expert tiles of one token tile are consecutive) and cut into eight
+  // contiguous parts, one per XCD (workgroup b runs on XCD b % 8), so the
+  // workgroups that read the same x rows run together and share them in one
+  // L2.  The grid is a multiple of 8; workgroups past the last tile leave.
+  const int ne = (E + WT - 1) / WT;
+  const int64_t total = ((N + WT - 1) / WT) * ne;
+  const int64_t v = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (v >= total) return;
+  const int64_t n0 = (v / ne) * WT;
+  const int e0 = (int)(v % ne) * WT;
   const int r = lane & 31, kh = lane >> 5;
 
   // k order inside a 64-deep block: MFMA step ks takes, in lane half kh,
@@ -134,12 +142,52 @@ router_mfma_kernel(int64_t N, int D, int E, int vec4, const uint16_t* __restrict
   };
   const int nkb = D / 64;
   if constexpr (WT == 64) {
-    // 64x64 tiles are issued when the grid already fills the chip: one
-    // register set, no look-ahead (two sets would spill).
-    Blk b0;
-    for (int kb = wave; kb < nkb; kb += S) {
-      load(b0, kb);
-      compute(b0);
+    // 64x64 tiles: two full register sets would spill, so the look-ahead is
+    // by half blocks (k-steps 0-1, then 2-3): the next half loads while the
+    // MFMAs of the current one run, in the registers of one block.  Same k
+    // order as above, so the same sums.
+    struct Half {
+      uint4 x[2][TB];
+      float4 wa[2][TB], wb[2][TB];
+    };
+    auto load_half = [&](Half& h, int kb, int part) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int k = kb * 64 + (2 * part + q) * 8;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          h.x[q][t] = *reinterpret_cast<const uint4*>(xr[t] + k);
+          h.wa[q][t] = *reinterpret_cast<const float4*>(wr[t] + k);
+          h.wb[q][t] = *reinterpret_cast<const float4*>(wr[t] + k + 4);
+        }
+      }
+    };
+    auto compute_half = [&](const Half& h) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < TB; ++i) {
+          bf16x8_t hi, mid, lo;
+          split3(h.wa[q][i], h.wb[q][i], hi, mid, lo);
+#pragma unroll
+          for (int j = 0; j < TB; ++j) {
+            const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, h.x[q][j]);
+            acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, xa, acc_hi[i][j], 0, 0, 0);
+            acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, xa, acc_lo[i][j], 0, 0, 0);
+            acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, xa, acc_lo[i][j], 0, 0, 0);
+          }
+        }
+    };
+    Half h0, h1;
+    int kb = wave;
+    if (kb < nkb) load_half(h0, kb, 0);
+    while (kb < nkb) {
+      load_half(h1, kb, 1);
+      compute_half(h0);
+      const int kn = kb + S;
+      if (kn < nkb) load_half(h0, kn, 0);
+      compute_half(h1);
+      kb = kn;
     }
   } else {
     Blk b0, b1;
@@ -299,7 +347,7 @@ hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, 
   const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
   if (t64 >= device_cu_count()) {
     const int S = nkb < 4 ? nkb : 4;
-    dim3 grid((unsigned)((d.N + 63) / 64), (unsigned)((d.E + 63) / 64));
+    dim3 grid((unsigned)((t64 + 7) / 8 * 8));
     hipLaunchKernelGGL(router_mfma_kernel<64>, grid, dim3(64 * S),
                        (S - 1) * 64 * 68 * sizeof(float), s, d.N, d.D, d.E, vec4, x, w,
                        logits);
@@ -310,7 +358,7 @@ hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, 
   if (S > 8) S = 8;
   if (S > nkb) S = nkb;
   if (S < 1) S = 1;
-  dim3 grid((unsigned)((d.N + 31) / 32), (unsigned)((d.E + 31) / 32));
+  dim3 grid((unsigned)((t32 + 7) / 8 * 8));
   hipLaunchKernelGGL(router_mfma_kernel<32>, grid, dim3(64 * S), (S - 1) * 32 * 36 * sizeof(float), s,
                      d.N, d.D, d.E, vec4, x, w, logits);
   return hipGetLastError();

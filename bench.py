@@ -132,60 +132,68 @@ def main():
         qg, qu, qd = quant(wg), quant(wu), quant(wd)
         torch.cuda.synchronize()
 
+    # ev: six events per step, recorded on the launch stream before the route
+    # and after the route, permute, gate/up (or up, or fused FFN), down and
+    # combine calls
+    def rec(ev, i):
+        if ev is not None:
+            ev[i].record(stream)
+
     def step_gelu(ev=None):
         i = inp
+        rec(ev, 0)
         moe.route_mlp(p, x, i["w_proj"], i["b_proj"], i["w_out"], i["b_out"], logits, ids, w, ws,
                       features=feats, stream=stream)
+        rec(ev, 1)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
+        rec(ev, 2)
         moe.expert_up_gelu(p, x_perm, offsets, i["w1"], i["b1"], h, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+        rec(ev, 3)
         moe.expert_down_bias(p, h, offsets, i["w2"], i["b2"], out_perm, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        rec(ev, 4)
         moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
+        rec(ev, 5)
 
     def step_fused(ev=None):
+        rec(ev, 0)
         moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
+        rec(ev, 1)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row, None, ws, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
+        rec(ev, 2)
         moe.fused_ffn(p, x, row_token, offsets, wg, wu, wd, out_perm, ws, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-            ev[2].record(stream)
+        rec(ev, 3)
+        rec(ev, 4)
         moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
+        rec(ev, 5)
 
     def step(ev=None):
         if gelu:
             return step_gelu(ev)
         if args.fused:
             return step_fused(ev)
+        rec(ev, 0)
         moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
+        rec(ev, 1)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
+        rec(ev, 2)
         if fp8:
             moe.expert_gateup_fp8(p, x_perm, offsets, qg, qu, h, stream=stream)
         else:
             moe.expert_gateup(p, x_perm, offsets, wg, wu, h, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+        rec(ev, 3)
         if fp8:
             moe.expert_down_fp8(p, h, offsets, qd, out_perm, stream=stream)
         else:
             moe.expert_down(p, h, offsets, wd, out_perm, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        rec(ev, 4)
         moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
+        rec(ev, 5)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6))
            for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -197,8 +205,12 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    gateup_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / args.steps
-    down_ms = sum(b.elapsed_time(c) for _, b, c in evs) / args.steps
+
+    def stage_ms(i, j):
+        return sum(ev[i].elapsed_time(ev[j]) for ev in evs) / args.steps
+    route_ms, permute_ms = stage_ms(0, 1), stage_ms(1, 2)
+    gateup_ms, down_ms, combine_ms = stage_ms(2, 3), stage_ms(3, 4), stage_ms(4, 5)
+    per_step = sorted(ev[0].elapsed_time(ev[5]) for ev in evs)
 
     counts_h = counts.cpu().numpy().astype(np.int64)
     kept = int(np.minimum(counts_h, capv).sum()) if capv else cfg.S
@@ -246,6 +258,30 @@ def main():
         roof["algorithmic"] = {"flop": f_flops, "bytes": f_bytes}
     roof["avg_ms"] = gateup_ms
     roof.setdefault("algorithmic", {"flop": gu_flops, "bytes": gu_bytes})
+    # the HBM-bound stages against 8 TB/s: permute (x read once, x_perm rows
+    # written, ids read, row_token and slot_row written, offsets), combine
+    # (out_perm rows read, y written, slot_row and weights read)
+    S_ = N * K
+    perm_bytes = (S_ * 4 * 3 + (E + 1) * 4 +
+                  (0 if args.fused else N * D * 2 + R * D * 2))
+    comb_bytes = kept * D * 2 + N * D * 2 + S_ * 8
+    stages = {
+        "route_ms": route_ms, "permute_ms": permute_ms, "ffn_ms": gateup_ms + down_ms,
+        "combine_ms": combine_ms,
+        "permute_gbps": perm_bytes / (permute_ms * 1e-3) / 1e9,
+        "permute_frac_hbm": perm_bytes / (permute_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "combine_gbps": comb_bytes / (combine_ms * 1e-3) / 1e9,
+        "combine_frac_hbm": comb_bytes / (combine_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "permute_bytes": perm_bytes, "combine_bytes": comb_bytes,
+        "step_ms_min": per_step[0], "step_ms_median": per_step[len(per_step) // 2],
+        "step_ms_max": per_step[-1],
+    }
+    if capv:   # the padded layout runs every expert over cap rows
+        exec_flops = flops - (4.0 if gelu else 6.0) * D * F * kept + \
+            (4.0 if gelu else 6.0) * D * F * E * capv
+        stages["kept_slots"] = kept
+        stages["utilisation"] = kept / (E * capv)
+        stages["executed_tflops"] = exec_flops / (ms_step * 1e-3) / 1e12
     line = {
         "metric": "MoE-layer tokens/sec + TFLOPS (% bf16 MFMA peak) / HBM GB/s (% peak), 1 GPU",
         "value": N / (ms_step * 1e-3),
@@ -275,6 +311,7 @@ def main():
         "down_ms": down_ms,
         "max_expert_rows": int(counts_h.max()),
         "dropped_slots": int(cfg.S - kept),
+        "stages": stages,
         "roofline": roof,
         "cpu_baseline": None,
     }
@@ -332,9 +369,22 @@ def cpu_baseline(cfg, inp, n, capv, fp8=False):
     O.forward(x, wr, bias, wg, wu, wd, cfg.K, cfg.gating, cap=cap)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    slots = n * cfg.K if cap is None else min(n * cfg.K, cfg.E * cap)
+    flop = 2.0 * n * cfg.D * cfg.E + 6.0 * cfg.D * cfg.F * slots
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "gflops": flop / dt / 1e9, "cpu_model": cpu_model(),
             "sample": f"first {n} of {cfg.N} tokens, same weights, float64 numpy oracle "
                       f"({dt:.1f} s)"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline_gelu(cfg, inp, n):
@@ -356,7 +406,10 @@ def cpu_baseline_gelu(cfg, inp, n):
                    a["b1"], a["w2"], a["b2"], cfg.K)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    D4 = cfg.D // 4
+    flop = 2.0 * n * (cfg.D * D4 + D4 * cfg.E) + 4.0 * cfg.D * cfg.F * n * cfg.K
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "gflops": flop / dt / 1e9, "cpu_model": cpu_model(),
             "sample": f"first {n} of {cfg.N} tokens, same weights, float64 numpy oracle "
                       f"({dt:.1f} s)"}
 

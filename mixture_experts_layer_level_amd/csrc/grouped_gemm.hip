@@ -1001,18 +1001,22 @@ hipError_t launch_regs(const Dims& d, const GemmArgs& a0, int occupancy, hipStre
   return hipGetLastError();
 }
 
-// Tile shape by the average number of rows per expert (R / E):
+// Tile shape by the average number of rows per expert (R / E).  Barriers cost
+// more than prefetch depth gains, so stages are as deep as LDS allows (FP8
+// weight stages are smaller: 128-deep when k is a multiple of 128):
 //   <= 48  : 32 x 256 tiles (decode: the weight stream rules), 4 waves; an
-//            LDS-DMA ring of 64-deep stages (4, or 6 with FP8 weights) when
+//            LDS-DMA ring of 64-deep stages (4; FP8: 3 of 128-deep) when
 //            k >= 1024, else register-staged
-//   <= 384 : 128 x 256 tiles, 8 waves (64 x 64 each), 64-deep stages, 3-stage ring
-//            (4 stages with FP8 weights, whose stages are a third smaller)
-//   else   : 256 x 256 tiles, 8 waves, 32-deep stages, 4-stage ring
+//   <= 192 : 128 x 256 tiles, 8 waves (64 x 64 each), 64-deep stages, 3-stage ring
+//            (FP8: 2 stages of 128-deep)
+//   else   : 256 x 256 tiles, 8 waves, 64-deep stages, 2-stage ring (3 with FP8
+//            weights): one barrier per 64 k (32-deep stages, twice the
+//            barriers, were 5-12% slower)
 enum class Shape { Small, Mid, Large };
 inline Shape pick(const Dims& d) {
   const double avg = (double)d.R / d.E;
   if (avg <= 48.0) return Shape::Small;
-  if (avg <= 384.0) return Shape::Mid;
+  if (avg <= 192.0) return Shape::Mid;
   return Shape::Large;
 }
 
@@ -1029,10 +1033,18 @@ hipError_t launch_gemm(const Dims& d, const GemmArgs& a, hipStream_t s, Shape sh
     case Shape::Small:
       // the weight stream rules: a deep LDS-DMA ring (over 100 KB in flight
       // per CU) when k is long enough to fill it, else register staging
+      if constexpr (FP8) {
+        if (a.Kd >= 1024 && a.Kd % 128 == 0)
+          return launch_ring<32, 256, 1, 4, 128, 3, EPI, FP8>(d, a, s);
+      }
       if (a.Kd >= 1024) return launch_ring<32, 256, 1, 4, 64, FP8 ? 6 : 4, EPI, FP8>(d, a, s);
       return launch_regs<32, 256, 1, 4, EPI, FP8>(d, a, 2, s);
-    case Shape::Mid: return launch_ring<128, 256, 2, 4, 64, FP8 ? 4 : 3, EPI, FP8>(d, a, s);
-    default: return launch_ring<256, 256, 2, 4, 32, 4, EPI, FP8>(d, a, s);
+    case Shape::Mid:
+      if constexpr (FP8) {
+        if (a.Kd % 128 == 0) return launch_ring<128, 256, 2, 4, 128, 2, EPI, FP8>(d, a, s);
+      }
+      return launch_ring<128, 256, 2, 4, 64, FP8 ? 4 : 3, EPI, FP8>(d, a, s);
+    default: return launch_ring<256, 256, 2, 4, 64, FP8 ? 3 : 2, EPI, FP8>(d, a, s);
   }
 }
 
@@ -1191,7 +1203,7 @@ hipError_t launch_fused_ffn(const Dims& d, const uint16_t* x, const int32_t* row
   switch (pick(d)) {
     case Shape::Small: return launch_fused<32, 256, 1, 4, 64, 4>(d, f, s);
     case Shape::Mid: return launch_fused<128, 256, 2, 4, 64, 3>(d, f, s);
-    default: return launch_fused<256, 256, 2, 4, 32, 4>(d, f, s);
+    default: return launch_fused<256, 256, 2, 4, 64, 2>(d, f, s);
   }
 }
 

@@ -1005,8 +1005,8 @@ hipError_t launch_regs(const Dims& d, const GemmArgs& a0, int occupancy, hipStre
 // more than prefetch depth gains, so stages are as deep as LDS allows (FP8
 // weight stages are smaller: 128-deep when k is a multiple of 128):
 //   <= 48  : 32 x 256 tiles (decode: the weight stream rules), 4 waves; an
-//            LDS-DMA ring of 64-deep stages (4; FP8: 3 of 128-deep) when
-//            k >= 1024, else register-staged
+//            LDS-DMA ring of 64-deep stages (4) when k >= 1024 (FP8: 3 of
+//            128-deep when k >= 512), else register-staged
 //   <= 192 : 128 x 256 tiles, 8 waves (64 x 64 each), 64-deep stages, 3-stage ring
 //            (FP8: 2 stages of 128-deep)
 //   else   : 256 x 256 tiles, 8 waves, 64-deep stages, 2-stage ring (3 with FP8
@@ -1034,7 +1034,7 @@ hipError_t launch_gemm(const Dims& d, const GemmArgs& a, hipStream_t s, Shape sh
       // the weight stream rules: a deep LDS-DMA ring (over 100 KB in flight
       // per CU) when k is long enough to fill it, else register staging
       if constexpr (FP8) {
-        if (a.Kd >= 1024 && a.Kd % 128 == 0)
+        if (a.Kd >= 512 && a.Kd % 128 == 0)
           return launch_ring<32, 256, 1, 4, 128, 3, EPI, FP8>(d, a, s);
       }
       if (a.Kd >= 1024) return launch_ring<32, 256, 1, 4, 64, FP8 ? 6 : 4, EPI, FP8>(d, a, s);

@@ -48,7 +48,7 @@ layer stores them: logits and router weights to fp32, and the bf16 tensors
 ``h`` (FFN intermediate), ``out_perm`` (FFN output rows) and ``y`` (layer
 output) to bf16 with round-to-nearest-even.  Top-K is decided on fp32 keys.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 ties in top-K go to the lower expert id, -0.0 equals +0.0 and NaN keys sort
 last; the K outputs are in descending key order; selection in sigmoid mode is
 done on the key itself (sigmoid is strictly increasing); the bias is one fp32

@@ -22,17 +22,21 @@
 // contiguous eighth of the list, so the row tiles that share a weight panel
 // meet in the same L2.
 //
-// Two kernels:
-//   grouped_gemm_ring  (prefill-sized experts): operands go straight from
-//     global memory into an S-stage LDS ring with LDS-DMA
-//     (global_load_lds_dwordx4), BK-deep stages, one barrier per stage.  The
-//     DMA for stage kt+S is issued right after the barrier of stage kt, when
-//     every wave has read all of stage kt, behind the last MFMAs of stage kt;
-//     the fragments of the first k-step of stage kt+1 are read from LDS while
+// Three kernels:
+//   grouped_gemm_split (256 x 256 tiles, bf16 weights, E <= 256): separate
+//     LDS rings for the A rows (2 slots, one stage ahead) and the weight rows
+//     (3 slots, two stages ahead), filled by LDS-DMA (global_load_lds_dwordx4)
+//     whose instructions are spread over the stage's MFMAs; one barrier per
+//     64-deep stage.
+//   grouped_gemm_ring  (other prefill-sized tiles, FP8 weights): A and weight
+//     rows of a stage share one slot of an S-stage LDS ring.  The DMA for
+//     stage kt+S is issued right after the barrier of stage kt, when every
+//     wave has read all of stage kt, behind the last MFMAs of stage kt; the
+//     fragments of the first k-step of stage kt+1 are read from LDS while
 //     those MFMAs run.
 //   grouped_gemm_regs  (decode-sized experts, 32-row tiles): operands staged
 //     through registers into a double-buffered LDS tile.
-// Both accumulate k in the same order (kchunk below), so they give
+// All accumulate k in the same order (kchunk below), so they give
 // bit-identical results.
 //
 // Block-scaled FP8 weights (FP8 = true; the FP8 weights of 第四层 DeepGEMM &
@@ -206,22 +210,18 @@ struct Tile {
   int rows;
   int mtg;      // row tile over all experts: mstart[e] + row tile within the expert
 };
+// Tile l of expert e, whose row tiles are [ms_e, ms_e1) of the work list.
 template <int BM>
-__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* mstart, int l) {
-  int lo = 0, hi = p.E - 1;
-  while (lo < hi) {  // last e with n_tiles * mstart[e] <= l
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.n_tiles * mstart[mid] <= l) lo = mid; else hi = mid - 1;
-  }
+__device__ __forceinline__ Tile tile_of(const GemmArgs& p, int e, int ms_e, int ms_e1, int l) {
   Tile t;
-  t.e = __builtin_amdgcn_readfirstlane(lo);
-  const int mt_e = __builtin_amdgcn_readfirstlane(mstart[t.e + 1] - mstart[t.e]);
+  t.e = e;
+  const int mt_e = ms_e1 - ms_e;
   // Within an expert, row tiles go in bands of kBand and each band runs
   // panel by panel: the tiles an XCD runs at once then share both their A
   // rows and their weight panels in its L2 (with one band per expert, an
   // expert of many row tiles ran one panel over all of them and re-read its
   // A rows from HBM for every panel).
-  const int idx = l - p.n_tiles * __builtin_amdgcn_readfirstlane(mstart[t.e]);
+  const int idx = l - p.n_tiles * ms_e;
   const int band = idx / (kBand * p.n_tiles), mt0 = band * kBand;
   const int gb = min(kBand, mt_e - mt0), within = idx - band * kBand * p.n_tiles;
   t.nt = within / gb;
@@ -236,8 +236,126 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* ms
   const int b0 = (int)((int64_t)mt * nbk / mt_e), b1 = (int)((int64_t)(mt + 1) * nbk / mt_e);
   t.row0 = (int64_t)seg0 + 32 * b0;
   t.rows = min(32 * (b1 - b0), m - 32 * b0);
-  t.mtg = __builtin_amdgcn_readfirstlane(mstart[t.e]) + mt;
+  t.mtg = ms_e + mt;
   return t;
+}
+
+template <int BM>
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* mstart, int l) {
+  int lo = 0, hi = p.E - 1;
+  while (lo < hi) {  // last e with n_tiles * mstart[e] <= l
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.n_tiles * mstart[mid] <= l) lo = mid; else hi = mid - 1;
+  }
+  const int e = __builtin_amdgcn_readfirstlane(lo);
+  return tile_of<BM>(p, e, __builtin_amdgcn_readfirstlane(mstart[e]),
+                     __builtin_amdgcn_readfirstlane(mstart[e + 1]), l);
+}
+
+// The work list of build_work_list kept in registers instead of LDS: lane
+// holds ms[i] = mstart[lane * PER + i] for the experts lane * PER + i < E
+// (E <= 64 * PER); returns mstart[E], the number of row tiles.  Same row
+// tiles, same extra tiles, same order as build_work_list.
+template <int BM, int PER>
+__device__ __forceinline__ int build_work_list_regs(const GemmArgs& p, int (&ms)[PER], int lane,
+                                                    int grid) {
+  const int e0 = lane * PER;
+  int nbk[PER];      // 32-row blocks of each expert
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = e0 + i;
+    int mt = 0, nb = 0;
+    if (e < p.E) {
+      const int m = p.offsets[e + 1] - p.offsets[e];
+      mt = m > 0 ? (m + BM - 1) / BM : 0;
+      nb = (m + 31) / 32;
+    }
+    ms[i] = mt;
+    nbk[i] = nb;
+    local += mt;
+  }
+  if (grid > 0) {
+    int total = local;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) total += __shfl_xor(total, d, 64);
+    const int64_t t0 = (int64_t)total * p.n_tiles;
+    const int64_t rounds = (t0 + grid - 1) / grid;
+    for (int64_t extra = (rounds * grid - t0) / p.n_tiles; extra > 0; --extra) {
+      int bb = 0, bt = 1, be = -1;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int nb = nbk[i], mt = ms[i];
+        if (mt > 0 && mt < nb && (int64_t)nb * bt > (int64_t)bb * mt) {
+          bb = nb;
+          bt = mt;
+          be = e0 + i;
+        }
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+        const int ob = __shfl_xor(bb, d, 64), ot = __shfl_xor(bt, d, 64);
+        const int oe = __shfl_xor(be, d, 64);
+        const int64_t l = (int64_t)ob * bt, r = (int64_t)bb * ot;
+        if (oe >= 0 && (be < 0 || l > r || (l == r && oe < be))) {
+          bb = ob;
+          bt = ot;
+          be = oe;
+        }
+      }
+      if (be < 0) break;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (e0 + i == be) ms[i] += 1;
+    }
+    local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) local += ms[i];
+  }
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
+  }
+  int run = incl - local;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int mt = ms[i];
+    ms[i] = run;
+    run += mt;
+  }
+  return __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+}
+
+// mstart[e] from the registers of build_work_list_regs (e <= E, uniform).
+template <int PER>
+__device__ __forceinline__ int mstart_at(const int (&ms)[PER], int e, int E, int total) {
+  if (e >= E) return total;
+  // read every register of the owning lane, then pick one (selecting on
+  // the per-lane array first would index it dynamically, in scratch)
+  const int le = e / PER, ie = e % PER;
+  int v = __builtin_amdgcn_readlane(ms[0], le);
+#pragma unroll
+  for (int i = 1; i < PER; ++i) {
+    const int w = __builtin_amdgcn_readlane(ms[i], le);
+    v = ie == i ? w : v;
+  }
+  return v;
+}
+
+template <int BM, int PER>
+__device__ __forceinline__ Tile decode_tile_regs(const GemmArgs& p, const int (&ms)[PER],
+                                                 int total, int lane, int l) {
+  // experts with n_tiles * mstart[e] <= l; the last of them holds tile l
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    c += __builtin_popcountll(
+        __ballot(lane * PER + i < p.E && p.n_tiles * ms[i] <= l));
+  const int e = c - 1;
+  return tile_of<BM>(p, e, mstart_at<PER>(ms, e, p.E, total),
+                     mstart_at<PER>(ms, e + 1, p.E, total), l);
 }
 
 // Weight row of tile row r (r in [0, BN)) and whether it is an up row.  In
@@ -674,6 +792,281 @@ grouped_gemm_ring(GemmArgs p) {
                                                wave, lane);
 }
 
+// ------------------------------------------------------------ split ring
+//
+// In the ring above a stage's A rows and weight rows share one LDS slot; at
+// 256 x 256 tiles two slots fill LDS, so while a CU computes one stage it has
+// only the next stage's bytes in flight.  Where the weights stream from HBM
+// (one row tile per expert, as at the DeepSeek-V3 shape) that is too little
+// to cover HBM latency.  The split ring keeps two rings: SA = 2 slots of A
+// rows, one stage ahead (A rows are mostly L2 hits: every column panel of a
+// row tile reads them), and SB slots of weight rows, SB - 1 stages ahead.
+// The rings fill LDS, so the work list's row-tile prefix is kept in
+// registers (build_work_list_regs).  Same tiles, same MFMAs in the same k
+// order as the ring kernel: the results are bit-identical.
+template <int BM, int BN, int WM, int WN, int BK, int SB_>
+struct Split {
+  using R = Ring<BM, BN, WM, WN, BK, 2, false>;   // tile geometry and DMA split
+  static constexpr int SA = 2, SB = SB_;
+  static constexpr int A_BYTES = R::A_U4 * 16, B_BYTES = R::B_U4 * 16;
+  static_assert(SA * A_BYTES + SB * B_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(SB >= 3 && 2 * R::PWB + R::PWA <= 63, "vmcnt range");
+};
+
+// MFMA fragments of k-step ks from an A slot and a weight slot (bf16; A
+// blocks mb >= nmb are not read).
+template <class R>
+__device__ __forceinline__ void read_frags_split(bf16x8_t (&af)[R::MB], bf16x8_t (&bfr)[R::NB],
+                                                 const uint4* sa, const uint4* sb, int ks, int wm,
+                                                 int wn, int lane, int nmb) {
+  constexpr int BK = R::CHA * 8;
+  const int kc = kchunk(ks, lane);
+#pragma unroll
+  for (int mb = 0; mb < R::MB; ++mb) {
+    const int r = wm * R::TM + mb * 32 + (lane & 31);
+    if (mb < nmb) af[mb] = __builtin_bit_cast(bf16x8_t, sa[r * R::CHA + (kc ^ swz<BK>(r))]);
+  }
+#pragma unroll
+  for (int nb = 0; nb < R::NB; ++nb) {
+    const int r = wn * R::TN + nb * 32 + (lane & 31);
+    bfr[nb] = __builtin_bit_cast(bf16x8_t, sb[r * R::CHB + (kc ^ swz<BK>(r))]);
+  }
+}
+
+// MFMAs [F, F + C) of one k-step, in mfma_step's (mb, nb) order.
+template <int F, int C, int MB, int NB>
+__device__ __forceinline__ void mfma_part(f32x16_t (&acc)[MB][NB], const bf16x8_t (&af)[MB],
+                                          const bf16x8_t (&bfr)[NB], int nmb) {
+#pragma unroll
+  for (int i = F; i < F + C; ++i) {
+    const int mb = i / NB, nb = i % NB;
+    if (mb < nmb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[mb][nb], 0, 0, 0);
+  }
+}
+
+template <int J, int C, int MB, int NB, class DmaA1>
+__device__ __forceinline__ void mfma_dma_a(f32x16_t (&acc)[MB][NB], const bf16x8_t (&af)[MB],
+                                           const bf16x8_t (&bfr)[NB], int nmb, bool an, int sa,
+                                           int kt, const DmaA1& dma_a1) {
+  mfma_part<J * C, C, MB, NB>(acc, af, bfr, nmb);
+  __builtin_amdgcn_sched_barrier(0);
+  if (an) dma_a1(sa, kt, J);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The k loop of a split-ring tile.  Stage kt's A rows are in A slot kt % 2,
+// its weight rows in weight slot kt % SB.  The DMA is spread over the stage
+// instead of being issued in one burst after the barrier: a CU's texture
+// path takes about as long to accept one stage's 64 DMA instructions as the
+// matrix cores take to compute half a stage, and a wave stalled behind its
+// DMA issues no MFMAs (issued in one burst, a 256 x 256 tile's stage took
+// 8-10% longer).
+//   - After the barrier that ends stage kt, A slot kt % 2 and weight slot
+//     kt % SB are free.  The last k-step's MFMAs of stage kt go first, each
+//     quarter followed by one of the wave's PWA A instructions of stage
+//     kt + 2 (A rows have one stage to land); then the first weight
+//     instruction of stage kt + SB.
+//   - In stage kt + 1, k-step ks (ks < KS - 1) is followed by weight
+//     instruction ks + 1 of that same stage kt + SB (the weights have
+//     SB - 1 stages to land).
+// So when stage kt ends, the DMA this wave issued after the A rows of stage
+// kt + 1 is exactly the PWB weight instructions of stage kt + SB - 1; the
+// weight rows of stage kt + 1 went before them.
+template <class SP, int NMB, class DmaA1, class DmaB1>
+__device__ __forceinline__ void split_kloop(f32x16_t (&acc)[SP::R::MB][SP::R::NB],
+                                            uint4 (*la)[SP::R::A_U4], uint4 (*lb)[SP::R::B_U4],
+                                            int nk, int wm, int wn, int lane,
+                                            const DmaA1& dma_a1, const DmaB1& dma_b1) {
+  using R = typename SP::R;
+  constexpr int MB = R::MB, NB = R::NB, KS = R::KS, PWA = R::PWA, PWB = R::PWB, SB = SP::SB;
+  constexpr int C = MB * NB / PWA;                   // MFMAs per A instruction
+  static_assert(PWB == KS && C * PWA == MB * NB && PWA == 4, "DMA spread");
+  bf16x8_t fa[2][MB], fb[2][NB];
+  read_frags_split<R>(fa[0], fb[0], la[0], lb[0], 0, wm, wn, lane, NMB);
+  int sa = 0, sb = 0, sbp = SB - 1;   // slots of stage kt; weight slot of stage kt - 1
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint4* ca = la[sa];
+    const uint4* cb = lb[sb];
+    const bool bdef = kt + SB - 1 < nk;   // stage kt + SB - 1 exists: its DMA goes on here
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      read_frags_split<R>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], ca, cb, ks + 1, wm, wn, lane, NMB);
+      mfma_step(acc, fa[ks & 1], fb[ks & 1], NMB);
+      if (bdef) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma_b1(sbp, kt + SB - 1, ks + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // this wave has read all of stage kt, and its DMA of stage kt+1 landed
+    wait_lgkmcnt0();
+    if (kt + 1 < nk) {
+      if (bdef) wait_vmcnt<PWB>();
+      else wait_vmcnt<0>();
+    }
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const bool an = kt + 2 < nk;
+    const bf16x8_t(&fl)[MB] = fa[(KS - 1) & 1];
+    const bf16x8_t(&gl)[NB] = fb[(KS - 1) & 1];
+    const int san = sa ^ 1, sbn = sb + 1 == SB ? 0 : sb + 1;
+    mfma_dma_a<0, C>(acc, fl, gl, NMB, an, sa, kt + 2, dma_a1);
+    mfma_dma_a<1, C>(acc, fl, gl, NMB, an, sa, kt + 2, dma_a1);
+    mfma_dma_a<2, C>(acc, fl, gl, NMB, an, sa, kt + 2, dma_a1);
+    mfma_dma_a<3, C>(acc, fl, gl, NMB, an, sa, kt + 2, dma_a1);
+    if (kt + SB < nk) dma_b1(sb, kt + SB, 0);
+    sbp = sb;
+    sa = san;
+    sb = sbn;
+    if (kt + 1 < nk)
+      read_frags_split<R>(fa[KS & 1], fb[KS & 1], la[sa], lb[sb], 0, wm, wn, lane, NMB);
+  }
+}
+
+template <class SP, int N, class DmaA1, class DmaB1>
+__device__ __forceinline__ void split_kloop_n(int nmb, f32x16_t (&acc)[SP::R::MB][SP::R::NB],
+                                              uint4 (*la)[SP::R::A_U4],
+                                              uint4 (*lb)[SP::R::B_U4], int nk, int wm, int wn,
+                                              int lane, const DmaA1& dma_a1, const DmaB1& dma_b1) {
+  if constexpr (N == 0) {
+    split_kloop<SP, 0>(acc, la, lb, nk, wm, wn, lane, dma_a1, dma_b1);
+  } else {
+    if (nmb == N) split_kloop<SP, N>(acc, la, lb, nk, wm, wn, lane, dma_a1, dma_b1);
+    else split_kloop_n<SP, N - 1>(nmb, acc, la, lb, nk, wm, wn, lane, dma_a1, dma_b1);
+  }
+}
+
+// Wait until at most n of this wave's DMA instructions are outstanding
+// (n in [0, N]; waiting for fewer is always safe).
+template <int N>
+__device__ __forceinline__ void wait_vm_le(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) { wait_vmcnt<N>(); return; }
+    wait_vm_le<N - 1>(n);
+  }
+}
+
+// One tile of the split-ring kernel (bf16 weights, A rows read in place).
+template <int BM, int BN, int WM, int WN, int BK, int SB, int EPI>
+__device__ __forceinline__ void split_tile(const GemmArgs& p, const Tile& t,
+                                           uint4 (*la)[Split<BM, BN, WM, WN, BK, SB>::R::A_U4],
+                                           uint4 (*lb)[Split<BM, BN, WM, WN, BK, SB>::R::B_U4],
+                                           uint32_t addr_a, uint32_t addr_b, int wave, int lane) {
+  constexpr bool GATEUP = EPI == kEpiSwiglu;
+  using SP = Split<BM, BN, WM, WN, BK, SB>;
+  using R = typename SP::R;
+  constexpr int MB = R::MB, NB = R::NB, PWA = R::PWA, PWB = R::PWB;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lra = lane / R::CHA, lca = lane % R::CHA;
+  const int lrb = lane / R::CHB, lcb = lane % R::CHB;
+  const int nk = p.Kd / BK;
+  const size_t wmat = (size_t)p.Nout * p.Kd;
+  // DMA sources and LDS offsets within a slot; as in ring_tile, the lane that
+  // writes LDS chunk c of a row fetches global chunk c ^ swizzle(row)
+  uint32_t offa[PWA], ldsa[PWA], offb[PWB], ldsb[PWB];
+  const void* baseb[PWB];
+  const uint16_t* basea = p.A + t.row0 * p.Kd;
+#pragma unroll
+  for (int j = 0; j < PWA; ++j) {
+    const int q = wave * PWA + j;
+    const int trow = q * R::RPIA + lra;
+    const int row = min(trow, t.rows - 1);
+    offa[j] = ((uint32_t)row * p.Kd + (uint32_t)(lca ^ swz<BK>(trow)) * 8) * 2u;
+    ldsa[j] = q * 1024;
+  }
+#pragma unroll
+  for (int jb = 0; jb < PWB; ++jb) {
+    const int q = wave * PWB + jb;
+    const int g0 = q * R::RPIB, trow = g0 + lrb;
+    bool up;
+    const int wrow = min(weight_row<BN, GATEUP>(t.nt, g0, up) + lrb, p.Nout - 1);
+    baseb[jb] = static_cast<const char*>(up ? p.B1 : p.B0) + (size_t)t.e * wmat * 2;
+    offb[jb] = ((uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz<BK>(trow)) * 8) * 2u;
+    ldsb[jb] = q * 1024;
+  }
+  auto dma_a = [&](int s, int kt) {
+    const uint32_t l0 = addr_a + (uint32_t)s * SP::A_BYTES;
+#pragma unroll
+    for (int j = 0; j < PWA; ++j)
+      lds_dma16(__builtin_amdgcn_readfirstlane(l0 + ldsa[j]), basea,
+                offa[j] + (uint32_t)kt * (BK * 2));
+  };
+  auto dma_b = [&](int s, int kt) {
+    const uint32_t l0 = addr_b + (uint32_t)s * SP::B_BYTES;
+#pragma unroll
+    for (int jb = 0; jb < PWB; ++jb)
+      lds_dma16(__builtin_amdgcn_readfirstlane(l0 + ldsb[jb]), baseb[jb],
+                offb[jb] + (uint32_t)kt * (BK * 2));
+  };
+
+  // single instructions: A instruction j, weight instruction jb (the callers
+  // pass constants once unrolled; the loops keep the arrays in registers)
+  auto dma_a1 = [&](int s, int kt, int j) {
+    const uint32_t l0 = addr_a + (uint32_t)s * SP::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < PWA; ++i)
+      if (i == j)
+        lds_dma16(__builtin_amdgcn_readfirstlane(l0 + ldsa[i]), basea,
+                  offa[i] + (uint32_t)kt * (BK * 2));
+  };
+  auto dma_b1 = [&](int s, int kt, int jb) {
+    const uint32_t l0 = addr_b + (uint32_t)s * SP::B_BYTES;
+#pragma unroll
+    for (int i = 0; i < PWB; ++i)
+      if (i == jb)
+        lds_dma16(__builtin_amdgcn_readfirstlane(l0 + ldsb[i]), baseb[i],
+                  offb[i] + (uint32_t)kt * (BK * 2));
+  };
+
+  f32x16_t acc[MB][NB];
+  zero(acc);
+  // every wave is past its last LDS read of the previous tile
+  wait_lgkmcnt0();
+  barrier();
+  // Prologue in the loop's issue order, as if steps -SB .. -1 had run:
+  // weight rows of stages 0 .. SB-3, A(0), B(SB-2), A(1), and the first
+  // weight instruction of B(SB-1) (step 0's k-steps issue the others).
+  for (int j = 0; j + 2 < SB; ++j)
+    if (j < nk) dma_b(j, j);
+  dma_a(0, 0);
+  if (SB - 2 < nk) dma_b(SB - 2, SB - 2);
+  if (1 < nk) dma_a(1, 1);
+  if (SB - 1 < nk) dma_b1(SB - 1, SB - 1, 0);
+  // stage 0 has landed: only B(SB-2), A(1) and B(SB-1)'s first instruction
+  // may be outstanding
+  wait_vm_le<PWB + PWA + 1>((SB - 2 < nk ? PWB : 0) + (1 < nk ? PWA : 0) +
+                            (SB - 1 < nk ? 1 : 0));
+  barrier();
+  // 32-row blocks of this wave that hold at least one row of the tile
+  const int nmb = min(MB, max(0, (t.rows - wm * R::TM + 31) / 32));
+  split_kloop_n<SP, MB>(nmb, acc, la, lb, nk, wm, wn, lane, dma_a1, dma_b1);
+  store_tile<MB, NB, R::TM, R::TN, BN, EPI>(p, t, acc, wm, wn, lane);
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int SB, int EPI, int PER>
+__global__ void __launch_bounds__(64 * WM * WN)
+grouped_gemm_split(GemmArgs p) {
+  using R = typename Split<BM, BN, WM, WN, BK, SB>::R;
+  __shared__ uint4 la[2][R::A_U4];
+  __shared__ uint4 lb[SB][R::B_U4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t addr_a = (uint32_t)(uintptr_t)(lds_void_t*)&la[0][0];
+  const uint32_t addr_b = (uint32_t)(uintptr_t)(lds_void_t*)&lb[0][0];
+  int ms[PER];
+  const int mt_total = build_work_list_regs<BM, PER>(p, ms, lane, gridDim.x);
+  const int total = p.n_tiles * mt_total;
+  const int xcd = blockIdx.x & 7, P8 = gridDim.x >> 3, j0 = blockIdx.x >> 3;
+  const int begin = (int)((int64_t)total * xcd / 8);
+  const int end = (int)((int64_t)total * (xcd + 1) / 8);
+  for (int l = begin + j0; l < end; l += P8)
+    split_tile<BM, BN, WM, WN, BK, SB, EPI>(p, decode_tile_regs<BM, PER>(p, ms, mt_total, lane, l),
+                                            la, lb, addr_a, addr_b, wave, lane);
+}
+
 // ------------------------------------------------------------ fused FFN
 //
 // The whole expert FFN in one persistent launch ("MoE 推理完整机制" (zoe.im),
@@ -992,6 +1385,17 @@ hipError_t launch_ring(const Dims& d, const GemmArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int BK, int SB, int EPI>
+hipError_t launch_split(const Dims& d, const GemmArgs& a0, hipStream_t s) {
+  const GemmArgs a = with_tiles<BN, EPI == kEpiSwiglu>(a0);
+  const dim3 grid((unsigned)grid_size<BM>(d, a.n_tiles, 1)), block(64 * WM * WN);
+  if (a.E <= 64)
+    hipLaunchKernelGGL((grouped_gemm_split<BM, BN, WM, WN, BK, SB, EPI, 1>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_split<BM, BN, WM, WN, BK, SB, EPI, 4>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, bool FP8>
 hipError_t launch_regs(const Dims& d, const GemmArgs& a0, int occupancy, hipStream_t s) {
   const GemmArgs a = with_tiles<BN, EPI == kEpiSwiglu>(a0);
@@ -1009,9 +1413,10 @@ hipError_t launch_regs(const Dims& d, const GemmArgs& a0, int occupancy, hipStre
 //            128-deep when k >= 512), else register-staged
 //   <= 192 : 128 x 256 tiles, 8 waves (64 x 64 each), 64-deep stages, 3-stage ring
 //            (FP8: 2 stages of 128-deep)
-//   else   : 256 x 256 tiles, 8 waves, 64-deep stages, 2-stage ring (3 with FP8
-//            weights): one barrier per 64 k (32-deep stages, twice the
-//            barriers, were 5-12% slower)
+//   else   : 256 x 256 tiles, 8 waves, 64-deep stages: the split ring with bf16
+//            weights and E <= 256 (its work list lives in 4 registers per
+//            lane), else a 2-stage ring (3 with FP8 weights); one barrier per
+//            64 k (32-deep stages, twice the barriers, were 5-12% slower)
 enum class Shape { Small, Mid, Large };
 inline Shape pick(const Dims& d) {
   const double avg = (double)d.R / d.E;
@@ -1044,7 +1449,11 @@ hipError_t launch_gemm(const Dims& d, const GemmArgs& a, hipStream_t s, Shape sh
         if (a.Kd % 128 == 0) return launch_ring<128, 256, 2, 4, 128, 2, EPI, FP8>(d, a, s);
       }
       return launch_ring<128, 256, 2, 4, 64, FP8 ? 4 : 3, EPI, FP8>(d, a, s);
-    default: return launch_ring<256, 256, 2, 4, 64, FP8 ? 3 : 2, EPI, FP8>(d, a, s);
+    default:
+      if constexpr (!FP8) {
+        if (a.E <= 256) return launch_split<256, 256, 2, 4, 64, 3, EPI>(d, a, s);
+      }
+      return launch_ring<256, 256, 2, 4, 64, FP8 ? 3 : 2, EPI, FP8>(d, a, s);
   }
 }
 

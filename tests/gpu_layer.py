@@ -38,6 +38,11 @@ SMALL = {
     "mid_tiles": C("mid_tiles", N=960, D=384, E=8, K=2, F=320, gating="sigmoid", seed=110),
     # K = 12: the combine and copy kernels take the slots of a token in groups of 8
     "wide_topk": C("wide_topk", N=80, D=128, E=32, K=12, F=128, gating="softmax", seed=111),
+    # 100 experts, 200 rows each on average under a Zipf bias (8 empty, most
+    # under 32 rows, the largest 5837 rows: 23 row tiles in bands): 256 x 256
+    # split-ring tiles with the work list in four registers per lane
+    "many_large_experts": C("many_large_experts", N=10000, D=128, E=100, K=2, F=128,
+                            gating="sigmoid", seed=112, zipf_s=1.2, zipf_alpha=0.7),
     "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
                 zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
     "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,

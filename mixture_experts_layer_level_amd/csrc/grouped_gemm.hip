@@ -558,6 +558,18 @@ __device__ __forceinline__ void wait_upto(int n) {
 template <int PW, int S>
 __device__ __forceinline__ void wait_stages(int n) { wait_upto<PW, S - 1>(n); }
 
+// Wait until at most n of this wave's DMA instructions are outstanding
+// (n in [0, N]; waiting for fewer is always safe).
+template <int N>
+__device__ __forceinline__ void wait_vm_le(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) { wait_vmcnt<N>(); return; }
+    wait_vm_le<N - 1>(n);
+  }
+}
+
 // FP8 scale area of a stage: wave w fetches LS 16-byte units, unit
 // (i * KB + kbl) * 2 + half holding rows 16*half .. 16*half+15 of its i-th
 // 32-row group for k-block kbl.  In gate/up tiles the first half of the waves
@@ -660,6 +672,99 @@ __device__ __forceinline__ void ring_kloop(f32x16_t (&acc)[R::MB][R::NB],
   }
 }
 
+// MFMAs [F, F + C) of one k-step, in mfma_step's (mb, nb) order.
+template <int F, int C, int MB, int NB>
+__device__ __forceinline__ void mfma_part(f32x16_t (&acc)[MB][NB], const bf16x8_t (&af)[MB],
+                                          const bf16x8_t (&bfr)[NB], int nmb) {
+#pragma unroll
+  for (int i = F; i < F + C; ++i) {
+    const int mb = i / NB, nb = i % NB;
+    if (mb < nmb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[mb][nb], 0, 0, 0);
+  }
+}
+
+// MFMA group J of a k-step (C MFMAs), then DMA instruction J of stage kt
+// into slot s (if `an`), in that order.
+template <int J, int C, int MB, int NB, class Dma1>
+__device__ __forceinline__ void mfma_dma_a(f32x16_t (&acc)[MB][NB], const bf16x8_t (&af)[MB],
+                                           const bf16x8_t (&bfr)[NB], int nmb, bool an, int s,
+                                           int kt, const Dma1& dma1) {
+  mfma_part<J * C, C, MB, NB>(acc, af, bfr, nmb);
+  __builtin_amdgcn_sched_barrier(0);
+  if (an) dma1(s, kt, J);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ring_kloop for rings of S >= 3 slots with the DMA spread over the stage
+// instead of one burst after the barrier (a wave stalled behind a burst of
+// DMA instructions issues no MFMAs).  The DMA of stage kt + S goes out in
+// pieces: its first NPOST instructions between the quarters of the last
+// k-step's MFMAs of stage kt, the others after the k-steps of stage kt + 1,
+// Q per k-step.  Every instruction of stage kt + S is thus issued before the
+// barrier that ends stage kt + 1, and when stage kt ends the DMA issued after
+// stage kt + 1's is exactly that of stages kt + 2 .. kt + S - 1: the wait is
+// ring_kloop's.
+template <class R, int NMB, bool FP8, bool GATEUP, class Dma1>
+__device__ __forceinline__ void ring_kloop_spread(f32x16_t (&acc)[R::MB][R::NB],
+                                                  uint4 (*lds)[R::STAGE_U4], int nk, int wm,
+                                                  int wn, int lane, const Dma1& dma1) {
+  constexpr int MB = R::MB, NB = R::NB, PW = R::PW, KS = R::KS, S = R::S;
+  constexpr int NPOST = 4, C = MB * NB / NPOST, Q = (PW - NPOST + KS - 2) / (KS - 1);
+  static_assert(S >= 3 && C * NPOST == MB * NB && PW > NPOST, "DMA spread");
+  bf16x8_t fa[2][MB], fb[2][NB];
+  float sc[NB];
+  uint4 qb[NB];
+  read_frags_ring<R, FP8, GATEUP>(fa[0], fb[0], sc, qb, lds[0], 0, wm, wn, lane, NMB);
+  int sp = S - 1;   // slot of stage kt + S - 1, whose DMA this step's k-steps finish
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s0 = kt % S;
+    const uint4* cur = lds[s0];
+    const bool bdef = kt + S - 1 < nk;
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      read_frags_ring<R, FP8, GATEUP>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sc, qb, cur, ks + 1,
+                                      wm, wn, lane, NMB);
+      mfma_step(acc, fa[ks & 1], fb[ks & 1], NMB);
+      if (bdef && NPOST + ks * Q < PW) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+          if (NPOST + ks * Q + q < PW) dma1(sp, kt + S - 1, NPOST + ks * Q + q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // this wave has read all of stage kt and its part of stage kt+1 landed
+    wait_lgkmcnt0();
+    if (kt + 1 < nk) wait_stages<PW, S>(min(S - 2, nk - 2 - kt));
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const bool an = kt + S < nk;
+    const bf16x8_t(&fl)[MB] = fa[(KS - 1) & 1];
+    const bf16x8_t(&gl)[NB] = fb[(KS - 1) & 1];
+    mfma_dma_a<0, C>(acc, fl, gl, NMB, an, s0, kt + S, dma1);
+    mfma_dma_a<1, C>(acc, fl, gl, NMB, an, s0, kt + S, dma1);
+    mfma_dma_a<2, C>(acc, fl, gl, NMB, an, s0, kt + S, dma1);
+    mfma_dma_a<3, C>(acc, fl, gl, NMB, an, s0, kt + S, dma1);
+    sp = s0;
+    if (kt + 1 < nk)
+      read_frags_ring<R, FP8, GATEUP>(fa[KS & 1], fb[KS & 1], sc, qb, lds[(kt + 1) % S], 0, wm,
+                                      wn, lane, NMB);
+  }
+}
+
+template <class R, int N, bool FP8, bool GATEUP, class Dma1>
+__device__ __forceinline__ void ring_kloop_spread_n(int nmb, f32x16_t (&acc)[R::MB][R::NB],
+                                                    uint4 (*lds)[R::STAGE_U4], int nk, int wm,
+                                                    int wn, int lane, const Dma1& dma1) {
+  if constexpr (N == 0) {
+    ring_kloop_spread<R, 0, FP8, GATEUP>(acc, lds, nk, wm, wn, lane, dma1);
+  } else {
+    if (nmb == N) ring_kloop_spread<R, N, FP8, GATEUP>(acc, lds, nk, wm, wn, lane, dma1);
+    else ring_kloop_spread_n<R, N - 1, FP8, GATEUP>(nmb, acc, lds, nk, wm, wn, lane, dma1);
+  }
+}
+
 // ring_kloop with NMB = nmb, chosen outside the loop so that the loop body
 // holds no branch on it.
 template <class R, int N, bool FP8, bool GATEUP, class Dma>
@@ -677,7 +782,8 @@ __device__ __forceinline__ void ring_kloop_n(int nmb, f32x16_t (&acc)[R::MB][R::
 // One tile of the ring kernel: its operands through the LDS ring, the k loop
 // and the epilogue.  Every wave of the workgroup takes part; on return each
 // wave has issued its stores of the tile.
-template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8, bool UNIFORM = false>
+template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8, bool UNIFORM = false,
+          bool SPREAD = false>
 __device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
                                           uint4 (*lds)[Ring<BM, BN, WM, WN, BK, S, FP8>::STAGE_U4],
                                           uint32_t lds_addr, int wave, int lane) {
@@ -761,18 +867,50 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
   // every wave is past its last LDS read of the previous tile
   wait_lgkmcnt0();
   barrier();
+  // 32-row blocks of this wave that hold at least one row of the tile
+  const int nmb = min(MB, max(0, (t.rows - wm * R::TM + 31) / 32));
+  if constexpr (SPREAD) {
+    // instruction j of the DMA set alone (the callers pass constants once
+    // unrolled)
+    auto dma1 = [&](int s, int kt, int j) {
+      const uint32_t l0 = lds_addr + (uint32_t)s * (R::STAGE_U4 * 16);
+#pragma unroll
+      for (int i = 0; i < PW; ++i) {
+        if (i != j) continue;
+        const uint32_t adv = i < PWA ? BK * 2 : i < PWA + PWB ? R::BRB : R::KB * 32;
+        const uint32_t la = __builtin_amdgcn_readfirstlane(l0 + ldso[i]);
+        if (FP8 && i == PW - 1) {
+          if (lane < R::LS) lds_dma16<UNIFORM>(la, base[i], off[i] + (uint32_t)kt * adv);
+        } else {
+          lds_dma16<UNIFORM>(la, base[i], off[i] + (uint32_t)kt * adv);
+        }
+      }
+    };
+    // prologue in the loop's issue order: stages 0 .. S-2 whole, stage S-1's
+    // first four instructions (step 0's k-steps issue the rest); then stage
+    // 0 has landed once at most the later ones are outstanding
+#pragma unroll
+    for (int s = 0; s + 1 < S; ++s)
+      if (s < nk) dma(s, s);
+    if (S - 1 < nk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma1(S - 1, S - 1, j);
+    wait_vm_le<(S - 2) * PW + 4>(min(S - 2, nk - 1) * PW + (S - 1 < nk ? 4 : 0));
+    barrier();
+    ring_kloop_spread_n<R, MB, FP8, GATEUP>(nmb, acc, lds, nk, wm, wn, lane, dma1);
+    store_tile<MB, NB, R::TM, R::TN, BN, EPI>(p, t, acc, wm, wn, lane);
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < S; ++s)
     if (s < nk) dma(s, s);
   wait_stages<PW, S>(min(S - 1, nk - 1));
   barrier();
-  // 32-row blocks of this wave that hold at least one row of the tile
-  const int nmb = min(MB, max(0, (t.rows - wm * R::TM + 31) / 32));
   ring_kloop_n<R, MB, FP8, GATEUP>(nmb, acc, lds, nk, wm, wn, lane, dma);
   store_tile<MB, NB, R::TM, R::TN, BN, EPI>(p, t, acc, wm, wn, lane);
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8>
+template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8, bool SPREAD = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_ring(GemmArgs p) {
   using R = Ring<BM, BN, WM, WN, BK, S, FP8>;
@@ -788,8 +926,8 @@ grouped_gemm_ring(GemmArgs p) {
   const int begin = (int)((int64_t)total * xcd / 8);
   const int end = (int)((int64_t)total * (xcd + 1) / 8);
   for (int l = begin + j0; l < end; l += P8)
-    ring_tile<BM, BN, WM, WN, BK, S, EPI, FP8>(p, decode_tile<BM>(p, mstart, l), lds, lds_addr,
-                                               wave, lane);
+    ring_tile<BM, BN, WM, WN, BK, S, EPI, FP8, false, SPREAD>(p, decode_tile<BM>(p, mstart, l),
+                                                              lds, lds_addr, wave, lane);
 }
 
 // ------------------------------------------------------------ split ring
@@ -831,28 +969,6 @@ __device__ __forceinline__ void read_frags_split(bf16x8_t (&af)[R::MB], bf16x8_t
     const int r = wn * R::TN + nb * 32 + (lane & 31);
     bfr[nb] = __builtin_bit_cast(bf16x8_t, sb[r * R::CHB + (kc ^ swz<BK>(r))]);
   }
-}
-
-// MFMAs [F, F + C) of one k-step, in mfma_step's (mb, nb) order.
-template <int F, int C, int MB, int NB>
-__device__ __forceinline__ void mfma_part(f32x16_t (&acc)[MB][NB], const bf16x8_t (&af)[MB],
-                                          const bf16x8_t (&bfr)[NB], int nmb) {
-#pragma unroll
-  for (int i = F; i < F + C; ++i) {
-    const int mb = i / NB, nb = i % NB;
-    if (mb < nmb)
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[mb][nb], 0, 0, 0);
-  }
-}
-
-template <int J, int C, int MB, int NB, class DmaA1>
-__device__ __forceinline__ void mfma_dma_a(f32x16_t (&acc)[MB][NB], const bf16x8_t (&af)[MB],
-                                           const bf16x8_t (&bfr)[NB], int nmb, bool an, int sa,
-                                           int kt, const DmaA1& dma_a1) {
-  mfma_part<J * C, C, MB, NB>(acc, af, bfr, nmb);
-  __builtin_amdgcn_sched_barrier(0);
-  if (an) dma_a1(sa, kt, J);
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // The k loop of a split-ring tile.  Stage kt's A rows are in A slot kt % 2,
@@ -937,17 +1053,6 @@ __device__ __forceinline__ void split_kloop_n(int nmb, f32x16_t (&acc)[SP::R::MB
   }
 }
 
-// Wait until at most n of this wave's DMA instructions are outstanding
-// (n in [0, N]; waiting for fewer is always safe).
-template <int N>
-__device__ __forceinline__ void wait_vm_le(int n) {
-  if constexpr (N == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (n >= N) { wait_vmcnt<N>(); return; }
-    wait_vm_le<N - 1>(n);
-  }
-}
 
 // One tile of the split-ring kernel (bf16 weights, A rows read in place).
 template <int BM, int BN, int WM, int WN, int BK, int SB, int EPI>
@@ -1377,10 +1482,10 @@ GemmArgs with_tiles(GemmArgs a) {  // (GATEUP: interleaved gate/up tile)
   return a;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8>
+template <int BM, int BN, int WM, int WN, int BK, int S, int EPI, bool FP8, bool SPREAD = false>
 hipError_t launch_ring(const Dims& d, const GemmArgs& a0, hipStream_t s) {
   const GemmArgs a = with_tiles<BN, EPI == kEpiSwiglu>(a0);
-  hipLaunchKernelGGL((grouped_gemm_ring<BM, BN, WM, WN, BK, S, EPI, FP8>),
+  hipLaunchKernelGGL((grouped_gemm_ring<BM, BN, WM, WN, BK, S, EPI, FP8, SPREAD>),
                      dim3((unsigned)grid_size<BM>(d, a.n_tiles, 1)), dim3(64 * WM * WN), 0, s, a);
   return hipGetLastError();
 }
@@ -1415,8 +1520,9 @@ hipError_t launch_regs(const Dims& d, const GemmArgs& a0, int occupancy, hipStre
 //            (FP8: 2 stages of 128-deep)
 //   else   : 256 x 256 tiles, 8 waves, 64-deep stages: the split ring with bf16
 //            weights and E <= 256 (its work list lives in 4 registers per
-//            lane), else a 2-stage ring (3 with FP8 weights); one barrier per
-//            64 k (32-deep stages, twice the barriers, were 5-12% slower)
+//            lane), else a 2-stage ring, or with FP8 weights a 3-stage ring
+//            with its DMA spread over the stage; one barrier per 64 k
+//            (32-deep stages, twice the barriers, were 5-12% slower)
 enum class Shape { Small, Mid, Large };
 inline Shape pick(const Dims& d) {
   const double avg = (double)d.R / d.E;
@@ -1453,7 +1559,8 @@ hipError_t launch_gemm(const Dims& d, const GemmArgs& a, hipStream_t s, Shape sh
       if constexpr (!FP8) {
         if (a.E <= 256) return launch_split<256, 256, 2, 4, 64, 3, EPI>(d, a, s);
       }
-      return launch_ring<256, 256, 2, 4, 64, FP8 ? 3 : 2, EPI, FP8>(d, a, s);
+      if constexpr (FP8) return launch_ring<256, 256, 2, 4, 64, 3, EPI, true, true>(d, a, s);
+      return launch_ring<256, 256, 2, 4, 64, 2, EPI, false>(d, a, s);
   }
 }
 

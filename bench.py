@@ -237,8 +237,8 @@ def main():
         roof = {"bound": "hbm", "achieved": gu_bytes / (gateup_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = (measured_traffic(args.config + ("_fp8" if fp8 else ""))
-                       if not capv else None)
+    roof["traffic"] = measured_traffic(args.config + ("_padded" if capv else "") +
+                                       ("_fp8" if fp8 else ""))
     roof["kernel"] = ("grouped up GEMM + bias + GELU" if gelu
                       else "grouped gate/up GEMM + SwiGLU")
     if args.fused:

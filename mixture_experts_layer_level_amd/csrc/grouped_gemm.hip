@@ -1054,8 +1054,9 @@ __device__ __forceinline__ void split_kloop_n(int nmb, f32x16_t (&acc)[SP::R::MB
 }
 
 
-// One tile of the split-ring kernel (bf16 weights, A rows read in place).
-template <int BM, int BN, int WM, int WN, int BK, int SB, int EPI>
+// One tile of the split-ring kernel (bf16 weights).  A rows are read in
+// place, or with p.gather set, row r of the tile is row gather[row0 + r] of A.
+template <int BM, int BN, int WM, int WN, int BK, int SB, int EPI, bool UNIFORM = false>
 __device__ __forceinline__ void split_tile(const GemmArgs& p, const Tile& t,
                                            uint4 (*la)[Split<BM, BN, WM, WN, BK, SB>::R::A_U4],
                                            uint4 (*lb)[Split<BM, BN, WM, WN, BK, SB>::R::B_U4],
@@ -1073,13 +1074,14 @@ __device__ __forceinline__ void split_tile(const GemmArgs& p, const Tile& t,
   // writes LDS chunk c of a row fetches global chunk c ^ swizzle(row)
   uint32_t offa[PWA], ldsa[PWA], offb[PWB], ldsb[PWB];
   const void* baseb[PWB];
-  const uint16_t* basea = p.A + t.row0 * p.Kd;
+  const uint16_t* basea = p.gather ? p.A : p.A + t.row0 * p.Kd;
 #pragma unroll
   for (int j = 0; j < PWA; ++j) {
     const int q = wave * PWA + j;
     const int trow = q * R::RPIA + lra;
     const int row = min(trow, t.rows - 1);
-    offa[j] = ((uint32_t)row * p.Kd + (uint32_t)(lca ^ swz<BK>(trow)) * 8) * 2u;
+    const uint32_t src = p.gather ? (uint32_t)p.gather[t.row0 + row] : (uint32_t)row;
+    offa[j] = (src * p.Kd + (uint32_t)(lca ^ swz<BK>(trow)) * 8) * 2u;
     ldsa[j] = q * 1024;
   }
 #pragma unroll
@@ -1096,14 +1098,14 @@ __device__ __forceinline__ void split_tile(const GemmArgs& p, const Tile& t,
     const uint32_t l0 = addr_a + (uint32_t)s * SP::A_BYTES;
 #pragma unroll
     for (int j = 0; j < PWA; ++j)
-      lds_dma16(__builtin_amdgcn_readfirstlane(l0 + ldsa[j]), basea,
+      lds_dma16<UNIFORM>(__builtin_amdgcn_readfirstlane(l0 + ldsa[j]), basea,
                 offa[j] + (uint32_t)kt * (BK * 2));
   };
   auto dma_b = [&](int s, int kt) {
     const uint32_t l0 = addr_b + (uint32_t)s * SP::B_BYTES;
 #pragma unroll
     for (int jb = 0; jb < PWB; ++jb)
-      lds_dma16(__builtin_amdgcn_readfirstlane(l0 + ldsb[jb]), baseb[jb],
+      lds_dma16<UNIFORM>(__builtin_amdgcn_readfirstlane(l0 + ldsb[jb]), baseb[jb],
                 offb[jb] + (uint32_t)kt * (BK * 2));
   };
 
@@ -1114,7 +1116,7 @@ __device__ __forceinline__ void split_tile(const GemmArgs& p, const Tile& t,
 #pragma unroll
     for (int i = 0; i < PWA; ++i)
       if (i == j)
-        lds_dma16(__builtin_amdgcn_readfirstlane(l0 + ldsa[i]), basea,
+        lds_dma16<UNIFORM>(__builtin_amdgcn_readfirstlane(l0 + ldsa[i]), basea,
                   offa[i] + (uint32_t)kt * (BK * 2));
   };
   auto dma_b1 = [&](int s, int kt, int jb) {
@@ -1122,7 +1124,7 @@ __device__ __forceinline__ void split_tile(const GemmArgs& p, const Tile& t,
 #pragma unroll
     for (int i = 0; i < PWB; ++i)
       if (i == jb)
-        lds_dma16(__builtin_amdgcn_readfirstlane(l0 + ldsb[i]), baseb[i],
+        lds_dma16<UNIFORM>(__builtin_amdgcn_readfirstlane(l0 + ldsb[i]), baseb[i],
                   offb[i] + (uint32_t)kt * (BK * 2));
   };
 
@@ -1295,6 +1297,94 @@ grouped_ffn_fused(FusedArgs f) {
       }
       __syncthreads();
       ring_tile<BM, BN, WM, WN, BK, S, kEpiStore, FP8, true>(f.dn, t, lds, lds_addr, wave, lane);
+    }
+  }
+}
+
+// The fused FFN on the split rings (256 x 256 tiles, bf16, E <= 64 * PER):
+// the same claim loop, dependency counts and ordering as grouped_ffn_fused,
+// with split_tile as the tile body and the work list in registers.  The
+// rings fill LDS, so the claimed tile goes from wave 0 to the other waves
+// through the first word of A slot 0.  That word is free whenever it is
+// used: after a tile's last barrier every wave is done with LDS (each waited
+// for its own reads before that barrier), and the next tile's DMA goes out
+// only after the barriers that follow the read of the word.
+template <int BM, int BN, int WM, int WN, int BK, int SB, int PER>
+__global__ void __launch_bounds__(64 * WM * WN)
+grouped_ffn_fused_split(FusedArgs f) {
+  using R = typename Split<BM, BN, WM, WN, BK, SB>::R;
+  __shared__ uint4 la[2][R::A_U4];
+  __shared__ uint4 lb[SB][R::B_U4];
+  volatile int32_t* ticket = reinterpret_cast<volatile int32_t*>(&la[0][0]);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t addr_a = (uint32_t)(uintptr_t)(lds_void_t*)&la[0][0];
+  const uint32_t addr_b = (uint32_t)(uintptr_t)(lds_void_t*)&lb[0][0];
+  int ms[PER];
+  const int M = build_work_list_regs<BM, PER>(f.gu, ms, lane, 0);   // one row split for both
+  // (the loop's control flow stays wave-uniform; see grouped_ffn_fused)
+  const int T1 = f.gu.n_tiles * M, T = T1 + f.dn.n_tiles * M;
+  const int need = f.gu.n_tiles;               // gate/up tiles per row tile
+  const int one = lane == 0 ? 1 : 0;
+  const int xcd = blockIdx.x & 7;
+  int list = 0, step = 0;                      // wave 0: list and XCD part being claimed from
+  for (;;) {
+    if (wave == 0) {
+      int got = T;
+      while (list < 2) {
+        const int n = list ? T - T1 : T1, x = (xcd + step) & 7;
+        const int b = (int)((int64_t)n * x / 8), e = (int)((int64_t)n * (x + 1) / 8);
+        const int c = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
+            f.claim + 8 * list + x, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (b + c < e) {
+          got = (list ? T1 : 0) + b + c;
+          break;
+        }
+        if (++step == 8) {
+          step = 0;
+          ++list;
+        }
+      }
+      *ticket = got;
+    }
+    __syncthreads();
+    const int l = __builtin_amdgcn_readfirstlane(*ticket);
+    __syncthreads();
+    if (l >= T) break;
+    if (l < T1) {
+      const Tile t = decode_tile_regs<BM, PER>(f.gu, ms, M, lane, l);
+      split_tile<BM, BN, WM, WN, BK, SB, kEpiSwiglu, true>(f.gu, t, la, lb, addr_a, addr_b,
+                                                           wave, lane);
+      // every wave's h stores have reached this XCD's L2; wave 0 writes the
+      // L2 back (agent-scope release) and counts the tile
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (wave == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(f.done + t.mtg, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      const Tile t = decode_tile_regs<BM, PER>(f.dn, ms, M, lane, l - T1);
+      // wave 0 waits for the row tile's count, then invalidates this CU's L1
+      // and this XCD's L2 (agent-scope acquire) before the other waves load
+      if (wave == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+          const int c = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(f.done + t.mtg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          if (c >= need) break;
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            __hip_atomic_fetch_or(f.err, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        wait_vmcnt<0>();
+      }
+      __syncthreads();
+      split_tile<BM, BN, WM, WN, BK, SB, kEpiStore, true>(f.dn, t, la, lb, addr_a, addr_b, wave,
+                                                          lane);
     }
   }
 }
@@ -1673,7 +1763,7 @@ hipError_t launch_dense_gelu(int64_t N, int Kd, int Nout, const uint16_t* A, con
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int BK, int S>
+template <int BM, int BN, int WM, int WN, int BK, int S, bool SPLIT = false>
 hipError_t launch_fused(const Dims& d, const FusedArgs& f0, hipStream_t s) {
   FusedArgs f = f0;
   f.gu = with_tiles<BN, true>(f.gu);
@@ -1686,8 +1776,17 @@ hipError_t launch_fused(const Dims& d, const FusedArgs& f0, hipStream_t s) {
   int64_t g = device_cu_count();
   const int64_t work = mt_max * (f.gu.n_tiles + f.dn.n_tiles);
   if (g > work) g = work;
-  hipLaunchKernelGGL((grouped_ffn_fused<BM, BN, WM, WN, BK, S, false>), dim3((unsigned)g),
-                     dim3(64 * WM * WN), 0, s, f);
+  if constexpr (SPLIT) {
+    if (d.E <= 64)
+      hipLaunchKernelGGL((grouped_ffn_fused_split<BM, BN, WM, WN, BK, S, 1>), dim3((unsigned)g),
+                         dim3(64 * WM * WN), 0, s, f);
+    else
+      hipLaunchKernelGGL((grouped_ffn_fused_split<BM, BN, WM, WN, BK, S, 4>), dim3((unsigned)g),
+                         dim3(64 * WM * WN), 0, s, f);
+  } else {
+    hipLaunchKernelGGL((grouped_ffn_fused<BM, BN, WM, WN, BK, S, false>), dim3((unsigned)g),
+                       dim3(64 * WM * WN), 0, s, f);
+  }
   return hipGetLastError();
 }
 
@@ -1719,7 +1818,10 @@ hipError_t launch_fused_ffn(const Dims& d, const uint16_t* x, const int32_t* row
   switch (pick(d)) {
     case Shape::Small: return launch_fused<32, 256, 1, 4, 64, 4>(d, f, s);
     case Shape::Mid: return launch_fused<128, 256, 2, 4, 64, 3>(d, f, s);
-    default: return launch_fused<256, 256, 2, 4, 64, 2>(d, f, s);
+    default:
+      // the split rings (three weight slots) when the work list fits in registers
+      if (d.E <= 256) return launch_fused<256, 256, 2, 4, 64, 3, true>(d, f, s);
+      return launch_fused<256, 256, 2, 4, 64, 2>(d, f, s);
   }
 }
 

@@ -43,6 +43,10 @@ SMALL = {
     # split-ring tiles with the work list in four registers per lane
     "many_large_experts": C("many_large_experts", N=10000, D=128, E=100, K=2, F=128,
                             gating="sigmoid", seed=112, zipf_s=1.2, zipf_alpha=0.7),
+    # 256 x 256 tiles with one 64-deep stage in the gate/up GEMM (D = 64) and
+    # two in the down GEMM (F = 128): the rings' shortest prologues
+    "short_k_large_tiles": C("short_k_large_tiles", N=1300, D=64, E=2, K=1, F=128,
+                             gating="softmax", seed=113),
     "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
                 zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
     "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,

@@ -957,15 +957,16 @@ grouped_gemm_ring(GemmArgs p) {
 // ------------------------------------------------------------ split ring
 //
 // In the ring above a stage's A rows and weight rows share one LDS slot; at
-// 256 x 256 tiles two slots fill LDS, so while a CU computes one stage it has
-// only the next stage's bytes in flight.  Where the weights stream from HBM
-// (one row tile per expert, as at the DeepSeek-V3 shape) that is too little
-// to cover HBM latency.  The split ring keeps two rings: SA = 2 slots of A
-// rows, one stage ahead (A rows are mostly L2 hits: every column panel of a
-// row tile reads them), and SB slots of weight rows, SB - 1 stages ahead.
-// The rings fill LDS, so the work list's row-tile prefix is kept in
-// registers (build_work_list_regs).  Same tiles, same MFMAs in the same k
-// order as the ring kernel: the results are bit-identical.
+// 256 x 256 tiles two slots fill LDS, so the DMA for stage kt+2 has to be
+// issued as soon as stage kt's slot frees, in one burst.  The split ring
+// keeps two rings: SA = 2 slots of A rows, one stage ahead (A rows are mostly
+// L2 hits: every column panel of a row tile reads them), and SB slots of
+// weight rows, SB - 1 stages ahead.  The weights' extra stage of slack is
+// what lets their DMA be spread over the next stage's k-steps (split_kloop);
+// the deeper ring alone gained little.  The rings fill LDS, so the work
+// list's row-tile prefix is kept in registers (build_work_list_regs).  Same
+// tiles, same MFMAs in the same k order as the ring kernel: the results are
+// bit-identical.
 template <int BM, int BN, int WM, int WN, int BK, int SB_>
 struct Split {
   using R = Ring<BM, BN, WM, WN, BK, 2, false>;   // tile geometry and DMA split

@@ -47,6 +47,11 @@ SMALL = {
     # two in the down GEMM (F = 128): the rings' shortest prologues
     "short_k_large_tiles": C("short_k_large_tiles", N=1300, D=64, E=2, K=1, F=128,
                              gating="softmax", seed=113),
+    # 300 experts of about 200 rows: 256 x 256 tiles with more experts than the
+    # split rings' register work list holds (the 2-slot ring, and the fused
+    # FFN on it)
+    "many_experts_ring": C("many_experts_ring", N=30000, D=128, E=300, K=2, F=192,
+                           gating="softmax", seed=114),
     "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
                 zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
     "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,

@@ -318,6 +318,23 @@ def main():
     print(f"[bench] {ms_step:.3f} ms/step, gate/up {gateup_ms:.3f} ms", file=sys.stderr,
           flush=True)
 
+    # Cold-cache steps, after the timed ones and outside them: before each,
+    # 512 MiB of scratch are written (twice the 256 MB memory-side cache), so
+    # no activation or weight of the previous step is still cached; each step
+    # is timed alone between events on the launch stream.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(5):
+        scratch.zero_()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        step()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    del scratch
+    line["cold_ms_per_step"] = sorted(cold)[len(cold) // 2]
+
     if args.cpu_tokens > 0:
         line["cpu_baseline"] = (cpu_baseline_gelu(cfg, inp, min(args.cpu_tokens, N)) if gelu else
                                 cpu_baseline(cfg, inp, min(args.cpu_tokens, N), capv, fp8))

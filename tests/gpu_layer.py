@@ -52,6 +52,10 @@ SMALL = {
     # FFN on it)
     "many_experts_ring": C("many_experts_ring", N=30000, D=128, E=300, K=2, F=192,
                            gating="softmax", seed=114),
+    # few router tiles over a long k: 8 waves share a 32 x 32 router tile's 17
+    # k blocks (one takes three), ragged token and expert tiles
+    "wide_router": C("wide_router", N=40, D=1088, E=48, K=4, F=128, gating="sigmoid",
+                     seed=115),
     "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
                 zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
     "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,

@@ -63,6 +63,10 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="the expert FFN as one persistent launch (moe_fused_ffn; rows gathered "
                          "from x, no permuted copy)")
+    ap.add_argument("--xperm", action="store_true",
+                    help="write the permuted copy of x and run gate/up on it; by default the "
+                         "bf16 SwiGLU layer's gate/up reads its rows of x through row_token "
+                         "(moe_expert_gateup_gathered) wherever the library takes the shape")
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
@@ -132,6 +136,22 @@ def main():
         qg, qu, qd = quant(wg), quant(wu), quant(wd)
         torch.cuda.synchronize()
 
+    # The bf16 SwiGLU layer's gate/up reads its rows of x through row_token
+    # wherever the library takes the shape; it refuses, before any launch, the
+    # shapes whose tiles have no gathered form.  One route + permute first, so
+    # that the trial call runs on real routing tables.
+    gather = not (args.xperm or gelu or args.fused or fp8 or capv)
+    if gather:
+        moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
+        moe.permute(p, x, ids, counts, offsets, row_token, slot_row, None, ws, stream=stream)
+        try:
+            moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=stream)
+        except moe.MoEError as err:
+            if err.status != 2:   # MOE_ERR_UNSUPPORTED: run the permuted copy instead
+                raise
+            gather = False
+        torch.cuda.synchronize()
+
     # ev: six events per step, recorded on the launch stream before the route
     # and after the route, permute, gate/up (or up, or fused FFN), down and
     # combine calls
@@ -174,9 +194,12 @@ def main():
         rec(ev, 0)
         moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
         rec(ev, 1)
-        moe.permute(p, x, ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=stream)
+        moe.permute(p, x, ids, counts, offsets, row_token, slot_row,
+                    None if gather else x_perm, ws, stream=stream)
         rec(ev, 2)
-        if fp8:
+        if gather:
+            moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=stream)
+        elif fp8:
             moe.expert_gateup_fp8(p, x_perm, offsets, qg, qu, h, stream=stream)
         else:
             moe.expert_gateup(p, x_perm, offsets, wg, wu, h, stream=stream)
@@ -238,9 +261,10 @@ def main():
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(args.config + ("_padded" if capv else "") +
-                                       ("_fp8" if fp8 else ""))
+                                       ("_fp8" if fp8 else "") + ("_xperm" if args.xperm else ""))
     roof["kernel"] = ("grouped up GEMM + bias + GELU" if gelu
-                      else "grouped gate/up GEMM + SwiGLU")
+                      else "grouped gate/up GEMM + SwiGLU" +
+                      (", rows gathered from x through row_token" if gather else ""))
     if args.fused:
         # the one fused launch: gate/up, SwiGLU and down of every expert
         f_flops = 6.0 * D * F * kept
@@ -263,7 +287,7 @@ def main():
     # (out_perm rows read, y written, slot_row and weights read)
     S_ = N * K
     perm_bytes = (S_ * 4 * 3 + (E + 1) * 4 +
-                  (0 if args.fused else N * D * 2 + R * D * 2))
+                  (0 if args.fused or gather else N * D * 2 + R * D * 2))
     comb_bytes = kept * D * 2 + N * D * 2 + S_ * 8
     stages = {
         "route_ms": route_ms, "permute_ms": permute_ms, "ffn_ms": gateup_ms + down_ms,
@@ -302,7 +326,9 @@ def main():
                                       if fp8 else "bf16"),
                    "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
                               else "SwiGLU"),
-                   "ffn_launch": "fused (one persistent launch)" if args.fused else "two grouped GEMMs"},
+                   "ffn_launch": ("fused (one persistent launch)" if args.fused else
+                                  "two grouped GEMMs, gate/up rows gathered from x" if gather
+                                  else "two grouped GEMMs")},
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "weight_stream_gbps": weight_bytes / (ms_step * 1e-3) / 1e9,

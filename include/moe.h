@@ -166,6 +166,22 @@ moe_status moe_expert_down(const moe_problem* p, const uint16_t* h,
                            const int32_t* expert_offsets, const uint16_t* w_down,
                            uint16_t* out_perm, void* stream);
 
+/* moe_expert_gateup on x[row_token] without the permuted copy: each tile
+ * reads its rows of x through row_token (the dispatch of zoe.im 范式 A Step 1
+ * folded into the GEMM's loads, as moe_fused_ffn does).  With it,
+ * moe_permute can be called with x_perm = NULL.  h is bit for bit what
+ * moe_expert_gateup writes from x_perm = x[row_token].
+ *   x [N, D] bf16; row_token [R] int32 and expert_offsets [E+1] int32 as
+ *   written by moe_permute (values of row_token not checked on the device);
+ *   w_gate, w_up [E, F, D] bf16; h [R, F] bf16 out.
+ * MOE_ERR_UNSUPPORTED for a padded problem (its padding rows have no token),
+ * for N * D * 2 >= 2^32 bytes of x, and where the tile shape has no gathered
+ * form: R / E <= 48 rows per expert with D < 1024.  Needs no workspace. */
+moe_status moe_expert_gateup_gathered(const moe_problem* p, const uint16_t* x,
+                                      const int32_t* row_token, const int32_t* expert_offsets,
+                                      const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h,
+                                      void* stream);
+
 /* Un-permutation and weighted combine (zoe.im 范式 A Step 3):
  *   y[n] = bf16( sum_{k=0..K-1, slot_row[n*K+k] >= 0} w[n,k] * out_perm[slot_row[n*K+k]] )
  * summed in k order in fp32.  Dropped slots contribute nothing and the kept
@@ -178,7 +194,10 @@ moe_status moe_unpermute_combine(const moe_problem* p, const uint16_t* out_perm,
                                  uint16_t* y, void* stream);
 
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn and
- * moe_unpermute_combine in sequence on one stream.
+ * moe_unpermute_combine in sequence on one stream.  Where
+ * moe_expert_gateup_gathered takes the problem, the gate/up GEMM runs as it
+ * (rows read from x through row_token) and no permuted copy of x is
+ * written; y is the same bit for bit.
  *   x [N, D] bf16; w_router [E, D] fp32; expert_bias [E] fp32 or NULL;
  *   w_gate, w_up [E, F, D] bf16; w_down [E, D, F] bf16; y [N, D] bf16 out.
  *   logits [N, E], topk_ids [N, K], topk_weights [N, K], expert_counts [E],

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     expert_down_bias,
     expert_down_fp8,
     expert_gateup,
+    expert_gateup_gathered,
     expert_gateup_fp8,
     expert_up_gelu,
     forward,

@@ -62,6 +62,8 @@ def _load():
     L.moe_grouped_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_gateup.restype = ctypes.c_int
     L.moe_expert_gateup.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_gateup_gathered.restype = ctypes.c_int
+    L.moe_expert_gateup_gathered.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_down.restype = ctypes.c_int
     L.moe_expert_down.argtypes = [P, vp, vp, vp, vp, vp]
     L.moe_unpermute_combine.restype = ctypes.c_int
@@ -184,6 +186,12 @@ def expert_gateup(p, x_perm, offsets, w_gate, w_up, h, stream=None):
     _check("moe_expert_gateup", lib.moe_expert_gateup(ctypes.byref(p), _ptr(x_perm), _ptr(offsets),
                                                       _ptr(w_gate), _ptr(w_up), _ptr(h),
                                                       _stream(stream)))
+
+
+def expert_gateup_gathered(p, x, row_token, offsets, w_gate, w_up, h, stream=None):
+    _check("moe_expert_gateup_gathered",
+           lib.moe_expert_gateup_gathered(ctypes.byref(p), _ptr(x), _ptr(row_token), _ptr(offsets),
+                                          _ptr(w_gate), _ptr(w_up), _ptr(h), _stream(stream)))
 
 
 def expert_down(p, h, offsets, w_down, out_perm, stream=None):

@@ -68,6 +68,11 @@ hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int
                                 hipStream_t s);
 hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
                               const uint16_t* wd, uint16_t* out_perm, hipStream_t s);
+bool gateup_gather_supported(const Dims& d);
+hipError_t launch_expert_gateup_gathered(const Dims& d, const uint16_t* x,
+                                         const int32_t* row_token, const int32_t* offsets,
+                                         const uint16_t* wg, const uint16_t* wu, uint16_t* h,
+                                         hipStream_t s);
 hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                               const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                               uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s);

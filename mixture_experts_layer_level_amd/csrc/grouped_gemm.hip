@@ -1693,6 +1693,19 @@ hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int
                                    nullptr, nullptr}, s);
 }
 
+// The LDS-DMA ring and split-ring tiles can read A rows through row_token;
+// the register-staged 32-row tiles (few rows per expert, k < 1024) cannot.
+bool gateup_gather_supported(const Dims& d) { return pick(d) != Shape::Small || d.D >= 1024; }
+
+hipError_t launch_expert_gateup_gathered(const Dims& d, const uint16_t* x,
+                                         const int32_t* row_token, const int32_t* offsets,
+                                         const uint16_t* wg, const uint16_t* wu, uint16_t* h,
+                                         hipStream_t s) {
+  if (!gateup_gather_supported(d)) return hipErrorNotSupported;
+  return launch_gemm<kEpiSwiglu, false>(d, GemmArgs{x, wg, wu, h, offsets, d.E, d.D, d.F, 0,
+                                   nullptr, nullptr, nullptr, row_token}, s);
+}
+
 hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
                               const uint16_t* wd, uint16_t* out_perm, hipStream_t s) {
   return launch_gemm<kEpiStore, false>(d, GemmArgs{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D,

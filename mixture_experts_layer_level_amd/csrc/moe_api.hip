@@ -94,12 +94,15 @@ inline moe_status hip_status(hipError_t e) {
 
 // The layer: the routing given by `route`, permute, the grouped FFN given by
 // `ffn`, combine.  weights_present / weights_aligned: the caller's checks of
-// its router and expert weights.
+// its router and expert weights.  can_gather: `ffn` can read its rows of x
+// through row_token; where the tiles allow it, the permuted copy of x is
+// then not written and `ffn` gets x and row_token (else x_perm and NULL).
 template <class Route, class Ffn>
 moe_status forward_impl(const moe_problem* p, const uint16_t* x, bool weights_present,
                         bool weights_aligned, uint16_t* y, float* logits, int32_t* topk_ids,
                         float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
-                        void* ws, size_t ws_bytes, void* stream, Route route, Ffn ffn) {
+                        void* ws, size_t ws_bytes, void* stream, bool can_gather, Route route,
+                        Ffn ffn) {
   Dims d;
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
@@ -123,10 +126,13 @@ moe_status forward_impl(const moe_problem* p, const uint16_t* x, bool weights_pr
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = hip_status(route(d, logits, topk_ids, topk_weights, base, L, s));
   if (st != MOE_OK) return st;
+  const bool gather = can_gather && !d.padded && (uint64_t)d.N * d.D * 2 < (1ull << 32) &&
+                      gateup_gather_supported(d);
   st = hip_status(launch_permute(d, x, topk_ids, expert_counts, expert_offsets, row_token,
-                                 slot_row, x_perm, base + L.perm, s));
+                                 slot_row, gather ? nullptr : x_perm, base + L.perm, s));
   if (st != MOE_OK) return st;
-  st = hip_status(ffn(d, x_perm, expert_offsets, out_perm, base + L.ffn, s));
+  st = hip_status(ffn(d, gather ? x : x_perm, gather ? row_token : nullptr, expert_offsets,
+                      out_perm, base + L.ffn, s));
   if (st != MOE_OK) return st;
   return hip_status(launch_combine(d, out_perm, slot_row, topk_weights, y, s));
 }
@@ -284,6 +290,24 @@ moe_status moe_expert_gateup(const moe_problem* p, const uint16_t* x_perm,
                                          static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_expert_gateup_gathered(const moe_problem* p, const uint16_t* x,
+                                      const int32_t* row_token, const int32_t* expert_offsets,
+                                      const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h,
+                                      void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !row_token || !expert_offsets || !w_gate || !w_up || !h) return MOE_ERR_INVALID_ARG;
+  if (d.padded || (uint64_t)d.N * d.D * 2 >= (1ull << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(h))
+    return MOE_ERR_UNSUPPORTED;
+  if (!gateup_gather_supported(d)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_gateup_gathered(d, x, row_token, expert_offsets, w_gate, w_up,
+                                                  h, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_expert_down(const moe_problem* p, const uint16_t* h,
                            const int32_t* expert_offsets, const uint16_t* w_down,
                            uint16_t* out_perm, void* stream) {
@@ -321,16 +345,22 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
   const bool aligned = aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) &&
                        aligned16(w_down);
   return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
-                      expert_offsets, ws, ws_bytes, stream,
+                      expert_offsets, ws, ws_bytes, stream, true,
                       [&](const Dims& d, float* lg, int32_t* ids, float* w, char*,
                           const ForwardWs&, hipStream_t s) {
                         const hipError_t e = launch_router_gemm(d, x, w_router, lg, s);
                         return e != hipSuccess ? e : launch_topk(d, lg, expert_bias, ids, w, s);
                       },
-                      [&](const Dims& d, const uint16_t* xp, const int32_t* offs, uint16_t* op,
-                          void* fws, hipStream_t s) {
-                        return launch_grouped_ffn(d, xp, offs, w_gate, w_up, w_down, op, nullptr,
-                                                  fws, s);
+                      [&](const Dims& d, const uint16_t* xp, const int32_t* rt,
+                          const int32_t* offs, uint16_t* op, void* fws, hipStream_t s) {
+                        if (!rt)
+                          return launch_grouped_ffn(d, xp, offs, w_gate, w_up, w_down, op,
+                                                    nullptr, fws, s);
+                        uint16_t* h = static_cast<uint16_t*>(fws);
+                        const hipError_t e =
+                            launch_expert_gateup_gathered(d, xp, rt, offs, w_gate, w_up, h, s);
+                        return e != hipSuccess ? e
+                                               : launch_expert_down(d, h, offs, w_down, op, s);
                       });
 }
 
@@ -434,14 +464,14 @@ moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float*
   const Fp8Weight wg{w_gate_codes, w_gate_scales}, wu{w_up_codes, w_up_scales},
       wd{w_down_codes, w_down_scales};
   return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
-                      expert_offsets, ws, ws_bytes, stream,
+                      expert_offsets, ws, ws_bytes, stream, false,
                       [&](const Dims& d, float* lg, int32_t* ids, float* w, char*,
                           const ForwardWs&, hipStream_t s) {
                         const hipError_t e = launch_router_gemm(d, x, w_router, lg, s);
                         return e != hipSuccess ? e : launch_topk(d, lg, expert_bias, ids, w, s);
                       },
-                      [&](const Dims& d, const uint16_t* xp, const int32_t* offs, uint16_t* op,
-                          void* fws, hipStream_t s) {
+                      [&](const Dims& d, const uint16_t* xp, const int32_t*,
+                          const int32_t* offs, uint16_t* op, void* fws, hipStream_t s) {
                         return launch_grouped_ffn_fp8(d, xp, offs, wg, wu, wd, op, nullptr, fws,
                                                       s);
                       });
@@ -538,7 +568,7 @@ moe_status moe_forward_gelu(const moe_problem* p, const uint16_t* x, const uint1
                        aligned16(w1) && aligned16(b1) && aligned16(w2) && aligned16(b2);
   if (present && aligned && x && y && d.D % 256 != 0) return MOE_ERR_UNSUPPORTED;
   return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
-                      expert_offsets, ws, ws_bytes, stream,
+                      expert_offsets, ws, ws_bytes, stream, false,
                       [&](const Dims& dd, float* lg, int32_t* ids, float* w, char* base,
                           const ForwardWs& L, hipStream_t s) {
                         return launch_route_mlp(dd, x, w_proj, b_proj, w_out, b_out,
@@ -546,8 +576,8 @@ moe_status moe_forward_gelu(const moe_problem* p, const uint16_t* x, const uint1
                                                 reinterpret_cast<int32_t*>(base + L.roff), lg,
                                                 ids, w, s);
                       },
-                      [&](const Dims& dd, const uint16_t* xp, const int32_t* offs, uint16_t* op,
-                          void* fws, hipStream_t s) {
+                      [&](const Dims& dd, const uint16_t* xp, const int32_t*,
+                          const int32_t* offs, uint16_t* op, void* fws, hipStream_t s) {
                         return launch_grouped_ffn_gelu(dd, xp, offs, w1, b1, w2, b2, op, nullptr,
                                                        fws, s);
                       });

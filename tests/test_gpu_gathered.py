@@ -1,0 +1,74 @@
+"""GPU parity of moe_expert_gateup_gathered against moe_expert_gateup.
+
+The gathered call reads row r of its input as x[row_token[r]] instead of
+x_perm[r]; tiles, k order and epilogue are the same, so h must be bit for
+bit what moe_expert_gateup writes from x_perm (which the parity tests check
+against the oracle).  Every case starts h as NaN, so a row the gathered call
+skipped fails too.  Shapes with no gathered tile form and the padded layout
+must be refused with MOE_ERR_UNSUPPORTED.
+"""
+import pytest
+import torch
+
+import moe_synth as ms
+
+pytestmark = pytest.mark.gpu
+
+from gpu_layer import DEV, SMALL, Layer  # noqa: E402
+import mixture_experts_layer_level_amd as moe  # noqa: E402
+
+UNSUPPORTED = 2
+
+
+def has_gathered_tiles(cfg):
+    # the register-staged 32-row tiles (<= 48 rows per expert, D < 1024) read
+    # A rows in place only
+    return not (cfg.N * cfg.K / cfg.E <= 48 and cfg.D < 1024)
+
+
+def gathered_h(L):
+    h = torch.full_like(L.h, float("nan"))
+    moe.expert_gateup_gathered(L.p, L.x, L.row_token, L.offsets, L.w_gate, L.w_up, h)
+    torch.cuda.synchronize()
+    return h
+
+
+def same_bits(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+CONTIGUOUS = [n for n, c in SMALL.items() if c.capacity is None]
+
+
+@pytest.mark.parametrize("name", CONTIGUOUS)
+def test_gathered_gateup_small(name):
+    cfg = SMALL[name]
+    print(f"[gathered] {name} N={cfg.N} D={cfg.D} E={cfg.E} K={cfg.K} F={cfg.F}", flush=True)
+    L = Layer(cfg)
+    L.staged()
+    if not has_gathered_tiles(cfg):
+        with pytest.raises(moe.MoEError) as err:
+            gathered_h(L)
+        assert err.value.status == UNSUPPORTED
+        return
+    assert same_bits(gathered_h(L), L.h)
+
+
+def test_gathered_gateup_refuses_padded():
+    L = Layer(SMALL["padded"], padded=True)
+    L.staged()
+    with pytest.raises(moe.MoEError) as err:
+        gathered_h(L)
+    assert err.value.status == UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["mixtral", "deepseek_v3", "qwen3_decode", "hot_skew"])
+def test_gathered_gateup_full_size(name):
+    """The workloads at full size, every row of h compared."""
+    cfg = ms.CONFIGS[name]
+    print(f"[gathered full] {name}", flush=True)
+    L = Layer(cfg)
+    L.staged()
+    assert same_bits(gathered_h(L), L.h)
+    del L
+    torch.cuda.empty_cache()

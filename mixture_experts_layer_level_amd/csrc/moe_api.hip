@@ -301,8 +301,8 @@ moe_status moe_expert_gateup_gathered(const moe_problem* p, const uint16_t* x,
   if (d.padded || (uint64_t)d.N * d.D * 2 >= (1ull << 32)) return MOE_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(h))
     return MOE_ERR_UNSUPPORTED;
-  if (!gateup_gather_supported(d)) return MOE_ERR_UNSUPPORTED;
   if (d.N == 0) return MOE_OK;
+  if (!gateup_gather_supported(d)) return MOE_ERR_UNSUPPORTED;
   (void)hipGetLastError();  // report only this call's launch errors
   return hip_status(launch_expert_gateup_gathered(d, x, row_token, expert_offsets, w_gate, w_up,
                                                   h, static_cast<hipStream_t>(stream)));

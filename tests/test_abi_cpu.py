@@ -117,12 +117,25 @@ def test_staged_argument_errors():
     assert L.moe_expert_gateup(bp, FAKE, FAKE, FAKE, FAKE, None, 0) == INVALID
     assert L.moe_expert_down(bp, FAKE, FAKE, FAKE, FAKE + 2, 0) == UNSUPPORTED
     assert L.moe_unpermute_combine(bp, FAKE, FAKE, None, FAKE, 0) == INVALID
+    # gathered gate/up: row_token required; refused for the padded layout, for
+    # x of 4 GiB or more and for the register-staged tiles (<= 48 rows per
+    # expert with D < 1024: P()'s 16 rows per expert, D = 256)
+    big = ctypes.byref(P(N=4096))                     # 1024 rows per expert
+    gg = L.moe_expert_gateup_gathered
+    assert gg(big, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0) == INVALID
+    assert gg(big, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == UNSUPPORTED
+    assert gg(ctypes.byref(P(N=4096, cn=5, cd=4)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) \
+        == UNSUPPORTED
+    assert gg(ctypes.byref(P(N=1 << 20, D=2048)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) \
+        == UNSUPPORTED                                                 # 4 GiB of x
+    assert gg(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == UNSUPPORTED
     # every entry point accepts N = 0 without launching
     z = ctypes.byref(P(N=0))
     assert L.moe_route(z, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, 0) == OK
     assert L.moe_permute(z, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0) == OK
     assert L.moe_grouped_ffn(z, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0) == OK
     assert L.moe_expert_gateup(z, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == OK
+    assert L.moe_expert_gateup_gathered(z, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == OK
     assert L.moe_expert_down(z, FAKE, FAKE, FAKE, FAKE, 0) == OK
     assert L.moe_unpermute_combine(z, FAKE, FAKE, FAKE, FAKE, 0) == OK
 

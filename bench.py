@@ -65,8 +65,9 @@ def main():
                          "from x, no permuted copy)")
     ap.add_argument("--xperm", action="store_true",
                     help="write the permuted copy of x and run gate/up on it; by default the "
-                         "bf16 SwiGLU layer's gate/up reads its rows of x through row_token "
-                         "(moe_expert_gateup_gathered) wherever the library takes the shape")
+                         "SwiGLU layer's gate/up (bf16 or FP8 weights) reads its rows of x "
+                         "through row_token (moe_expert_gateup_gathered, "
+                         "moe_expert_gateup_fp8_gathered) wherever the library takes the shape")
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
@@ -136,16 +137,19 @@ def main():
         qg, qu, qd = quant(wg), quant(wu), quant(wd)
         torch.cuda.synchronize()
 
-    # The bf16 SwiGLU layer's gate/up reads its rows of x through row_token
+    # The SwiGLU layer's gate/up (bf16 or FP8 weights) reads its rows of x through row_token
     # wherever the library takes the shape; it refuses, before any launch, the
     # shapes whose tiles have no gathered form.  One route + permute first, so
     # that the trial call runs on real routing tables.
-    gather = not (args.xperm or gelu or args.fused or fp8 or capv)
+    gather = not (args.xperm or gelu or args.fused or capv)
     if gather:
         moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row, None, ws, stream=stream)
         try:
-            moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=stream)
+            if fp8:
+                moe.expert_gateup_fp8_gathered(p, x, row_token, offsets, qg, qu, h, stream=stream)
+            else:
+                moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=stream)
         except moe.MoEError as err:
             if err.status != 2:   # MOE_ERR_UNSUPPORTED: run the permuted copy instead
                 raise
@@ -197,7 +201,9 @@ def main():
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row,
                     None if gather else x_perm, ws, stream=stream)
         rec(ev, 2)
-        if gather:
+        if gather and fp8:
+            moe.expert_gateup_fp8_gathered(p, x, row_token, offsets, qg, qu, h, stream=stream)
+        elif gather:
             moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=stream)
         elif fp8:
             moe.expert_gateup_fp8(p, x_perm, offsets, qg, qu, h, stream=stream)

@@ -335,7 +335,8 @@ moe_status moe_quantize_fp8(int64_t rows, int32_t cols, const uint16_t* w, uint8
                             uint8_t* scales, void* stream);
 
 /* moe_expert_gateup / moe_expert_down / moe_grouped_ffn / moe_forward with
- * FP8 weight stacks in place of the bf16 ones: w_gate_*, w_up_* [E, F, D]
+ * FP8 weight stacks in place of the bf16 ones (moe_forward_fp8 gathers the
+ * gate/up rows from x as moe_forward does): w_gate_*, w_up_* [E, F, D]
  * (scales [E, F/32, D/32, 32]), w_down_* [E, D, F] (scales
  * [E, D/32, F/32, 32]).  Codes and scales must be 16-byte aligned
  * (MOE_ERR_UNSUPPORTED else).  Everything else -- shapes, layouts, row
@@ -344,6 +345,17 @@ moe_status moe_expert_gateup_fp8(const moe_problem* p, const uint16_t* x_perm,
                                  const int32_t* expert_offsets, const uint8_t* w_gate_codes,
                                  const uint8_t* w_gate_scales, const uint8_t* w_up_codes,
                                  const uint8_t* w_up_scales, uint16_t* h, void* stream);
+/* moe_expert_gateup_gathered with FP8 weight stacks: rows read from x through
+ * row_token, h bit for bit that of moe_expert_gateup_fp8 on x_perm =
+ * x[row_token].  Refused (MOE_ERR_UNSUPPORTED) as the bf16 call, except that
+ * with R / E <= 48 the FP8 tiles also take D >= 512 in multiples of 128. */
+moe_status moe_expert_gateup_fp8_gathered(const moe_problem* p, const uint16_t* x,
+                                          const int32_t* row_token,
+                                          const int32_t* expert_offsets,
+                                          const uint8_t* w_gate_codes,
+                                          const uint8_t* w_gate_scales,
+                                          const uint8_t* w_up_codes, const uint8_t* w_up_scales,
+                                          uint16_t* h, void* stream);
 moe_status moe_expert_down_fp8(const moe_problem* p, const uint16_t* h,
                                const int32_t* expert_offsets, const uint8_t* w_down_codes,
                                const uint8_t* w_down_scales, uint16_t* out_perm, void* stream);

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     expert_gateup,
     expert_gateup_gathered,
     expert_gateup_fp8,
+    expert_gateup_fp8_gathered,
     expert_up_gelu,
     forward,
     forward_fp8,

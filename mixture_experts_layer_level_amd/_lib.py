@@ -91,6 +91,8 @@ def _load():
     L.moe_quantize_fp8.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp]
     L.moe_expert_gateup_fp8.restype = ctypes.c_int
     L.moe_expert_gateup_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_gateup_fp8_gathered.restype = ctypes.c_int
+    L.moe_expert_gateup_fp8_gathered.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_down_fp8.restype = ctypes.c_int
     L.moe_expert_down_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.moe_grouped_ffn_fp8.restype = ctypes.c_int
@@ -233,6 +235,14 @@ def expert_gateup_fp8(p, x_perm, offsets, w_gate, w_up, h, stream=None):
            lib.moe_expert_gateup_fp8(ctypes.byref(p), _ptr(x_perm), _ptr(offsets), _ptr(w_gate[0]),
                                      _ptr(w_gate[1]), _ptr(w_up[0]), _ptr(w_up[1]), _ptr(h),
                                      _stream(stream)))
+
+
+def expert_gateup_fp8_gathered(p, x, row_token, offsets, w_gate, w_up, h, stream=None):
+    _check("moe_expert_gateup_fp8_gathered",
+           lib.moe_expert_gateup_fp8_gathered(ctypes.byref(p), _ptr(x), _ptr(row_token),
+                                              _ptr(offsets), _ptr(w_gate[0]), _ptr(w_gate[1]),
+                                              _ptr(w_up[0]), _ptr(w_up[1]), _ptr(h),
+                                              _stream(stream)))
 
 
 def expert_down_fp8(p, h, offsets, w_down, out_perm, stream=None):

@@ -68,7 +68,7 @@ hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int
                                 hipStream_t s);
 hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
                               const uint16_t* wd, uint16_t* out_perm, hipStream_t s);
-bool gateup_gather_supported(const Dims& d);
+bool gateup_gather_supported(const Dims& d, bool fp8 = false);
 hipError_t launch_expert_gateup_gathered(const Dims& d, const uint16_t* x,
                                          const int32_t* row_token, const int32_t* offsets,
                                          const uint16_t* wg, const uint16_t* wu, uint16_t* h,
@@ -86,6 +86,10 @@ struct Fp8Weight {
 hipError_t launch_expert_gateup_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                     const Fp8Weight& wg, const Fp8Weight& wu, uint16_t* h,
                                     hipStream_t s);
+hipError_t launch_expert_gateup_fp8_gathered(const Dims& d, const uint16_t* x,
+                                             const int32_t* row_token, const int32_t* offsets,
+                                             const Fp8Weight& wg, const Fp8Weight& wu,
+                                             uint16_t* h, hipStream_t s);
 hipError_t launch_expert_down_fp8(const Dims& d, const uint16_t* h, const int32_t* offsets,
                                   const Fp8Weight& wd, uint16_t* out_perm, hipStream_t s);
 hipError_t launch_grouped_ffn_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,

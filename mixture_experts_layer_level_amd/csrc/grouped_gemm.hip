@@ -1694,8 +1694,11 @@ hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int
 }
 
 // The LDS-DMA ring and split-ring tiles can read A rows through row_token;
-// the register-staged 32-row tiles (few rows per expert, k < 1024) cannot.
-bool gateup_gather_supported(const Dims& d) { return pick(d) != Shape::Small || d.D >= 1024; }
+// the register-staged 32-row tiles (few rows per expert, short k) cannot.
+// With FP8 weights the 32-row ring also serves k >= 512 in steps of 128.
+bool gateup_gather_supported(const Dims& d, bool fp8) {
+  return pick(d) != Shape::Small || d.D >= 1024 || (fp8 && d.D >= 512 && d.D % 128 == 0);
+}
 
 hipError_t launch_expert_gateup_gathered(const Dims& d, const uint16_t* x,
                                          const int32_t* row_token, const int32_t* offsets,
@@ -1726,6 +1729,15 @@ hipError_t launch_expert_gateup_fp8(const Dims& d, const uint16_t* x_perm, const
                                     hipStream_t s) {
   return launch_gemm<kEpiSwiglu, true>(d, GemmArgs{x_perm, wg.codes, wu.codes, h, offsets, d.E, d.D, d.F,
                                   0, wg.scales, wu.scales}, s);
+}
+
+hipError_t launch_expert_gateup_fp8_gathered(const Dims& d, const uint16_t* x,
+                                             const int32_t* row_token, const int32_t* offsets,
+                                             const Fp8Weight& wg, const Fp8Weight& wu,
+                                             uint16_t* h, hipStream_t s) {
+  if (!gateup_gather_supported(d, true)) return hipErrorNotSupported;
+  return launch_gemm<kEpiSwiglu, true>(d, GemmArgs{x, wg.codes, wu.codes, h, offsets, d.E, d.D,
+                                  d.F, 0, wg.scales, wu.scales, nullptr, row_token}, s);
 }
 
 hipError_t launch_expert_down_fp8(const Dims& d, const uint16_t* h, const int32_t* offsets,

@@ -94,15 +94,18 @@ inline moe_status hip_status(hipError_t e) {
 
 // The layer: the routing given by `route`, permute, the grouped FFN given by
 // `ffn`, combine.  weights_present / weights_aligned: the caller's checks of
-// its router and expert weights.  can_gather: `ffn` can read its rows of x
-// through row_token; where the tiles allow it, the permuted copy of x is
-// then not written and `ffn` gets x and row_token (else x_perm and NULL).
+// its router and expert weights.  gather: `ffn` can read its rows of x
+// through row_token (kGatherBf16 / kGatherFp8: with bf16 or FP8 weight
+// tiles); where the tiles allow it, the permuted copy of x is then not
+// written and `ffn` gets x and row_token (else x_perm and NULL).
+enum GatherKind { kNoGather, kGatherBf16, kGatherFp8 };
+
 template <class Route, class Ffn>
 moe_status forward_impl(const moe_problem* p, const uint16_t* x, bool weights_present,
                         bool weights_aligned, uint16_t* y, float* logits, int32_t* topk_ids,
                         float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
-                        void* ws, size_t ws_bytes, void* stream, bool can_gather, Route route,
-                        Ffn ffn) {
+                        void* ws, size_t ws_bytes, void* stream, GatherKind can_gather,
+                        Route route, Ffn ffn) {
   Dims d;
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
@@ -126,8 +129,9 @@ moe_status forward_impl(const moe_problem* p, const uint16_t* x, bool weights_pr
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = hip_status(route(d, logits, topk_ids, topk_weights, base, L, s));
   if (st != MOE_OK) return st;
-  const bool gather = can_gather && !d.padded && (uint64_t)d.N * d.D * 2 < (1ull << 32) &&
-                      gateup_gather_supported(d);
+  const bool gather = can_gather != kNoGather && !d.padded &&
+                      (uint64_t)d.N * d.D * 2 < (1ull << 32) &&
+                      gateup_gather_supported(d, can_gather == kGatherFp8);
   st = hip_status(launch_permute(d, x, topk_ids, expert_counts, expert_offsets, row_token,
                                  slot_row, gather ? nullptr : x_perm, base + L.perm, s));
   if (st != MOE_OK) return st;
@@ -345,7 +349,7 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
   const bool aligned = aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) &&
                        aligned16(w_down);
   return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
-                      expert_offsets, ws, ws_bytes, stream, true,
+                      expert_offsets, ws, ws_bytes, stream, kGatherBf16,
                       [&](const Dims& d, float* lg, int32_t* ids, float* w, char*,
                           const ForwardWs&, hipStream_t s) {
                         const hipError_t e = launch_router_gemm(d, x, w_router, lg, s);
@@ -406,6 +410,29 @@ moe_status moe_expert_gateup_fp8(const moe_problem* p, const uint16_t* x_perm,
                                              static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_expert_gateup_fp8_gathered(const moe_problem* p, const uint16_t* x,
+                                          const int32_t* row_token,
+                                          const int32_t* expert_offsets,
+                                          const uint8_t* w_gate_codes,
+                                          const uint8_t* w_gate_scales,
+                                          const uint8_t* w_up_codes, const uint8_t* w_up_scales,
+                                          uint16_t* h, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !row_token || !expert_offsets || !h) return MOE_ERR_INVALID_ARG;
+  if ((st = check_fp8(w_gate_codes, w_gate_scales)) != MOE_OK) return st;
+  if ((st = check_fp8(w_up_codes, w_up_scales)) != MOE_OK) return st;
+  if (d.padded || (uint64_t)d.N * d.D * 2 >= (1ull << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(h)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  if (!gateup_gather_supported(d, true)) return MOE_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_gateup_fp8_gathered(
+      d, x, row_token, expert_offsets, Fp8Weight{w_gate_codes, w_gate_scales},
+      Fp8Weight{w_up_codes, w_up_scales}, h, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_expert_down_fp8(const moe_problem* p, const uint16_t* h,
                                const int32_t* expert_offsets, const uint8_t* w_down_codes,
                                const uint8_t* w_down_scales, uint16_t* out_perm, void* stream) {
@@ -464,14 +491,21 @@ moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float*
   const Fp8Weight wg{w_gate_codes, w_gate_scales}, wu{w_up_codes, w_up_scales},
       wd{w_down_codes, w_down_scales};
   return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
-                      expert_offsets, ws, ws_bytes, stream, false,
+                      expert_offsets, ws, ws_bytes, stream, kGatherFp8,
                       [&](const Dims& d, float* lg, int32_t* ids, float* w, char*,
                           const ForwardWs&, hipStream_t s) {
                         const hipError_t e = launch_router_gemm(d, x, w_router, lg, s);
                         return e != hipSuccess ? e : launch_topk(d, lg, expert_bias, ids, w, s);
                       },
-                      [&](const Dims& d, const uint16_t* xp, const int32_t*,
+                      [&](const Dims& d, const uint16_t* xp, const int32_t* rt,
                           const int32_t* offs, uint16_t* op, void* fws, hipStream_t s) {
+                        if (rt) {
+                          uint16_t* h = static_cast<uint16_t*>(fws);
+                          const hipError_t e =
+                              launch_expert_gateup_fp8_gathered(d, xp, rt, offs, wg, wu, h, s);
+                          return e != hipSuccess ? e
+                                                 : launch_expert_down_fp8(d, h, offs, wd, op, s);
+                        }
                         return launch_grouped_ffn_fp8(d, xp, offs, wg, wu, wd, op, nullptr, fws,
                                                       s);
                       });
@@ -568,7 +602,7 @@ moe_status moe_forward_gelu(const moe_problem* p, const uint16_t* x, const uint1
                        aligned16(w1) && aligned16(b1) && aligned16(w2) && aligned16(b2);
   if (present && aligned && x && y && d.D % 256 != 0) return MOE_ERR_UNSUPPORTED;
   return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
-                      expert_offsets, ws, ws_bytes, stream, false,
+                      expert_offsets, ws, ws_bytes, stream, kNoGather,
                       [&](const Dims& dd, float* lg, int32_t* ids, float* w, char* base,
                           const ForwardWs& L, hipStream_t s) {
                         return launch_route_mlp(dd, x, w_proj, b_proj, w_out, b_out,

@@ -129,6 +129,11 @@ def test_staged_argument_errors():
     assert gg(ctypes.byref(P(N=1 << 20, D=2048)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) \
         == UNSUPPORTED                                                 # 4 GiB of x
     assert gg(bp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == UNSUPPORTED
+    g8 = L.moe_expert_gateup_fp8_gathered
+    assert g8(big, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == INVALID
+    assert g8(big, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0) == INVALID
+    assert g8(ctypes.byref(P(N=4096, cn=5, cd=4)), *([FAKE] * 8), 0) == UNSUPPORTED
+    assert g8(bp, *([FAKE] * 8), 0) == UNSUPPORTED                  # D = 256
     # every entry point accepts N = 0 without launching
     z = ctypes.byref(P(N=0))
     assert L.moe_route(z, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, 0) == OK
@@ -136,6 +141,7 @@ def test_staged_argument_errors():
     assert L.moe_grouped_ffn(z, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0) == OK
     assert L.moe_expert_gateup(z, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == OK
     assert L.moe_expert_gateup_gathered(z, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == OK
+    assert L.moe_expert_gateup_fp8_gathered(z, *([FAKE] * 8), 0) == OK
     assert L.moe_expert_down(z, FAKE, FAKE, FAKE, FAKE, 0) == OK
     assert L.moe_unpermute_combine(z, FAKE, FAKE, FAKE, FAKE, 0) == OK
 

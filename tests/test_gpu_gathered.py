@@ -1,4 +1,5 @@
-"""GPU parity of moe_expert_gateup_gathered against moe_expert_gateup.
+"""GPU parity of moe_expert_gateup_gathered against moe_expert_gateup (and of
+the FP8-weight pair).
 
 The gathered call reads row r of its input as x[row_token[r]] instead of
 x_perm[r]; tiles, k order and epilogue are the same, so h must be bit for
@@ -20,10 +21,22 @@ import mixture_experts_layer_level_amd as moe  # noqa: E402
 UNSUPPORTED = 2
 
 
-def has_gathered_tiles(cfg):
+def has_gathered_tiles(cfg, fp8=False):
     # the register-staged 32-row tiles (<= 48 rows per expert, D < 1024) read
-    # A rows in place only
-    return not (cfg.N * cfg.K / cfg.E <= 48 and cfg.D < 1024)
+    # A rows in place only; with FP8 weights the 32-row ring also takes
+    # D >= 512 in multiples of 128
+    if cfg.N * cfg.K / cfg.E > 48 or cfg.D >= 1024:
+        return True
+    return fp8 and cfg.D >= 512 and cfg.D % 128 == 0
+
+
+def quantize(w):
+    """moe_quantize_fp8 of a bf16 stack [E, rows, cols]: (codes, scales)."""
+    rows, cols = w.shape[-2], w.shape[-1]
+    codes = torch.empty(w.shape, dtype=torch.uint8, device=DEV)
+    scales = torch.empty((w.shape[0], rows // 32, cols // 32, 32), dtype=torch.uint8, device=DEV)
+    moe.quantize_fp8(w.numel() // cols, cols, w, codes, scales)
+    return codes, scales
 
 
 def gathered_h(L):
@@ -31,6 +44,17 @@ def gathered_h(L):
     moe.expert_gateup_gathered(L.p, L.x, L.row_token, L.offsets, L.w_gate, L.w_up, h)
     torch.cuda.synchronize()
     return h
+
+
+def fp8_pair(L):
+    """h of moe_expert_gateup_fp8 on x_perm, and of the gathered call."""
+    qg, qu = quantize(L.w_gate), quantize(L.w_up)
+    h_ref = torch.empty_like(L.h)
+    moe.expert_gateup_fp8(L.p, L.x_perm, L.offsets, qg, qu, h_ref)
+    h = torch.full_like(L.h, float("nan"))
+    moe.expert_gateup_fp8_gathered(L.p, L.x, L.row_token, L.offsets, qg, qu, h)
+    torch.cuda.synchronize()
+    return h_ref, h
 
 
 def same_bits(a, b):
@@ -71,4 +95,31 @@ def test_gathered_gateup_full_size(name):
     L.staged()
     assert same_bits(gathered_h(L), L.h)
     del L
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", CONTIGUOUS)
+def test_gathered_gateup_fp8_small(name):
+    cfg = SMALL[name]
+    print(f"[gathered fp8] {name} N={cfg.N} D={cfg.D} E={cfg.E} K={cfg.K} F={cfg.F}", flush=True)
+    L = Layer(cfg)
+    L.staged()
+    if not has_gathered_tiles(cfg, fp8=True):
+        with pytest.raises(moe.MoEError) as err:
+            fp8_pair(L)
+        assert err.value.status == UNSUPPORTED
+        return
+    h_ref, h = fp8_pair(L)
+    assert same_bits(h, h_ref)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "deepseek_v3", "qwen3_decode", "hot_skew"])
+def test_gathered_gateup_fp8_full_size(name):
+    cfg = ms.CONFIGS[name]
+    print(f"[gathered fp8 full] {name}", flush=True)
+    L = Layer(cfg)
+    L.staged()
+    h_ref, h = fp8_pair(L)
+    assert same_bits(h, h_ref)
+    del L, h_ref, h
     torch.cuda.empty_cache()

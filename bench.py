@@ -64,10 +64,10 @@ def main():
                     help="the expert FFN as one persistent launch (moe_fused_ffn; rows gathered "
                          "from x, no permuted copy)")
     ap.add_argument("--xperm", action="store_true",
-                    help="write the permuted copy of x and run gate/up on it; by default the "
-                         "SwiGLU layer's gate/up (bf16 or FP8 weights) reads its rows of x "
-                         "through row_token (moe_expert_gateup_gathered, "
-                         "moe_expert_gateup_fp8_gathered) wherever the library takes the shape")
+                    help="write the permuted copy of x and run the first expert GEMM on it; by "
+                         "default that GEMM reads its rows of x through row_token "
+                         "(moe_expert_gateup_gathered, moe_expert_gateup_fp8_gathered, "
+                         "moe_expert_up_gelu_gathered) wherever the library takes the shape")
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
@@ -137,16 +137,23 @@ def main():
         qg, qu, qd = quant(wg), quant(wu), quant(wd)
         torch.cuda.synchronize()
 
-    # The SwiGLU layer's gate/up (bf16 or FP8 weights) reads its rows of x through row_token
+    # The first expert GEMM (gate/up, or the GELU layer's up GEMM) reads its rows of x through row_token
     # wherever the library takes the shape; it refuses, before any launch, the
     # shapes whose tiles have no gathered form.  One route + permute first, so
     # that the trial call runs on real routing tables.
-    gather = not (args.xperm or gelu or args.fused or capv)
+    gather = not (args.xperm or args.fused or capv)
     if gather:
-        moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
+        if gelu:
+            moe.route_mlp(p, x, inp["w_proj"], inp["b_proj"], inp["w_out"], inp["b_out"], logits,
+                          ids, w, ws, features=feats, stream=stream)
+        else:
+            moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row, None, ws, stream=stream)
         try:
-            if fp8:
+            if gelu:
+                moe.expert_up_gelu_gathered(p, x, row_token, offsets, inp["w1"], inp["b1"], h,
+                                            stream=stream)
+            elif fp8:
                 moe.expert_gateup_fp8_gathered(p, x, row_token, offsets, qg, qu, h, stream=stream)
             else:
                 moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=stream)
@@ -169,9 +176,14 @@ def main():
         moe.route_mlp(p, x, i["w_proj"], i["b_proj"], i["w_out"], i["b_out"], logits, ids, w, ws,
                       features=feats, stream=stream)
         rec(ev, 1)
-        moe.permute(p, x, ids, counts, offsets, row_token, slot_row, x_perm, ws, stream=stream)
+        moe.permute(p, x, ids, counts, offsets, row_token, slot_row,
+                    None if gather else x_perm, ws, stream=stream)
         rec(ev, 2)
-        moe.expert_up_gelu(p, x_perm, offsets, i["w1"], i["b1"], h, stream=stream)
+        if gather:
+            moe.expert_up_gelu_gathered(p, x, row_token, offsets, i["w1"], i["b1"], h,
+                                        stream=stream)
+        else:
+            moe.expert_up_gelu(p, x_perm, offsets, i["w1"], i["b1"], h, stream=stream)
         rec(ev, 3)
         moe.expert_down_bias(p, h, offsets, i["w2"], i["b2"], out_perm, stream=stream)
         rec(ev, 4)
@@ -268,8 +280,8 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(args.config + ("_padded" if capv else "") +
                                        ("_fp8" if fp8 else "") + ("_xperm" if args.xperm else ""))
-    roof["kernel"] = ("grouped up GEMM + bias + GELU" if gelu
-                      else "grouped gate/up GEMM + SwiGLU" +
+    roof["kernel"] = (("grouped up GEMM + bias + GELU" if gelu
+                       else "grouped gate/up GEMM + SwiGLU") +
                       (", rows gathered from x through row_token" if gather else ""))
     if args.fused:
         # the one fused launch: gate/up, SwiGLU and down of every expert
@@ -333,7 +345,7 @@ def main():
                    "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
                               else "SwiGLU"),
                    "ffn_launch": ("fused (one persistent launch)" if args.fused else
-                                  "two grouped GEMMs, gate/up rows gathered from x" if gather
+                                  "two grouped GEMMs, rows of the first gathered from x" if gather
                                   else "two grouped GEMMs")},
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,

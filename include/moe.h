@@ -281,6 +281,14 @@ moe_status moe_route_mlp(const moe_problem* p, const uint16_t* x, const uint16_t
 moe_status moe_expert_up_gelu(const moe_problem* p, const uint16_t* x_perm,
                               const int32_t* expert_offsets, const uint16_t* w1, const float* b1,
                               uint16_t* h, void* stream);
+/* moe_expert_up_gelu on x[row_token] without the permuted copy, as
+ * moe_expert_gateup_gathered is to moe_expert_gateup (same arguments for x
+ * and row_token, same refusals); h bit for bit that of moe_expert_up_gelu.
+ * moe_forward_gelu uses it where the problem allows. */
+moe_status moe_expert_up_gelu_gathered(const moe_problem* p, const uint16_t* x,
+                                       const int32_t* row_token, const int32_t* expert_offsets,
+                                       const uint16_t* w1, const float* b1, uint16_t* h,
+                                       void* stream);
 moe_status moe_expert_down_bias(const moe_problem* p, const uint16_t* h,
                                 const int32_t* expert_offsets, const uint16_t* w2,
                                 const float* b2, uint16_t* out_perm, void* stream);

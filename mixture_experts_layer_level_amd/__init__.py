@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     expert_gateup_fp8,
     expert_gateup_fp8_gathered,
     expert_up_gelu,
+    expert_up_gelu_gathered,
     forward,
     forward_fp8,
     forward_fused,

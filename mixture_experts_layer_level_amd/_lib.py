@@ -78,6 +78,8 @@ def _load():
     L.moe_fused_error_offset.argtypes = [P, ctypes.c_int32, ctypes.POINTER(sz)]
     L.moe_route_mlp.restype = ctypes.c_int
     L.moe_route_mlp.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_up_gelu_gathered.restype = ctypes.c_int
+    L.moe_expert_up_gelu_gathered.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_up_gelu.restype = ctypes.c_int
     L.moe_expert_up_gelu.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.moe_expert_down_bias.restype = ctypes.c_int
@@ -284,6 +286,13 @@ def expert_up_gelu(p, x_perm, offsets, w1, b1, h, stream=None):
     _check("moe_expert_up_gelu", lib.moe_expert_up_gelu(ctypes.byref(p), _ptr(x_perm),
                                                         _ptr(offsets), _ptr(w1), _ptr(b1),
                                                         _ptr(h), _stream(stream)))
+
+
+def expert_up_gelu_gathered(p, x, row_token, offsets, w1, b1, h, stream=None):
+    _check("moe_expert_up_gelu_gathered",
+           lib.moe_expert_up_gelu_gathered(ctypes.byref(p), _ptr(x), _ptr(row_token),
+                                           _ptr(offsets), _ptr(w1), _ptr(b1), _ptr(h),
+                                           _stream(stream)))
 
 
 def expert_down_bias(p, h, offsets, w2, b2, out_perm, stream=None):

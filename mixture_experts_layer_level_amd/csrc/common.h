@@ -101,6 +101,10 @@ hipError_t launch_grouped_ffn_fp8(const Dims& d, const uint16_t* x_perm, const i
 hipError_t launch_expert_up_gelu(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                  const uint16_t* w1, const float* b1, uint16_t* h,
                                  hipStream_t s);
+hipError_t launch_expert_up_gelu_gathered(const Dims& d, const uint16_t* x,
+                                          const int32_t* row_token, const int32_t* offsets,
+                                          const uint16_t* w1, const float* b1, uint16_t* h,
+                                          hipStream_t s);
 hipError_t launch_expert_down_bias(const Dims& d, const uint16_t* h, const int32_t* offsets,
                                    const uint16_t* w2, const float* b2, uint16_t* out_perm,
                                    hipStream_t s);

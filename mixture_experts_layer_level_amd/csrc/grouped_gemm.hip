@@ -1762,6 +1762,16 @@ hipError_t launch_expert_up_gelu(const Dims& d, const uint16_t* x_perm, const in
       d, GemmArgs{x_perm, w1, nullptr, h, offsets, d.E, d.D, d.F, 0, nullptr, nullptr, b1}, s);
 }
 
+hipError_t launch_expert_up_gelu_gathered(const Dims& d, const uint16_t* x,
+                                          const int32_t* row_token, const int32_t* offsets,
+                                          const uint16_t* w1, const float* b1, uint16_t* h,
+                                          hipStream_t s) {
+  if (!gateup_gather_supported(d)) return hipErrorNotSupported;
+  return launch_gemm<kEpiBiasGelu, false>(
+      d, GemmArgs{x, w1, nullptr, h, offsets, d.E, d.D, d.F, 0, nullptr, nullptr, b1, row_token},
+      s);
+}
+
 hipError_t launch_expert_down_bias(const Dims& d, const uint16_t* h, const int32_t* offsets,
                                    const uint16_t* w2, const float* b2, uint16_t* out_perm,
                                    hipStream_t s) {

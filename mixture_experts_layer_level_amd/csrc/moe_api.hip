@@ -551,6 +551,24 @@ moe_status moe_expert_up_gelu(const moe_problem* p, const uint16_t* x_perm,
                                           static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_expert_up_gelu_gathered(const moe_problem* p, const uint16_t* x,
+                                       const int32_t* row_token, const int32_t* expert_offsets,
+                                       const uint16_t* w1, const float* b1, uint16_t* h,
+                                       void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !row_token || !expert_offsets || !w1 || !b1 || !h) return MOE_ERR_INVALID_ARG;
+  if (d.padded || (uint64_t)d.N * d.D * 2 >= (1ull << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(b1) || !aligned16(h))
+    return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  if (!gateup_gather_supported(d)) return MOE_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_up_gelu_gathered(d, x, row_token, expert_offsets, w1, b1, h,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_expert_down_bias(const moe_problem* p, const uint16_t* h,
                                 const int32_t* expert_offsets, const uint16_t* w2,
                                 const float* b2, uint16_t* out_perm, void* stream) {
@@ -602,7 +620,7 @@ moe_status moe_forward_gelu(const moe_problem* p, const uint16_t* x, const uint1
                        aligned16(w1) && aligned16(b1) && aligned16(w2) && aligned16(b2);
   if (present && aligned && x && y && d.D % 256 != 0) return MOE_ERR_UNSUPPORTED;
   return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
-                      expert_offsets, ws, ws_bytes, stream, kNoGather,
+                      expert_offsets, ws, ws_bytes, stream, kGatherBf16,
                       [&](const Dims& dd, float* lg, int32_t* ids, float* w, char* base,
                           const ForwardWs& L, hipStream_t s) {
                         return launch_route_mlp(dd, x, w_proj, b_proj, w_out, b_out,
@@ -610,8 +628,16 @@ moe_status moe_forward_gelu(const moe_problem* p, const uint16_t* x, const uint1
                                                 reinterpret_cast<int32_t*>(base + L.roff), lg,
                                                 ids, w, s);
                       },
-                      [&](const Dims& dd, const uint16_t* xp, const int32_t*,
+                      [&](const Dims& dd, const uint16_t* xp, const int32_t* rt,
                           const int32_t* offs, uint16_t* op, void* fws, hipStream_t s) {
+                        if (rt) {
+                          uint16_t* h = static_cast<uint16_t*>(fws);
+                          const hipError_t e =
+                              launch_expert_up_gelu_gathered(dd, xp, rt, offs, w1, b1, h, s);
+                          return e != hipSuccess
+                                     ? e
+                                     : launch_expert_down_bias(dd, h, offs, w2, b2, op, s);
+                        }
                         return launch_grouped_ffn_gelu(dd, xp, offs, w1, b1, w2, b2, op, nullptr,
                                                        fws, s);
                       });

@@ -134,6 +134,10 @@ def test_staged_argument_errors():
     assert g8(big, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0) == INVALID
     assert g8(ctypes.byref(P(N=4096, cn=5, cd=4)), *([FAKE] * 8), 0) == UNSUPPORTED
     assert g8(bp, *([FAKE] * 8), 0) == UNSUPPORTED                  # D = 256
+    gl = L.moe_expert_up_gelu_gathered
+    assert gl(big, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0) == INVALID
+    assert gl(ctypes.byref(P(N=4096, cn=5, cd=4)), *([FAKE] * 6), 0) == UNSUPPORTED
+    assert gl(bp, *([FAKE] * 6), 0) == UNSUPPORTED
     # every entry point accepts N = 0 without launching
     z = ctypes.byref(P(N=0))
     assert L.moe_route(z, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, 0) == OK
@@ -142,6 +146,7 @@ def test_staged_argument_errors():
     assert L.moe_expert_gateup(z, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == OK
     assert L.moe_expert_gateup_gathered(z, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == OK
     assert L.moe_expert_gateup_fp8_gathered(z, *([FAKE] * 8), 0) == OK
+    assert L.moe_expert_up_gelu_gathered(z, *([FAKE] * 6), 0) == OK
     assert L.moe_expert_down(z, FAKE, FAKE, FAKE, FAKE, 0) == OK
     assert L.moe_unpermute_combine(z, FAKE, FAKE, FAKE, FAKE, 0) == OK
 

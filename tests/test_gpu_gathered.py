@@ -15,7 +15,7 @@ import moe_synth as ms
 
 pytestmark = pytest.mark.gpu
 
-from gpu_layer import DEV, SMALL, Layer  # noqa: E402
+from gpu_layer import DEV, SMALL, GeluLayer, Layer  # noqa: E402
 import mixture_experts_layer_level_amd as moe  # noqa: E402
 
 UNSUPPORTED = 2
@@ -122,4 +122,38 @@ def test_gathered_gateup_fp8_full_size(name):
     h_ref, h = fp8_pair(L)
     assert same_bits(h, h_ref)
     del L, h_ref, h
+    torch.cuda.empty_cache()
+
+
+# GELU-expert layers: tiny (register-staged tiles, refused), about 240 and
+# 550 rows per expert (256 x 256 split-ring tiles), and the full-size layer
+GELU_CASES = {
+    "gelu_tiny": ms.CONFIGS["gelu_tiny"],
+    "g_mid": ms.MoEConfig("g_mid", N=960, D=512, E=8, K=2, F=320, gating="softmax", seed=203,
+                          expert="gelu"),
+    "g_large": ms.MoEConfig("g_large", N=1100, D=256, E=2, K=1, F=192, gating="softmax",
+                            seed=204, expert="gelu"),
+    "gelu_mlp": ms.CONFIGS["gelu_mlp"],
+}
+
+
+@pytest.mark.parametrize("name", list(GELU_CASES))
+def test_gathered_up_gelu(name):
+    cfg = GELU_CASES[name]
+    print(f"[gathered gelu] {name} N={cfg.N} D={cfg.D} E={cfg.E} K={cfg.K} F={cfg.F}", flush=True)
+    L = GeluLayer(cfg)
+    L.staged()
+    i = L.inp
+    h = torch.full_like(L.h, float("nan"))
+    call = lambda: moe.expert_up_gelu_gathered(L.p, i["x"], L.row_token, L.offsets, i["w1"],
+                                               i["b1"], h)
+    if not has_gathered_tiles(cfg):
+        with pytest.raises(moe.MoEError) as err:
+            call()
+        assert err.value.status == UNSUPPORTED
+        return
+    call()
+    torch.cuda.synchronize()
+    assert same_bits(h, L.h)
+    del L, h
     torch.cuda.empty_cache()

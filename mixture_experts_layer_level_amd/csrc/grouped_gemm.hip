@@ -1618,6 +1618,8 @@ hipError_t launch_split(const Dims& d, const GemmArgs& a0, hipStream_t s) {
 
 template <int BM, int BN, int WM, int WN, int EPI, bool FP8>
 hipError_t launch_regs(const Dims& d, const GemmArgs& a0, int occupancy, hipStream_t s) {
+  // these tiles read A rows in place: a gathered A would be read as x_perm
+  if (a0.gather) return hipErrorNotSupported;
   const GemmArgs a = with_tiles<BN, EPI == kEpiSwiglu>(a0);
   hipLaunchKernelGGL((grouped_gemm_regs<BM, BN, WM, WN, EPI, FP8>),
                      dim3((unsigned)grid_size<BM>(d, a.n_tiles, occupancy)), dim3(64 * WM * WN),

@@ -43,10 +43,13 @@ What it computes, step by step, in the order and notation of the pages:
   their dequantised values [zoe.im 第四层 DeepGEMM & MegaMoE Kernel (FP8
   weights); jsqmd.com 5.3 技巧2 (8-bit expert weights, dequantised for use)].
 
-Precision: every sum is taken in float64.  Values are rounded only where the
-layer stores them: logits and router weights to fp32, and the bf16 tensors
-``h`` (FFN intermediate), ``out_perm`` (FFN output rows) and ``y`` (layer
-output) to bf16 with round-to-nearest-even.  Top-K is decided on fp32 keys.
+Precision: every sum is taken in float64.  Values are rounded where the GPU
+holds or stores them: the logits, the gate and up pre-activations g and u,
+the product silu(g) * u, the down dot and the combine sum to fp32 (the GPU's
+arithmetic type), and then the bf16 tensors ``h`` (FFN intermediate),
+``out_perm`` (FFN output rows) and ``y`` (layer output) to bf16, each with
+round-to-nearest-even; the router weights are computed in float64 and rounded
+to fp32.  Top-K is decided on fp32 keys.
 
 Readings where the pages are silent:
 ties in top-K go to the lower expert id, -0.0 equals +0.0 and NaN keys sort
@@ -98,6 +101,11 @@ def f64_to_bf16_bits(v) -> np.ndarray:
 
 def round_f32(v) -> np.ndarray:
     return np.asarray(v, dtype=np.float64).astype(np.float32)
+
+
+def _f32(v) -> np.ndarray:
+    """fp32 rounding of float64 values, kept as float64 (IEEE nearest even)."""
+    return round_f32(v).astype(np.float64)
 
 
 # --------------------------------------------------------------------------
@@ -262,17 +270,18 @@ def silu(g):
 def swiglu_rows(a, wg_bits, wu_bits, wd_bits):
     """One expert's FFN on rows a [m, D] (float64 values).
 
-    g = a Wg^T, u = a Wu^T (float64); h = bf16(silu(g) * u);
-    out = bf16(h Wd^T).  Wg, Wu are [F, D] and Wd is [D, F] (nn.Linear layout).
-    Returns (h, out) as float64 arrays holding bf16 values.
+    g = fl32(a Wg^T), u = fl32(a Wu^T) (float64 sums rounded to fp32);
+    h = bf16(fl32(silu(g) * u)); out = bf16(fl32(h Wd^T)).  Wg, Wu are [F, D]
+    and Wd is [D, F] (nn.Linear layout).  Returns (h, out) as float64 arrays
+    holding bf16 values.
     """
     wg = bf16_to_f64(wg_bits)
     wu = bf16_to_f64(wu_bits)
     wd = bf16_to_f64(wd_bits)
-    g = a @ wg.T
-    u = a @ wu.T
-    h = round_bf16(silu(g) * u)
-    out = round_bf16(h @ wd.T)
+    g = _f32(a @ wg.T)
+    u = _f32(a @ wu.T)
+    h = round_bf16(_f32(silu(g) * u))
+    out = round_bf16(_f32(h @ wd.T))
     return h, out
 
 
@@ -301,7 +310,7 @@ def expert_ffn(x_perm_bits, offsets, w_gate_bits, w_up_bits, w_down_bits):
 
 
 def combine(out_perm, slot_row, topk_w) -> np.ndarray:
-    """y[n] = bf16( sum_k w[n,k] * out_perm[slot_row[n*K+k]] ), k ascending, kept slots only.
+    """y[n] = bf16(fl32( sum_k w[n,k] * out_perm[slot_row[n*K+k]] )), k ascending, kept slots only.
 
     zoe.im 范式 A Step 3: restore token order and multiply by the router
     weights; the opening dataflow then sums the K weighted results.
@@ -315,7 +324,7 @@ def combine(out_perm, slot_row, topk_w) -> np.ndarray:
         rows = sr[:, k]
         kept = rows >= 0
         y[kept] += w[kept, k][:, None] * op[rows[kept]]
-    return round_bf16(y)
+    return round_bf16(_f32(y))
 
 
 # --------------------------------------------------------------------------
@@ -370,7 +379,7 @@ def token_outputs(x_bits, topk_ids, topk_w, kept_mask, expert_weights, rows_fn=N
     y = np.zeros((n, D))
     for k in range(K):
         y += np.where(np.asarray(kept_mask)[:, k:k + 1], w[:, k:k + 1] * outs[:, k], 0.0)
-    return round_bf16(y), outs
+    return round_bf16(_f32(y)), outs
 
 
 # --------------------------------------------------------------------------
@@ -558,7 +567,7 @@ def mlp_router_features(x_bits, w_proj_bits, b_proj) -> np.ndarray:
     x = bf16_to_f64(x_bits)
     w = bf16_to_f64(w_proj_bits)
     b = np.asarray(b_proj, dtype=np.float32).astype(np.float64)
-    return round_bf16(gelu(x @ w.T + b))
+    return round_bf16(_f32(gelu(_f32(_f32(x @ w.T) + b))))
 
 
 def mlp_router_logits(a, w_out) -> np.ndarray:
@@ -570,14 +579,16 @@ def mlp_router_logits(a, w_out) -> np.ndarray:
 
 
 def gelu_ffn_rows(a, w1_bits, b1, w2_bits, b2):
-    """One GELU expert on rows a [m, D]: h = bf16(GELU(a W1^T + b1)),
-    out = bf16(h W2^T + b2); W1 [F, D], W2 [D, F] (nn.Linear layout)."""
+    """One GELU expert on rows a [m, D]: h = bf16(fl32(GELU(v))) with
+    v = fl32(fl32(a W1^T) + b1), out = bf16(fl32(fl32(h W2^T) + b2)); W1 [F, D],
+    W2 [D, F] (nn.Linear layout).  fl32 marks the fp32 roundings of the GPU's
+    arithmetic: the dot, the bias add, the activation."""
     w1 = bf16_to_f64(w1_bits)
     w2 = bf16_to_f64(w2_bits)
     b1 = np.asarray(b1, dtype=np.float32).astype(np.float64)
     b2 = np.asarray(b2, dtype=np.float32).astype(np.float64)
-    h = round_bf16(gelu(a @ w1.T + b1))
-    out = round_bf16(h @ w2.T + b2)
+    h = round_bf16(_f32(gelu(_f32(_f32(a @ w1.T) + b1))))
+    out = round_bf16(_f32(_f32(h @ w2.T) + b2))
     return h, out
 
 

@@ -4,24 +4,39 @@
 One step = the whole layer on one batch: router GEMM + top-K gating, permute
 into expert segments, grouped gate/up GEMM with SwiGLU, grouped down GEMM,
 unpermute + weighted combine -- the five libmoe calls moe_forward is made of,
-issued separately so the dominant kernel (the gate/up grouped GEMM) can be
-bracketed with HIP events on the stream it runs on.  Inputs are synthetic,
-seeded and already resident in HBM when timing starts.
+issued separately so that every stage, and the dominant kernel (the gate/up
+grouped GEMM), can be bracketed with HIP events on the stream it runs on.
+Inputs are synthetic, seeded and already resident in HBM when timing starts.
 
-``--config gelu_mlp`` runs the pages' other layer: an MLP router
-(Linear(D, D/4) + GELU, then the gate Linear) and experts
-Linear(D, 4D) - GELU - Linear(4D, D) with biases; its dominant kernel is the
-up GEMM with the bias + GELU epilogue.
+Timing: W untimed warm-up steps, then K timed steps.  Before every timed step
+512 MiB of scratch are written outside its events (twice the 256 MB
+memory-side cache), so no activation or weight of the previous step is still
+cached: ``ms_per_step`` is the mean of the K cold steps.  K more steps run
+back to back afterwards and give ``warm_ms_per_step``.
 
-With ``--weights fp8`` the expert weights are stored as block-scaled FP8
-(E4M3 codes, one power-of-two scale per 32 values; quantised once before
-timing) and the two grouped GEMMs read them through the FP8 entry points.
+The headline workload is the DeepSeek-V3 layer shape (N=8192, D=7168,
+E=256, K=8, F=2048, sigmoid gating).  The other workloads -- the Qwen3 decode
+step, the hot-expert skew (contiguous and capacity-padded) and the Mixtral
+shape -- run after it in the same process and are reported under
+``workloads``, each with its own roofline of its dominant kernel.
+``cpu_baseline`` is the C++ oracle on a bounded sample of the headline
+workload's tokens, on the host's cores.
 
-Prints one JSON line.  ``value`` is tokens/s of the layer on this GPU.
+``--config gelu_mlp`` runs the pages' other layer (MLP router, GELU experts);
+``--weights fp8`` reads block-scaled FP8 expert weights; ``--fused`` runs the
+expert FFN as one persistent launch.
+
+Also: ``--trace-summary DIR`` and ``--pmc-summary ...`` turn rocprofv3 output
+of a profiled run of this script into the tables kept under profiles/.
+
+Prints one JSON line.  ``value`` is tokens/s of the headline layer on this GPU.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -31,13 +46,22 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_level_amd", "csrc", "grouped_gemm.hip")
+FLUSH_BYTES = 512 << 20
+DEFAULT_EXTRA = "qwen3_decode,hot_skew,hot_skew:padded,mixtral"
+# tokens of the CPU-oracle sample per workload (about 10-30 s of CPU work on
+# 16 host cores for the C++ oracle)
+CPU_TOKENS = {"deepseek_v3": 2048, "mixtral": 512, "hot_skew": 1024, "qwen3_decode": 64,
+              "tiny": 64, "gelu_mlp": 256, "gelu_tiny": 64}
+
+
+def source_sha() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per gate/up launch from the committed rocprofv3 --pmc summary of
-    this workload, or None when there is none or the kernel source has changed
-    since the counters were taken."""
-    import hashlib
+    """HBM bytes per gate/up launch from the committed rocprofv3 --pmc summary
+    of this workload, or None when there is none or the kernel source has
+    changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -47,67 +71,51 @@ def measured_traffic(workload: str):
             rec = json.loads(line[len("traffic: "):])
     if rec is None:
         return None
-    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-    return rec["bytes"] if rec.get("source_sha256") == sha else None
+    return rec["bytes"] if rec.get("source_sha256") == source_sha() else None
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mixtral",
-                    help="tiny | mixtral | deepseek_v3 | qwen3_decode | hot_skew | gelu_mlp | "
-                         "gelu_tiny")
-    ap.add_argument("--padded", action="store_true", help="capacity-padded layout (hot_skew)")
-    ap.add_argument("--fused", action="store_true",
-                    help="the expert FFN as one persistent launch (moe_fused_ffn; rows gathered "
-                         "from x, no permuted copy)")
-    ap.add_argument("--xperm", action="store_true",
-                    help="write the permuted copy of x and run the first expert GEMM on it; by "
-                         "default that GEMM reads its rows of x through row_token "
-                         "(moe_expert_gateup_gathered, moe_expert_gateup_fp8_gathered, "
-                         "moe_expert_up_gelu_gathered) wherever the library takes the shape")
-    ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
-                    help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
-                    help="tokens of the CPU-oracle sample, at most the workload's N (0 = skip "
-                         "the CPU baseline); the oracle's fixed cost (weights to float64) "
-                         "dominates small samples")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="only run a plain device-to-device copy of this many MiB, three "
-                         "times (the reference kernel for HBM byte counters), then exit")
-    args = ap.parse_args()
-    if args.calib_copy_mib > 0:
-        calib_copy(args.calib_copy_mib)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              f"(the library has no multi-GPU path)", file=sys.stderr)
-        sys.exit(2)
+def roofline(flop, nbytes, ms):
+    """Bound of a kernel from its algorithmic work, and what it achieved."""
+    t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+    if t_mfma >= t_hbm:
+        r = {"bound": "mfma", "achieved": flop / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s"}
+    else:
+        r = {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
+             "unit": "GB/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    return r
 
+
+class Opts:
+    def __init__(self, padded=False, fused=False, xperm=False, weights="bf16"):
+        self.padded, self.fused, self.xperm, self.weights = padded, fused, xperm, weights
+
+
+def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
+    """Build the layer's inputs on the GPU, time it, return (result dict,
+    inputs).  The result holds the cold step time, the warm one, the stage
+    times and the roofline of the dominant kernel."""
     import numpy as np
     import torch
 
     import mixture_experts_layer_level_amd as moe
     import moe_synth as ms
 
-    cfg = ms.CONFIGS[args.config]
     dev = "cuda"
-    torch.cuda.set_device(0)
-    cap = cfg.capacity if args.padded else None
-    if args.padded and cap is None:
+    cap = cfg.capacity if o.padded else None
+    if o.padded and cap is None:
         raise SystemExit(f"{cfg.name} has no capacity factor")
     gelu = cfg.expert == "gelu"
-    if args.fused and (gelu or args.weights != "bf16" or args.padded):
+    if o.fused and (gelu or o.weights != "bf16" or o.padded):
         raise SystemExit("--fused runs the SwiGLU layer, bf16 weights, contiguous layout")
-    if gelu and args.weights != "bf16":
+    if gelu and o.weights != "bf16":
         raise SystemExit("the GELU-expert layer runs with bf16 weights")
     t0 = time.time()
     inp = ms.make_gelu_inputs(cfg, device=dev) if gelu else ms.make_inputs(cfg, device=dev)
     torch.cuda.synchronize()
-    print(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s", file=sys.stderr,
-          flush=True)
+    log(f"inputs {cfg.name} generated in {time.time() - t0:.1f}s")
     p = moe.problem(cfg.N, cfg.D, cfg.F, cfg.E, cfg.K, cfg.gating, cap)
     R, capv = moe.permuted_rows(p)
     N, D, E, K, F = cfg.N, cfg.D, cfg.E, cfg.K, cfg.F
@@ -115,7 +123,7 @@ def main():
     logits, ids, w = e(N, E), e(N, K, dt=torch.int32), e(N, K)
     counts, offsets = e(E, dt=torch.int32), e(E + 1, dt=torch.int32)
     row_token, slot_row = e(R, dt=torch.int32), e(N * K, dt=torch.int32)
-    x_perm, h = e(R, D, dt=torch.bfloat16), e(R, F, dt=torch.bfloat16)
+    h = e(R, F, dt=torch.bfloat16)
     out_perm, y = e(R, D, dt=torch.bfloat16), e(N, D, dt=torch.bfloat16)
     ws = torch.empty(moe.workspace_size(p), dtype=torch.uint8, device=dev)
     x = inp["x"]
@@ -125,7 +133,7 @@ def main():
         wr, bias = inp["w_router"], inp["bias"]
         wg, wu, wd = inp["w_gate"], inp["w_up"], inp["w_down"]
     stream = torch.cuda.current_stream()
-    fp8 = args.weights == "fp8"
+    fp8 = o.weights == "fp8"
     if fp8:
         def quant(wt):
             rows, cols = wt.shape[-2], wt.shape[-1]
@@ -137,83 +145,24 @@ def main():
         qg, qu, qd = quant(wg), quant(wu), quant(wd)
         torch.cuda.synchronize()
 
-    # The first expert GEMM (gate/up, or the GELU layer's up GEMM) reads its rows of x through row_token
-    # wherever the library takes the shape; it refuses, before any launch, the
-    # shapes whose tiles have no gathered form.  One route + permute first, so
-    # that the trial call runs on real routing tables.
-    gather = not (args.xperm or args.fused or capv)
-    if gather:
-        if gelu:
-            moe.route_mlp(p, x, inp["w_proj"], inp["b_proj"], inp["w_out"], inp["b_out"], logits,
-                          ids, w, ws, features=feats, stream=stream)
-        else:
-            moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
-        moe.permute(p, x, ids, counts, offsets, row_token, slot_row, None, ws, stream=stream)
-        try:
-            if gelu:
-                moe.expert_up_gelu_gathered(p, x, row_token, offsets, inp["w1"], inp["b1"], h,
-                                            stream=stream)
-            elif fp8:
-                moe.expert_gateup_fp8_gathered(p, x, row_token, offsets, qg, qu, h, stream=stream)
-            else:
-                moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=stream)
-        except moe.MoEError as err:
-            if err.status != 2:   # MOE_ERR_UNSUPPORTED: run the permuted copy instead
-                raise
-            gather = False
-        torch.cuda.synchronize()
+    # The first expert GEMM reads its rows of x through row_token wherever the
+    # library takes the shape; it refuses, before any launch, the shapes whose
+    # tiles have no gathered form.  The trial call runs one whole step.
+    gather = not (o.xperm or o.fused or capv)
+    x_perm = None if gather else e(R, D, dt=torch.bfloat16)
 
-    # ev: six events per step, recorded on the launch stream before the route
-    # and after the route, permute, gate/up (or up, or fused FFN), down and
-    # combine calls
     def rec(ev, i):
         if ev is not None:
             ev[i].record(stream)
 
-    def step_gelu(ev=None):
-        i = inp
-        rec(ev, 0)
-        moe.route_mlp(p, x, i["w_proj"], i["b_proj"], i["w_out"], i["b_out"], logits, ids, w, ws,
-                      features=feats, stream=stream)
-        rec(ev, 1)
-        moe.permute(p, x, ids, counts, offsets, row_token, slot_row,
-                    None if gather else x_perm, ws, stream=stream)
-        rec(ev, 2)
-        if gather:
-            moe.expert_up_gelu_gathered(p, x, row_token, offsets, i["w1"], i["b1"], h,
-                                        stream=stream)
-        else:
-            moe.expert_up_gelu(p, x_perm, offsets, i["w1"], i["b1"], h, stream=stream)
-        rec(ev, 3)
-        moe.expert_down_bias(p, h, offsets, i["w2"], i["b2"], out_perm, stream=stream)
-        rec(ev, 4)
-        moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
-        rec(ev, 5)
-
-    def step_fused(ev=None):
-        rec(ev, 0)
-        moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
-        rec(ev, 1)
-        moe.permute(p, x, ids, counts, offsets, row_token, slot_row, None, ws, stream=stream)
-        rec(ev, 2)
-        moe.fused_ffn(p, x, row_token, offsets, wg, wu, wd, out_perm, ws, stream=stream)
-        rec(ev, 3)
-        rec(ev, 4)
-        moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
-        rec(ev, 5)
-
-    def step(ev=None):
+    def gateup():
         if gelu:
-            return step_gelu(ev)
-        if args.fused:
-            return step_fused(ev)
-        rec(ev, 0)
-        moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
-        rec(ev, 1)
-        moe.permute(p, x, ids, counts, offsets, row_token, slot_row,
-                    None if gather else x_perm, ws, stream=stream)
-        rec(ev, 2)
-        if gather and fp8:
+            if gather:
+                moe.expert_up_gelu_gathered(p, x, row_token, offsets, inp["w1"], inp["b1"], h,
+                                            stream=stream)
+            else:
+                moe.expert_up_gelu(p, x_perm, offsets, inp["w1"], inp["b1"], h, stream=stream)
+        elif gather and fp8:
             moe.expert_gateup_fp8_gathered(p, x, row_token, offsets, qg, qu, h, stream=stream)
         elif gather:
             moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=stream)
@@ -221,37 +170,90 @@ def main():
             moe.expert_gateup_fp8(p, x_perm, offsets, qg, qu, h, stream=stream)
         else:
             moe.expert_gateup(p, x_perm, offsets, wg, wu, h, stream=stream)
-        rec(ev, 3)
-        if fp8:
-            moe.expert_down_fp8(p, h, offsets, qd, out_perm, stream=stream)
+
+    # ev: six events per step, recorded on the launch stream before the route
+    # and after the route, permute, gate/up (or fused FFN), down and combine
+    def step(ev=None):
+        rec(ev, 0)
+        if gelu:
+            moe.route_mlp(p, x, inp["w_proj"], inp["b_proj"], inp["w_out"], inp["b_out"],
+                          logits, ids, w, ws, features=feats, stream=stream)
         else:
-            moe.expert_down(p, h, offsets, wd, out_perm, stream=stream)
+            moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
+        rec(ev, 1)
+        moe.permute(p, x, ids, counts, offsets, row_token, slot_row,
+                    None if (gather or o.fused) else x_perm, ws, stream=stream)
+        rec(ev, 2)
+        if o.fused:
+            moe.fused_ffn(p, x, row_token, offsets, wg, wu, wd, out_perm, ws, stream=stream)
+            rec(ev, 3)
+        else:
+            gateup()
+            rec(ev, 3)
+            if gelu:
+                moe.expert_down_bias(p, h, offsets, inp["w2"], inp["b2"], out_perm,
+                                     stream=stream)
+            elif fp8:
+                moe.expert_down_fp8(p, h, offsets, qd, out_perm, stream=stream)
+            else:
+                moe.expert_down(p, h, offsets, wd, out_perm, stream=stream)
         rec(ev, 4)
         moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
         rec(ev, 5)
 
-    for _ in range(args.warmup):
+    if gather:
+        try:
+            step()
+        except moe.MoEError as err:
+            if err.status != 2:   # MOE_ERR_UNSUPPORTED: run the permuted copy instead
+                raise
+            gather = False
+            x_perm = e(R, D, dt=torch.bfloat16)
+            step()
+    else:
+        step()
+    torch.cuda.synchronize()
+    pre_steps = 1 + warmup            # whole steps before the timed ones (for trace summaries)
+
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6))
-           for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    # timed: every step cold, each preceded by a 512 MiB scratch write
+    # outside its events
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6)) for _ in range(steps)]
     torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
+    t_wall = time.perf_counter()
+    for i in range(steps):
+        scratch.zero_()
         step(evs[i])
-    stop.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
+    wall_s = time.perf_counter() - t_wall
+    del scratch
+    if o.fused:
+        off = moe.fused_error_offset(p, whole_layer=False)
+        err_word = int(ws[off:off + 4].view(torch.int32).item())
+        if err_word != 0:
+            raise SystemExit(f"fused FFN: a bounded wait ran out during the timed steps "
+                             f"(error word {err_word}); its results are wrong")
 
     def stage_ms(i, j):
-        return sum(ev[i].elapsed_time(ev[j]) for ev in evs) / args.steps
+        return sum(ev[i].elapsed_time(ev[j]) for ev in evs) / steps
+    per_step = sorted(ev[0].elapsed_time(ev[5]) for ev in evs)
+    ms_step = sum(per_step) / steps
     route_ms, permute_ms = stage_ms(0, 1), stage_ms(1, 2)
     gateup_ms, down_ms, combine_ms = stage_ms(2, 3), stage_ms(3, 4), stage_ms(4, 5)
-    per_step = sorted(ev[0].elapsed_time(ev[5]) for ev in evs)
+
+    warm_ms = None
+    if warm_steps > 0:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(warm_steps):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        warm_ms = a.elapsed_time(b) / warm_steps
 
     counts_h = counts.cpu().numpy().astype(np.int64)
     kept = int(np.minimum(counts_h, capv).sum()) if capv else cfg.S
@@ -264,52 +266,45 @@ def main():
         flops = 2.0 * N * D * E + 6.0 * D * F * kept
     tflops = flops / (ms_step * 1e-3) / 1e12
     weight_bytes = nmat * touched * F * D * wb
-    # the dominant kernel (gate/up grouped GEMM; up GEMM of the GELU experts):
-    # algorithmic work per launch
+    # dominant kernel: the gate/up grouped GEMM (the GELU experts' up GEMM),
+    # algorithmic work per launch: touched experts' weights once, the kept
+    # rows of x read once, h written once
     gu_mats = nmat - 1
     gu_flops = 2.0 * gu_mats * D * F * kept
-    gu_bytes = gu_mats * touched * F * D * wb + kept * D * 2 + kept * F * 2   # weights, x_perm, h
-    t_mfma = gu_flops / (PEAK_BF16_TFLOPS * 1e12)
-    t_hbm = gu_bytes / (PEAK_HBM_GBPS * 1e9)
-    if t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": gu_flops / (gateup_ms * 1e-3) / 1e12,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": gu_bytes / (gateup_ms * 1e-3) / 1e9,
-                "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(args.config + ("_padded" if capv else "") +
-                                       ("_fp8" if fp8 else "") + ("_xperm" if args.xperm else ""))
-    roof["kernel"] = (("grouped up GEMM + bias + GELU" if gelu
-                       else "grouped gate/up GEMM + SwiGLU") +
-                      (", rows gathered from x through row_token" if gather else ""))
-    if args.fused:
+    gu_bytes = gu_mats * touched * F * D * wb + kept * D * 2 + kept * F * 2
+    suffix = ("_padded" if capv else "") + ("_fp8" if fp8 else "") + \
+             ("_xperm" if o.xperm else "")
+    if o.fused:
         # the one fused launch: gate/up, SwiGLU and down of every expert
         f_flops = 6.0 * D * F * kept
         f_bytes = 3.0 * touched * F * D * 2 + kept * D * 2 * 2 + kept * F * 2 * 2
-        t_m, t_h = f_flops / (PEAK_BF16_TFLOPS * 1e12), f_bytes / (PEAK_HBM_GBPS * 1e9)
-        if t_m >= t_h:
-            roof = {"bound": "mfma", "achieved": f_flops / (gateup_ms * 1e-3) / 1e12,
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-        else:
-            roof = {"bound": "hbm", "achieved": f_bytes / (gateup_ms * 1e-3) / 1e9,
-                    "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
-        roof["frac"] = roof["achieved"] / roof["peak"]
-        roof["traffic"] = measured_traffic(args.config + "_fused")
+        roof = roofline(f_flops, f_bytes, gateup_ms)
+        roof["traffic"] = measured_traffic(cfg.name + "_fused")
         roof["kernel"] = "fused expert FFN (gate/up + SwiGLU + down, one launch)"
         roof["algorithmic"] = {"flop": f_flops, "bytes": f_bytes}
+    else:
+        roof = roofline(gu_flops, gu_bytes, gateup_ms)
+        roof["traffic"] = measured_traffic(cfg.name + suffix)
+        roof["kernel"] = (("grouped up GEMM + bias + GELU" if gelu
+                           else "grouped gate/up GEMM + SwiGLU") +
+                          (", rows gathered from x through row_token" if gather else ""))
+        roof["algorithmic"] = {"flop": gu_flops, "bytes": gu_bytes,
+                               "per_unit": "per kept slot: %d flop, %d bytes of its row and h; "
+                                           "per touched expert: %d weight bytes"
+                                           % (2 * gu_mats * D * F, D * 2 + F * 2,
+                                              gu_mats * F * D * wb)}
     roof["avg_ms"] = gateup_ms
-    roof.setdefault("algorithmic", {"flop": gu_flops, "bytes": gu_bytes})
-    # the HBM-bound stages against 8 TB/s: permute (x read once, x_perm rows
-    # written, ids read, row_token and slot_row written, offsets), combine
-    # (out_perm rows read, y written, slot_row and weights read)
+    # the HBM-bound stages against 8 TB/s: permute (x read once and x_perm
+    # rows written, when the copy is made; ids read, row_token and slot_row
+    # written, offsets), combine (kept out_perm rows read, y written,
+    # slot_row and weights read)
     S_ = N * K
     perm_bytes = (S_ * 4 * 3 + (E + 1) * 4 +
-                  (0 if args.fused or gather else N * D * 2 + R * D * 2))
+                  (0 if (o.fused or gather) else N * D * 2 + R * D * 2))
     comb_bytes = kept * D * 2 + N * D * 2 + S_ * 8
     stages = {
-        "route_ms": route_ms, "permute_ms": permute_ms, "ffn_ms": gateup_ms + down_ms,
-        "combine_ms": combine_ms,
+        "route_ms": route_ms, "permute_ms": permute_ms, "gateup_ms": gateup_ms,
+        "down_ms": down_ms, "ffn_ms": gateup_ms + down_ms, "combine_ms": combine_ms,
         "permute_gbps": perm_bytes / (permute_ms * 1e-3) / 1e9,
         "permute_frac_hbm": perm_bytes / (permute_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "combine_gbps": comb_bytes / (combine_ms * 1e-3) / 1e9,
@@ -324,19 +319,8 @@ def main():
         stages["kept_slots"] = kept
         stages["utilisation"] = kept / (E * capv)
         stages["executed_tflops"] = exec_flops / (ms_step * 1e-3) / 1e12
-    line = {
-        "metric": "MoE-layer tokens/sec + TFLOPS (% bf16 MFMA peak) / HBM GB/s (% peak), 1 GPU",
-        "value": N / (ms_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded counter-based draws, random-init weights)",
+    res = {
+        "workload": cfg.note + (" [capacity-padded]" if capv else ""),
         "config": {"workload": cfg.note + (" [capacity-padded]" if capv else ""),
                    "tokens": N, "hidden": D, "experts": E, "top_k": K, "ffn": F,
                    "gating": cfg.gating, "capacity": capv or None,
@@ -344,44 +328,151 @@ def main():
                                       if fp8 else "bf16"),
                    "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
                               else "SwiGLU"),
-                   "ffn_launch": ("fused (one persistent launch)" if args.fused else
-                                  "two grouped GEMMs, rows of the first gathered from x" if gather
-                                  else "two grouped GEMMs")},
+                   "ffn_launch": ("fused (one persistent launch)" if o.fused else
+                                  "two grouped GEMMs, rows of the first gathered from x"
+                                  if gather else "two grouped GEMMs")},
+        "value": N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_step": ms_step,
+        "warm_ms_per_step": warm_ms,
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "weight_stream_gbps": weight_bytes / (ms_step * 1e-3) / 1e9,
+        "pct_hbm_peak_weights": 100.0 * weight_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "ffn_weight_stream_gbps": weight_bytes / ((gateup_ms + down_ms) * 1e-3) / 1e9,
-        "gateup_ms": gateup_ms,
-        "down_ms": down_ms,
         "max_expert_rows": int(counts_h.max()),
         "dropped_slots": int(cfg.S - kept),
         "stages": stages,
         "roofline": roof,
-        "cpu_baseline": None,
+        "timed_wall_s": wall_s,
+        "pre_steps": pre_steps,
     }
-    print(f"[bench] {ms_step:.3f} ms/step, gate/up {gateup_ms:.3f} ms", file=sys.stderr,
-          flush=True)
+    log(f"{cfg.name}{suffix}: {ms_step:.3f} ms/step cold (warm {warm_ms or 0:.3f}), "
+        f"gate/up {gateup_ms:.3f} ms, down {down_ms:.3f} ms")
+    return res, inp
 
-    # Cold-cache steps, after the timed ones and outside them: before each,
-    # 512 MiB of scratch are written (twice the 256 MB memory-side cache), so
-    # no activation or weight of the previous step is still cached; each step
-    # is timed alone between events on the launch stream.
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold = []
-    for _ in range(5):
-        scratch.zero_()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        step()
-        c1.record(stream)
-        torch.cuda.synchronize()
-        cold.append(c0.elapsed_time(c1))
-    del scratch
-    line["cold_ms_per_step"] = sorted(cold)[len(cold) // 2]
 
-    if args.cpu_tokens > 0:
-        line["cpu_baseline"] = (cpu_baseline_gelu(cfg, inp, min(args.cpu_tokens, N)) if gelu else
-                                cpu_baseline(cfg, inp, min(args.cpu_tokens, N), capv, fp8))
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-steps", type=int, default=None,
+                    help="back-to-back steps after the timed cold ones (default: --steps; 0 = "
+                         "none)")
+    ap.add_argument("--config", default="deepseek_v3",
+                    help="tiny | mixtral | deepseek_v3 | qwen3_decode | hot_skew | gelu_mlp | "
+                         "gelu_tiny")
+    ap.add_argument("--extra", default=DEFAULT_EXTRA,
+                    help="workloads run after the headline one, reported under 'workloads' "
+                         "(comma-separated, name[:padded]; 'none' for none)")
+    ap.add_argument("--padded", action="store_true", help="capacity-padded layout (hot_skew)")
+    ap.add_argument("--fused", action="store_true",
+                    help="the expert FFN as one persistent launch (moe_fused_ffn; rows gathered "
+                         "from x, no permuted copy)")
+    ap.add_argument("--xperm", action="store_true",
+                    help="write the permuted copy of x and run the first expert GEMM on it; by "
+                         "default that GEMM reads its rows of x through row_token wherever the "
+                         "library takes the shape")
+    ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
+                    help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
+    ap.add_argument("--cpu-tokens", type=int, default=-1,
+                    help="tokens of the CPU-oracle sample (-1: a per-workload default of about "
+                         "10-30 s of CPU work; 0: skip the CPU baseline)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, three "
+                         "times (the reference kernel for HBM byte counters), then exit")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="only summarise the rocprofv3 kernel trace under DIR: per libmoe "
+                         "kernel, the launches of the timed steps (after --pre-steps whole "
+                         "steps, --steps of them); prints a markdown table")
+    ap.add_argument("--pre-steps", type=int, default=None,
+                    help="with --trace-summary: whole steps before the timed ones (the trial "
+                         "step plus the warm-up steps: 1 + --warmup of the profiled run)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                                                       "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="only summarise four rocprofv3 --pmc runs (the workload's FETCH_SIZE "
+                         "and WRITE_SIZE, then those of --calib-copy-mib 1024) into HBM bytes "
+                         "per launch; prints a markdown table and the traffic line")
+    ap.add_argument("--label", default=None, help="kernel label for --pmc-summary's traffic line")
+    args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.pre_steps, args.steps,
+                      args.steps if args.warm_steps is None else args.warm_steps)
+        return
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, label=args.label)
+        return
+    if args.calib_copy_mib > 0:
+        calib_copy(args.calib_copy_mib)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library "
+              f"runs one whole MoE layer per GPU and has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    warm_steps = args.steps if args.warm_steps is None else args.warm_steps
+
+    import torch
+
+    import mixture_experts_layer_level_amd as moe  # noqa: F401  (fails loudly without libmoe.so)
+    import moe_synth as ms
+
+    torch.cuda.set_device(0)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    cfg = ms.CONFIGS[args.config]
+    head, inp = run_layer(cfg, Opts(args.padded, args.fused, args.xperm, args.weights),
+                          args.steps, args.warmup, warm_steps, log)
+    line = {
+        "metric": "MoE-layer tokens/sec + TFLOPS (% bf16 MFMA peak) / HBM GB/s (% peak), 1 GPU",
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based draws, random-init weights)",
+        "config": head["config"],
+        "timing": "each timed step cold: 512 MiB scratch write outside its HIP events; "
+                  "warm_ms_per_step: the same steps back to back",
+    }
+    for k in ("warm_ms_per_step", "tflops", "pct_bf16_mfma_peak", "weight_stream_gbps",
+              "pct_hbm_peak_weights", "ffn_weight_stream_gbps", "max_expert_rows",
+              "dropped_slots", "stages", "roofline"):
+        line[k] = head[k]
+    line["cpu_baseline"] = None
+    ntok = CPU_TOKENS.get(cfg.name, 256) if args.cpu_tokens < 0 else args.cpu_tokens
+    if ntok > 0:
+        log(f"CPU oracle on {min(ntok, cfg.N)} tokens")
+        line["cpu_baseline"] = (cpu_baseline_gelu(cfg, inp, min(ntok, cfg.N))
+                                if cfg.expert == "gelu" else
+                                cpu_baseline(cfg, inp, min(ntok, cfg.N),
+                                             head["config"]["capacity"], args.weights == "fp8"))
+    del inp
+    torch.cuda.empty_cache()
+
+    extras = {}
+    if args.extra and args.extra != "none" and not (args.fused or args.weights != "bf16"):
+        for item in args.extra.split(","):
+            name, _, mode = item.partition(":")
+            if name == cfg.name and (mode == "padded") == args.padded:
+                continue
+            res, inp = run_layer(ms.CONFIGS[name], Opts(padded=mode == "padded"), args.steps,
+                                 args.warmup, warm_steps, log)
+            del inp
+            torch.cuda.empty_cache()
+            keep = ("workload", "value", "unit", "ms_per_step", "warm_ms_per_step", "tflops",
+                    "pct_bf16_mfma_peak", "weight_stream_gbps", "pct_hbm_peak_weights",
+                    "max_expert_rows", "dropped_slots", "stages", "roofline")
+            extras[name + ("_padded" if mode == "padded" else "")] = {k: res[k] for k in keep}
+    line["workloads"] = extras
     print(json.dumps(line), flush=True)
 
 
@@ -398,46 +489,6 @@ def calib_copy(mib: int):
     print(f"[calib] copied {n} bytes three times", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, inp, n, capv, fp8=False):
-    """The CPU oracle, as it stands, on the first n tokens of the same layer
-    (FP8 weights: quantised by the oracle before the timed run, as the GPU's
-    are before its timed steps)."""
-    import numpy as np
-    import torch
-    from threadpoolctl import threadpool_info
-
-    from oracle import moe_oracle as O
-
-    wbytes = 3 * cfg.E * cfg.F * cfg.D * 2
-    if wbytes > 8e9:
-        return {"value": None, "unit": "tokens/s", "cores": None, "kind": "oracle",
-                "sample": f"skipped: {wbytes / 1e9:.1f} GB of expert weights do not fit "
-                          f"the host-side oracle run"}
-
-    def b(t):
-        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-    x = b(inp["x"][:n])
-    wr = inp["w_router"].cpu().numpy()
-    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
-    wg, wu, wd = b(inp["w_gate"]), b(inp["w_up"]), b(inp["w_down"])
-    if fp8:
-        wg, wu, wd = (O.dequantize_fp8_bits(*O.quantize_fp8(m)) for m in (wg, wu, wd))
-    cap = None
-    if capv:
-        cap = O.capacity(n, cfg.K, cfg.E, *cfg.capacity)
-    t0 = time.perf_counter()
-    O.forward(x, wr, bias, wg, wu, wd, cfg.K, cfg.gating, cap=cap)
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    slots = n * cfg.K if cap is None else min(n * cfg.K, cfg.E * cap)
-    flop = 2.0 * n * cfg.D * cfg.E + 6.0 * cfg.D * cfg.F * slots
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "gflops": flop / dt / 1e9, "cpu_model": cpu_model(),
-            "sample": f"first {n} of {cfg.N} tokens, same weights, float64 numpy oracle "
-                      f"({dt:.1f} s)"}
-
-
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo", encoding="utf-8"):
@@ -448,8 +499,41 @@ def cpu_model():
     return None
 
 
+def cpu_baseline(cfg, inp, n, capv, fp8=False):
+    """The C++ oracle, as it stands, on the first n tokens of the same layer
+    (route, permute, expert FFN, combine; the experts stream one at a time).
+    FP8 weights: quantised and dequantised by the numpy oracle before the
+    timed run, as the GPU's are quantised before its timed steps."""
+    import numpy as np
+    import torch
+
+    from oracle import cpp as C
+    from oracle import moe_oracle as O
+
+    def b(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    x = b(inp["x"][:n])
+    wr = inp["w_router"].cpu().numpy()
+    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    wg, wu, wd = b(inp["w_gate"]), b(inp["w_up"]), b(inp["w_down"])
+    if fp8:
+        wg, wu, wd = (O.dequantize_fp8_bits(*O.quantize_fp8(m)) for m in (wg, wu, wd))
+    cap = C.capacity(n, cfg.K, cfg.E, *cfg.capacity) if capv else None
+    t0 = time.perf_counter()
+    C.forward(x, wr, bias, wg, wu, wd, cfg.K, cfg.gating, cap=cap, want_h=False)
+    dt = time.perf_counter() - t0
+    slots = n * cfg.K if cap is None else min(n * cfg.K, cfg.E * cap)
+    flop = 2.0 * n * cfg.D * cfg.E + 6.0 * cfg.D * cfg.F * slots
+    return {"value": n / dt, "unit": "tokens/s", "cores": C.threads(), "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(), "gflops": flop / dt / 1e9,
+            "seconds": dt,
+            "sample": f"first {n} of {cfg.N} tokens of the same layer (same weights), C++ "
+                      f"oracle (float64 sums, OpenMP over rows and output columns)"}
+
+
 def cpu_baseline_gelu(cfg, inp, n):
-    """The CPU oracle of the GELU-expert layer on the first n tokens."""
+    """The numpy oracle of the GELU-expert layer on the first n tokens."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -470,9 +554,129 @@ def cpu_baseline_gelu(cfg, inp, n):
     D4 = cfg.D // 4
     flop = 2.0 * n * (cfg.D * D4 + D4 * cfg.E) + 4.0 * cfg.D * cfg.F * n * cfg.K
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "gflops": flop / dt / 1e9, "cpu_model": cpu_model(),
-            "sample": f"first {n} of {cfg.N} tokens, same weights, float64 numpy oracle "
-                      f"({dt:.1f} s)"}
+            "nproc": os.cpu_count(), "gflops": flop / dt / 1e9, "cpu_model": cpu_model(),
+            "seconds": dt,
+            "sample": f"first {n} of {cfg.N} tokens, same weights, float64 numpy oracle"}
+
+
+# ---------------------------------------------------------------- profile summaries
+
+def _rows(path):
+    with open(path, newline="", encoding="utf-8") as f:
+        return list(csv.DictReader(f))
+
+
+def _is_libmoe(name: str) -> bool:
+    keys = ("grouped_gemm", "grouped_ffn", "router_", "topk_", "perm_", "combine_",
+            "quantize_fp8", "routing_stats", "fused_reset", "write_offsets", "route_decode",
+            "moe_")
+    return any(k in name for k in keys)
+
+
+def _short(name: str) -> str:
+    """Kernel name without the namespace, return type and argument list."""
+    n = name
+    for pre in ("void ", "moe::(anonymous namespace)::", "(anonymous namespace)::", "moe::"):
+        n = n.replace(pre, "")
+    depth = 0
+    for i, ch in enumerate(n):      # cut at the argument list's "(" outside any <...>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i].strip()
+    return n.strip()
+
+
+def trace_summary(d: str, pre_steps, steps: int, warm_steps: int):
+    """Per libmoe kernel: the launches of the timed steps of a profiled run
+    (pre_steps whole steps, then the `steps` timed ones, then `warm_steps`).
+    A kernel launched c times per step has its first pre_steps * c launches
+    skipped and the next steps * c taken; c = its launches / all steps."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    launches = {}
+    for f in files:
+        for r in _rows(f):
+            name = _short(r.get("Kernel_Name", ""))
+            if not _is_libmoe(name):
+                continue
+            launches.setdefault(name, []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    if pre_steps is None:
+        raise SystemExit("--pre-steps is needed")
+    counts = {k: len(v) for k, v in launches.items()}
+    total_steps = pre_steps + steps + warm_steps
+    out = []
+    layer = 0.0
+    for name, v in launches.items():
+        v.sort()
+        c = len(v) / total_steps
+        if abs(c - round(c)) > 1e-9 or round(c) == 0:
+            # a kernel outside the per-step pattern (e.g. input generation)
+            continue
+        c = int(round(c))
+        sel = v[pre_steps * c:(pre_steps + steps) * c]
+        dur = [(b - a) / 1e3 for a, b in sel]
+        avg = sum(dur) / len(dur)
+        layer += avg * c
+        out.append((name, len(dur), avg, min(dur), max(dur), c))
+    out.sort(key=lambda r: -r[2] * r[5])
+    print("| kernel | launches (timed) | avg µs | min µs | max µs | share of layer |")
+    print("|---|---|---|---|---|---|")
+    for name, n, avg, lo, hi, c in out:
+        print(f"| `{name}` | {n} | {avg:.1f} | {lo:.1f} | {hi:.1f} | "
+              f"{100 * avg * c / layer:.1f}% |")
+    print(f"\nSum of libmoe kernel time per step: {layer:.1f} µs (timed steps only; "
+          f"launches per kernel in the whole run: "
+          + ", ".join(f"{k} {v}" for k, v in sorted(counts.items())) + ")")
+
+
+def _pmc_avg(d: str, counter: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    acc = {}
+    for f in files:
+        for r in _rows(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = _short(r.get("Kernel_Name", ""))
+            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, label=None):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a copy of known size."""
+    fetch, write = _pmc_avg(fetch_dir, "FETCH_SIZE"), _pmc_avg(write_dir, "WRITE_SIZE")
+    cf, cw = _pmc_avg(cfetch_dir, "FETCH_SIZE"), _pmc_avg(cwrite_dir, "WRITE_SIZE")
+    copy_f = max(cf.values())   # the copy kernel is the largest dispatch of that run
+    copy_w = max(cw.values())
+    n = 1024 * 1024             # KiB copied by --calib-copy-mib 1024
+    kf, kw = n / copy_f, n / copy_w
+    print(f"Calibration: a 1 GiB device-to-device copy reads FETCH_SIZE = {copy_f:.0f} KiB and "
+          f"WRITE_SIZE = {copy_w:.0f} KiB, so bytes = FETCH_SIZE x 1024 x {kf:.4f} and "
+          f"WRITE_SIZE x 1024 x {kw:.4f}. Values are averages over the dispatches of each "
+          f"kernel.\n")
+    print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read GB | HBM write GB | total GB |")
+    print("|---|---|---|---|---|---|")
+    best = None
+    for name in sorted(fetch, key=lambda k: -fetch[k]):
+        if not _is_libmoe(name):
+            continue
+        f, w = fetch[name], write.get(name, 0.0)
+        rd, wr = f * 1024 * kf / 1e9, w * 1024 * kw / 1e9
+        print(f"| `{name}` | {f:.0f} | {w:.0f} | {rd:.3f} | {wr:.3f} | {rd + wr:.3f} |")
+        if label and label in name and best is None:
+            best = (name, int((rd + wr) * 1e9))
+    if best:
+        print("\nMachine-readable line for the benchmark (bytes per launch of the dominant "
+              "kernel; valid only while the kernel source has this SHA-256):\n")
+        print("traffic: " + json.dumps({"kernel": best[0], "bytes": best[1],
+                                        "source_sha256": source_sha()}))
 
 
 if __name__ == "__main__":

@@ -16,8 +16,9 @@
 //              ballots (no atomics decide positions, so the layout is
 //              deterministic); writes slot_row and row_token.
 //   4. copy  : each token row is read once and written to its K rows.
-//   5. pad   : (padded layout) row_token = -1 and zero rows past each
-//              expert's kept slots.
+//   5. pad   : (padded layout) row_token = -1 for the rows past each
+//              expert's kept slots, and zero x_perm rows there when x_perm
+//              is given.
 #include <algorithm>
 
 #include "common.h"
@@ -208,19 +209,25 @@ perm_small_kernel(int64_t S, int E, int K, int nbits, int64_t cap, int padded,
   }
 }
 
-// Padded layout: rows [e*cap + min(count_e, cap), (e+1)*cap) are padding.
+// Padded layout: rows [e*cap + min(count_e, cap), (e+1)*cap) are padding:
+// row_token = -1 and, when x_perm is given, a zero row.  Grid-stride over all
+// E*cap rows (many workgroups, each row's test is one cached load of its
+// expert's count); a workgroup writes a padding row with 16-byte stores.
 __global__ void __launch_bounds__(256)
-perm_pad_kernel(int E, int64_t cap, int D, const int32_t* __restrict__ counts,
+perm_pad_kernel(int64_t R, int64_t cap, int D, const int32_t* __restrict__ counts,
                 int32_t* __restrict__ row_token, uint16_t* __restrict__ x_perm) {
-  const int e = blockIdx.x;
-  const int64_t kept = min<int64_t>(counts[e], cap);
-  const int64_t npad = cap - kept;
-  const int64_t r0 = e * cap + kept;
-  for (int64_t i = threadIdx.x; i < npad; i += 256) row_token[r0 + i] = -1;
   const int cpr = D / 8;
   const uint4 z = {0u, 0u, 0u, 0u};
-  for (int64_t w = threadIdx.x; w < npad * cpr; w += 256)
-    reinterpret_cast<uint4*>(x_perm + (r0 + w / cpr) * D)[w % cpr] = z;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const int64_t e = r / cap;
+    const int64_t kept = min<int64_t>(counts[e], cap);
+    if (r - e * cap < kept) continue;             // a kept row (workgroup-uniform)
+    if (threadIdx.x == 0) row_token[r] = -1;
+    if (x_perm) {
+      uint4* row = reinterpret_cast<uint4*>(x_perm + r * D);
+      for (int c = threadIdx.x; c < cpr; c += 256) row[c] = z;
+    }
+  }
 }
 
 }  // namespace
@@ -249,14 +256,17 @@ hipError_t launch_permute(const Dims& d, const uint16_t* x, const int32_t* ids, 
                        d.E, d.K, nbits, d.cap, (int)d.padded, ids, table, offsets, slot_row,
                        row_token);
   }
+  if (d.padded) {
+    // padding rows: row_token = -1 always, zero rows when x_perm is given
+    const int64_t blocks = std::min<int64_t>(d.R, 8 * (int64_t)device_cu_count());
+    hipLaunchKernelGGL(perm_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, s, d.R, d.cap, d.D,
+                       counts, row_token, x_perm);
+  }
   if (!x_perm) return hipGetLastError();      // routing tables only
   const int64_t items = d.N * (d.D / 8);
   const int64_t blocks = std::min<int64_t>((items + 255) / 256, 1 << 20);
   hipLaunchKernelGGL(perm_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, d.N, d.D, d.K, x,
                      slot_row, x_perm);
-  if (d.padded)
-    hipLaunchKernelGGL(perm_pad_kernel, dim3(d.E), dim3(256), 0, s, d.E, d.cap, d.D, counts,
-                       row_token, x_perm);
   return hipGetLastError();
 }
 

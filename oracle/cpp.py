@@ -50,7 +50,9 @@ def _declare(L):
     L.oracle_combine.argtypes = [I64, I32, I32, P, P, P, P]
     L.oracle_forward.argtypes = [I64, I32, I32, I32, I32, I32, I64, P, P, P, P, P, P, I32,
                                  P, P, P, P, P, P, P, P, P, P]
-    for f in ("oracle_router_logits", "oracle_route", "oracle_permute", "oracle_ffn_rows",
+    L.oracle_quantize_fp8.argtypes = [I64, I32, P, P, P]
+    L.oracle_dequantize_fp8.argtypes = [I64, I32, P, P, P]
+    for f in ("oracle_quantize_fp8", "oracle_dequantize_fp8", "oracle_router_logits", "oracle_route", "oracle_permute", "oracle_ffn_rows",
               "oracle_expert_ffn", "oracle_combine", "oracle_forward"):
         getattr(L, f).restype = None
 
@@ -78,6 +80,27 @@ def threads() -> int:
 
 def capacity(N: int, K: int, E: int, num: int, den: int) -> int:
     return int(lib().oracle_capacity(N, K, E, num, den))
+
+
+def quantize_fp8(w_bits):
+    """bf16 weights [..., cols] -> (codes uint8 [..., cols], scales uint8 [..., cols/32])."""
+    w = _c(w_bits, np.uint16)
+    cols = w.shape[-1]
+    rows = w.size // cols
+    codes = np.empty(w.shape, dtype=np.uint8)
+    scales = np.empty(w.shape[:-1] + (cols // 32,), dtype=np.uint8)
+    lib().oracle_quantize_fp8(rows, cols, _p(w), _p(codes), _p(scales))
+    return codes, scales
+
+
+def dequantize_fp8_bits(codes, scales):
+    """(codes, scales) -> bf16 bit patterns of the dequantised weights."""
+    c = _c(codes, np.uint8)
+    s = _c(scales, np.uint8)
+    cols = c.shape[-1]
+    out = np.empty(c.shape, dtype=np.uint16)
+    lib().oracle_dequantize_fp8(c.size // cols, cols, _p(c), _p(s), _p(out))
+    return out
 
 
 def router_logits(x_bits, w_router):

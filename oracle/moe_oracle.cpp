@@ -184,9 +184,97 @@ void swiglu_expert(int64_t m, const uint16_t* const* rows, int D, int F, const u
   }
 }
 
+// ------------------------------------------------------------ FP8 weights
+//
+// Block-scaled FP8 expert weights ([zoe] 第四层 DeepGEMM & MegaMoE Kernel: FP8
+// weights; [jsq] 5.3 技巧2: 8-bit expert weights dequantised for use).  The
+// pages fix no format; the reading is the OCP microscaling layout with E4M3
+// elements: 32 consecutive values along a weight row's contraction axis share
+// a power-of-two scale 2^s, stored as the byte s + 127.
+
+constexpr double kE4m3Max = 448.0;
+constexpr int kScaleMin = -117;   // every dequantised value stays a normal bf16 number
+constexpr int kScaleMax = 119;
+
+// floor(log2 a) for a finite a > 0.
+int floor_log2(double a) {
+  int e = 0;
+  std::frexp(a, &e);             // a = m 2^e, 0.5 <= m < 1
+  return e - 1;
+}
+
+// A value to the nearest E4M3 code, ties to even, saturating at +-448; a
+// non-finite value gives the NaN code 0x7f with the value's sign bit.
+// E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is
+// subnormal (M * 2^-9); S.1111.111 is NaN; the largest finite value is 448.
+uint8_t e4m3_encode(double t) {
+  const uint8_t sign = std::signbit(t) ? 0x80 : 0x00;
+  if (!std::isfinite(t)) return sign | 0x7f;
+  const double a = std::min(std::fabs(t), kE4m3Max);
+  // grid step: 2^(floor(log2 a) - 3) in the normal range, 2^-9 below 2^-6
+  const int step = a >= std::ldexp(1.0, -6) ? floor_log2(a) - 3 : -9;
+  const double v = std::ldexp(std::nearbyint(std::ldexp(a, -step)), step);
+  if (v >= std::ldexp(1.0, -6)) {
+    const int e = floor_log2(v);                                   // carry may raise it
+    const int man = static_cast<int>(std::ldexp(v, -e) * 8.0 - 8.0);   // exact, 0..7
+    return sign | static_cast<uint8_t>(((e + 7) << 3) | man);
+  }
+  return sign | static_cast<uint8_t>(std::ldexp(v, 9));           // subnormal: v / 2^-9
+}
+
+double e4m3_decode(uint8_t c) {
+  const int ef = (c >> 3) & 15, mf = c & 7;
+  double mag;
+  if (ef == 15 && mf == 7) mag = NAN;
+  else if (ef == 0) mag = std::ldexp(static_cast<double>(mf), -9);
+  else mag = std::ldexp(static_cast<double>(8 + mf), ef - 10);
+  return (c & 0x80) ? -mag : mag;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Quantise bf16 weights [rows, cols] (cols a multiple of 32): per block of 32
+// consecutive values of a row, s = floor(log2(largest finite |w|)) - 8
+// clamped to [-117, 119] (an all-zero block takes -117), so the block's
+// largest value lands in E4M3's top binade [256, 512); code = E4M3(w / 2^s)
+// (the division by a power of two is exact); scale byte = s + 127.
+// codes [rows, cols], scales [rows, cols / 32].
+void oracle_quantize_fp8(int64_t rows, int cols, const uint16_t* w, uint8_t* codes,
+                         uint8_t* scales) {
+  const int nb = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int b = 0; b < nb; ++b) {
+      const size_t o = static_cast<size_t>(r) * cols + 32 * b;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        const double v = bf16_value(w[o + i]);
+        if (std::isfinite(v)) amax = std::max(amax, std::fabs(v));
+      }
+      int s = amax > 0.0 ? floor_log2(amax) - 8 : kScaleMin;
+      s = std::min(std::max(s, kScaleMin), kScaleMax);
+      for (int i = 0; i < 32; ++i) codes[o + i] = e4m3_encode(std::ldexp(bf16_value(w[o + i]), -s));
+      scales[static_cast<size_t>(r) * nb + b] = static_cast<uint8_t>(s + 127);
+    }
+  }
+}
+
+// Dequantise: value = E4M3(code) * 2^(byte - 127), as bf16 bits (exact for the
+// scale bytes the quantiser writes).  w [rows, cols] out.
+void oracle_dequantize_fp8(int64_t rows, int cols, const uint8_t* codes, const uint8_t* scales,
+                           uint16_t* w) {
+  const int nb = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c) {
+      const size_t o = static_cast<size_t>(r) * cols + c;
+      const int s = static_cast<int>(scales[static_cast<size_t>(r) * nb + c / 32]) - 127;
+      w[o] = bf16_bits(std::ldexp(e4m3_decode(codes[o]), s));
+    }
+}
+
 
 int oracle_version(void) { return 1; }
 

@@ -138,41 +138,3 @@ def test_fp8_ffn_small(name):
     torch.cuda.synchronize()
     assert np.array_equal(bits(out2)[covered], out8[covered])
     assert torch.equal(y2.view(torch.int16), L.y.view(torch.int16))
-
-
-# (workload, sampled tokens): qwen3_decode runs the register-staged kernel,
-# deepseek_v3 the 128 x 256 ring, hot_skew the 256 x 256 ring with one expert
-# holding about a quarter of the rows.
-FULL_FP8 = [("qwen3_decode", 8), ("deepseek_v3", 2), ("hot_skew", 2)]
-
-
-@pytest.mark.parametrize("name,ntok", FULL_FP8, ids=[n for n, _ in FULL_FP8])
-def test_fp8_full_size(name, ntok):
-    """Full-size workloads through moe_forward_fp8: y of sampled tokens
-    against the oracle FFN on the oracle's own quantisation of each expert
-    used, and the GPU codes of those experts bit-exact."""
-    cfg = ms.CONFIGS[name]
-    print(f"[fp8 full] {name}", flush=True)
-    L = Layer(cfg)
-    L.staged()                                    # routing of the bf16 path (identical)
-    qg, qu, qd = _fp8_weights(L)
-    y8 = torch.empty_like(L.y)
-    moe.forward_fp8(L.p, L.x, L.w_router, L.bias, qg, qu, qd, y8, L.ws)
-    torch.cuda.synchronize()
-    tokens = sample_tokens(cfg.N, ntok)
-
-    def expert_weights(e):
-        out = []
-        for w, q, what in ((L.w_gate, qg, "gate"), (L.w_up, qu, "up"), (L.w_down, qd, "down")):
-            oq = check_quantized((q[0][e], q[1][e]), bits(w[e]), f"expert {e} {what}")
-            out.append(O.dequantize_fp8_bits(*oq))
-        return tuple(out)
-
-    x_bits = bits(L.x[torch.as_tensor(tokens, device=DEV)])
-    ids = np_(L.ids)[tokens]
-    w = np_(L.w)[tokens]
-    kept = np_(L.slot_row).reshape(cfg.N, cfg.K)[tokens] >= 0
-    y_ref, _ = O.token_outputs(x_bits, ids, w, kept, expert_weights)
-    assert_fp_close(O.bf16_to_f64(bits(y8)[tokens]), y_ref, f"y[{len(tokens)} sampled tokens]")
-    del L, qg, qu, qd
-    torch.cuda.empty_cache()

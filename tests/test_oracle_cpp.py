@@ -350,3 +350,40 @@ def test_cpp_equals_numpy_on_sampled_deepseek_v3_tokens():
     _assert_close(out_c.reshape(out_n.shape), out_n, "out")
     _assert_close(y_c, y_n, "y")
     assert np.mean(out_c.reshape(out_n.shape) == out_n) > 0.999
+
+
+# ---------------------------------------------------------------- FP8 weights
+
+@pytest.mark.parametrize("kind", ["normal", "all_bits", "specials"])
+def test_cpp_fp8_quantizer_equals_numpy(kind):
+    """Codes and scale bytes bit for bit those of the numpy quantiser (itself
+    pinned to torch's E4M3 conversions): normal weights, uniformly random bf16
+    bit patterns (subnormals, huge values, infinities, NaNs) and hand-built
+    blocks (all zero, one subnormal, saturating, ties)."""
+    rng = np.random.default_rng({"normal": 1, "all_bits": 2, "specials": 3}[kind])
+    if kind == "normal":
+        w = O.f64_to_bf16_bits(rng.standard_normal((96, 256)) * 0.02)
+    elif kind == "all_bits":
+        w = rng.integers(0, 65536, (128, 512), dtype=np.uint16)
+    else:
+        v = np.zeros((4, 32))
+        v[1, 3] = 2.0 ** -133                          # a bf16 subnormal alone in its block
+        v[2] = np.linspace(-3.0e38, 3.0e38, 32)         # near the top of bf16
+        v[3] = (np.arange(32) - 16) * 2.0 ** -4 * 17    # many exact ties after scaling
+        w = O.f64_to_bf16_bits(v)
+    a, b = O.quantize_fp8(w), C.quantize_fp8(w)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    da, db = O.dequantize_fp8_bits(*a), C.dequantize_fp8_bits(*b)
+    nan = np.isnan(O.bf16_to_f64(da))
+    assert np.array_equal(da[~nan], db[~nan]) and np.all(np.isnan(O.bf16_to_f64(db)[nan]))
+
+
+def test_cpp_e4m3_decoder_against_torch():
+    """Every E4M3 code dequantised with scale 2^0 equals torch's float8_e4m3fn value."""
+    codes = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    scales = np.full((8, 1), 127, dtype=np.uint8)
+    got = O.bf16_to_f64(C.dequantize_fp8_bits(codes, scales))
+    ref = torch.from_numpy(codes.reshape(-1)).view(torch.float8_e4m3fn).to(torch.float64)
+    ref = ref.numpy().reshape(8, 32)
+    both_nan = np.isnan(got) & np.isnan(ref)
+    assert np.array_equal(got[~both_nan], ref[~both_nan]) and both_nan.sum() == 2

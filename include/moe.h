@@ -209,6 +209,27 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                        float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops (a decode step), harnesses that forbid
+ * hipMalloc.  It takes no workspace: the one moe_forward needs lives in a
+ * static device array of MOE_STATIC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends (its address is looked up once
+ * per device, on the first call there).  No call allocates or frees memory.
+ *   Arguments, outputs and results as moe_forward (bit for bit the same).
+ *   MOE_ERR_WORKSPACE, before any HIP call, when moe_workspace_size(p)
+ *   exceeds MOE_STATIC_SCRATCH_BYTES (e.g. a decode step of the Qwen3-30B-A3B
+ *   layer shape needs about 6 MB; prefill batches do not fit).
+ *   The scratch is shared by every call on one GPU and keeps the last call's
+ *   contents; nothing in it needs to start at zero.  Calls that overlap on
+ *   one GPU (other streams, other threads) race on it and give undefined
+ *   results: serialise them. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_static(const moe_problem* p, const uint16_t* x, const float* w_router,
+                              const float* expert_bias, const uint16_t* w_gate,
+                              const uint16_t* w_up, const uint16_t* w_down, uint16_t* y,
+                              float* logits, int32_t* topk_ids, float* topk_weights,
+                              int32_t* expert_counts, int32_t* expert_offsets, void* stream);
+
 /* ------------------------------------------------------------ fused FFN */
 /* The whole expert FFN as one persistent launch (the single-kernel MoE of
  * "MoE 推理完整机制" (zoe.im) 第四层, DeepGEMM & MegaMoE Kernel: workgroups

@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     forward,
     forward_fp8,
     forward_fused,
+    forward_static,
     forward_gelu,
     fused_error_offset,
     fused_ffn,
@@ -37,6 +38,7 @@ from ._lib import (  # noqa: F401
     permuted_rows,
     problem,
     quantize_fp8,
+    STATIC_SCRATCH_BYTES,
     route,
     route_mlp,
     routing_stats,

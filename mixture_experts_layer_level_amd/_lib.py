@@ -70,6 +70,8 @@ def _load():
     L.moe_unpermute_combine.argtypes = [P, vp, vp, vp, vp, vp]
     L.moe_forward.restype = ctypes.c_int
     L.moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_forward_static.restype = ctypes.c_int
+    L.moe_forward_static.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_fused_ffn.restype = ctypes.c_int
     L.moe_fused_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_forward_fused.restype = ctypes.c_int
@@ -216,6 +218,19 @@ def forward(p, x, w_router, bias, w_gate, w_up, w_down, y, ws, logits=None, topk
                                           _ptr(logits), _ptr(topk_ids), _ptr(topk_weights),
                                           _ptr(counts), _ptr(offsets), _ptr(ws), _nbytes(ws),
                                           _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 64 << 20     # MOE_STATIC_SCRATCH_BYTES
+
+
+def forward_static(p, x, w_router, bias, w_gate, w_up, w_down, y, logits=None, topk_ids=None,
+                   topk_weights=None, counts=None, offsets=None, stream=None):
+    """moe_forward_static: moe_forward with the library's static scratch (no workspace)."""
+    _check("moe_forward_static",
+           lib.moe_forward_static(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
+                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(logits),
+                                  _ptr(topk_ids), _ptr(topk_weights), _ptr(counts),
+                                  _ptr(offsets), _stream(stream)))
 
 
 def routing_stats(num_experts, expert_counts, ema, expert_bias, decay=0.99, step=0.1, stream=None):

@@ -2,8 +2,16 @@
 // Every check runs on the host before the first HIP call of an entry point.
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
+
+// Scratch of moe_forward_static, the entry point for callers that cannot
+// allocate: the workspace of moe_forward for problems that need at most
+// MOE_STATIC_SCRATCH_BYTES.  Each GPU the library runs on holds its own copy
+// for as long as the process lives.  In host code this name is only a handle:
+// its device address comes from hipGetSymbolAddress (static_scratch below).
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace moe {
 
@@ -165,6 +173,30 @@ inline moe_status check_fp8(const uint8_t* codes, const uint8_t* scales) {
 }
 inline bool fp8_present(const uint8_t* c, const uint8_t* s) { return c && s; }
 inline bool fp8_aligned(const uint8_t* c, const uint8_t* s) { return aligned16(c) && aligned16(s); }
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+moe_status static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !ptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -366,6 +398,26 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                         return e != hipSuccess ? e
                                                : launch_expert_down(d, h, offs, w_down, op, s);
                       });
+}
+
+moe_status moe_forward_static(const moe_problem* p, const uint16_t* x, const float* w_router,
+                              const float* expert_bias, const uint16_t* w_gate,
+                              const uint16_t* w_up, const uint16_t* w_down, uint16_t* y,
+                              float* logits, int32_t* topk_ids, float* topk_weights,
+                              int32_t* expert_counts, int32_t* expert_offsets, void* stream) {
+  // host-side checks first (forward_impl repeats them): problem, pointers and
+  // the workspace size against the static scratch
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !y || !w_router || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARG;
+  if (forward_layout(d).total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  if (d.N == 0) return MOE_OK;
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != MOE_OK) return st;
+  return moe_forward(p, x, w_router, expert_bias, w_gate, w_up, w_down, y, logits, topk_ids,
+                     topk_weights, expert_counts, expert_offsets, ws, MOE_STATIC_SCRATCH_BYTES,
+                     stream);
 }
 
 moe_status moe_routing_stats(int32_t num_experts, const int32_t* expert_counts, float* ema,

@@ -275,3 +275,25 @@ def test_fused_argument_checks():
     assert n.value % 4 == 0 and n1.value > n.value and n1.value + 4 <= need
     assert L.moe_fused_error_offset(bp, 0, None) == INVALID
 
+
+
+def forward_static_status(p, x=FAKE, w=FAKE, y=FAKE):
+    return moe.lib.moe_forward_static(ctypes.byref(p), x, w, None, w, w, w, y, None, None, None,
+                                      None, None, None)
+
+
+def test_forward_static_host_checks():
+    """moe_forward_static: the problem, the pointers and the scratch size are
+    checked on the host; a problem whose workspace exceeds the static scratch
+    is refused before any HIP call (nothing here touches a GPU)."""
+    assert moe.STATIC_SCRATCH_BYTES == 64 << 20
+    assert forward_static_status(P(K=0)) == INVALID
+    assert forward_static_status(P(D=100)) == UNSUPPORTED
+    assert forward_static_status(P(), x=None) == INVALID
+    assert forward_static_status(P(), y=None) == INVALID
+    assert forward_static_status(P(N=0)) == OK
+    big = P(N=8192, D=7168, F=2048, E=256, K=8, g=1)      # a DeepSeek-V3-shape prefill batch
+    assert moe.workspace_size(big) > moe.STATIC_SCRATCH_BYTES
+    assert forward_static_status(big) == WORKSPACE
+    dec = P(N=64, D=2048, F=768, E=128, K=8)               # a Qwen3-30B-A3B-shape decode step
+    assert moe.workspace_size(dec) <= moe.STATIC_SCRATCH_BYTES

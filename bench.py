@@ -9,10 +9,12 @@ grouped GEMM), can be bracketed with HIP events on the stream it runs on.
 Inputs are synthetic, seeded and already resident in HBM when timing starts.
 
 Timing: W untimed warm-up steps, then K timed steps.  Before every timed step
-512 MiB of scratch are written outside its events (twice the 256 MB
-memory-side cache), so no activation or weight of the previous step is still
-cached: ``ms_per_step`` is the mean of the K cold steps.  K more steps run
-back to back afterwards and give ``warm_ms_per_step``.
+512 MiB of scratch are written and then read back outside its events (twice
+the 256 MB memory-side cache): no activation or weight of the previous step is
+still cached, and the caches hold clean lines, so the step pays for no
+write-back of the flush's own data.  ``ms_per_step`` is the mean of the K cold
+steps.  K more steps run back to back afterwards and give
+``warm_ms_per_step``.
 
 The headline workload is the DeepSeek-V3 layer shape (N=8192, D=7168,
 E=256, K=8, F=2048, sigmoid gating).  The other workloads -- the Qwen3 decode
@@ -179,7 +181,7 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
             moe.route_mlp(p, x, inp["w_proj"], inp["b_proj"], inp["w_out"], inp["b_out"],
                           logits, ids, w, ws, features=feats, stream=stream)
         else:
-            moe.route(p, x, wr, bias, logits, ids, w, stream=stream)
+            moe.route(p, x, wr, bias, logits, ids, w, ws, stream=stream)
         rec(ev, 1)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row,
                     None if (gather or o.fused) else x_perm, ws, stream=stream)
@@ -219,18 +221,24 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         step()
     torch.cuda.synchronize()
 
-    # timed: every step cold, each preceded by a 512 MiB scratch write
-    # outside its events
-    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    # timed: every step cold, each preceded by a 512 MiB scratch write and a
+    # read of it, outside its events
+    scratch = torch.empty(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def flush():
+        scratch.zero_()
+        torch.sum(scratch, dim=0, out=sink)
+
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(6)) for _ in range(steps)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for i in range(steps):
-        scratch.zero_()
+        flush()
         step(evs[i])
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    del scratch
+    del scratch, sink
     if o.fused:
         off = moe.fused_error_offset(p, whole_layer=False)
         err_word = int(ws[off:off + 4].view(torch.int32).item())
@@ -440,8 +448,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded counter-based draws, random-init weights)",
         "config": head["config"],
-        "timing": "each timed step cold: 512 MiB scratch write outside its HIP events; "
-                  "warm_ms_per_step: the same steps back to back",
+        "timing": "each timed step cold: 512 MiB scratch written then read outside its HIP "
+                  "events; warm_ms_per_step: the same steps back to back",
     }
     for k in ("warm_ms_per_step", "tflops", "pct_bf16_mfma_peak", "weight_stream_gbps",
               "pct_hbm_peak_weights", "ffn_weight_stream_gbps", "max_expert_rows",

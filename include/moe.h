@@ -111,7 +111,10 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
  *   logits       [N, E] fp32: written when x != NULL (pre-bias), read else.
  *   topk_ids     [N, K] int32, out: selected experts, largest key first.
  *   topk_weights [N, K] fp32, out: router weights, sum to 1 per row.
- * Needs no workspace (ws may be NULL). */
+ * Workspace optional (ws may be NULL): given moe_workspace_size bytes,
+ * 16-byte aligned, a small problem (few token x expert tiles, e.g. a decode
+ * step) runs its router GEMM spread over more compute units.  The logits,
+ * and so every output, are bit for bit the same with or without it. */
 moe_status moe_route(const moe_problem* p, const uint16_t* x, const float* w_router,
                      const float* expert_bias, float* logits, int32_t* topk_ids,
                      float* topk_weights, void* ws, size_t ws_bytes, void* stream);

@@ -49,11 +49,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // ---------------------------------------------------------------- launchers
 
-// route.hip
+// route.hip.  With a partials buffer of router_ws_bytes(d) (when nonzero) the
+// router runs in its split form and writes partial logits there; launch_topk
+// with the same buffer then sums them into logits before selecting (the
+// logits are bit-identical to the unsplit router's).  partials NULL: the
+// router writes logits and launch_topk reads them.
+size_t router_ws_bytes(const Dims& d);
 hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, float* logits,
-                              hipStream_t s);
-hipError_t launch_topk(const Dims& d, const float* logits, const float* bias, int32_t* ids,
-                       float* weights, hipStream_t s);
+                              float* partials, hipStream_t s);
+hipError_t launch_topk(const Dims& d, float* logits, const float* bias, int32_t* ids,
+                       float* weights, const float* partials, hipStream_t s);
 
 // permute.hip (x_perm NULL: the routing tables only, no row copy)
 size_t permute_ws_bytes(const Dims& d);

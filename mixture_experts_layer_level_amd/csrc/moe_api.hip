@@ -63,7 +63,7 @@ moe_status check_problem(const moe_problem* p, Dims* d) {
 
 struct ForwardWs {
   size_t logits, ids, weights, counts, offsets, row_token, slot_row, x_perm, out_perm, perm,
-      ffn, feats, roff, fused, total;
+      ffn, feats, roff, fused, rpart, total;
 };
 
 ForwardWs forward_layout(const Dims& d) {
@@ -88,6 +88,7 @@ ForwardWs forward_layout(const Dims& d) {
   w.feats = take((size_t)d.N * (d.D / 4) * 2);   // MLP router: compressed features
   w.roff = take(2 * 4);                          // MLP router: offsets {0, N} of its GEMM
   w.fused = take(fused_ws_bytes(d));             // fused FFN: h and its counters
+  w.rpart = take(router_ws_bytes(d));            // split router: partial logits
   w.total = o;
   return w;
 }
@@ -160,9 +161,9 @@ hipError_t launch_route_mlp(const Dims& d, const uint16_t* x, const uint16_t* w_
   if (e != hipSuccess) return e;
   Dims dr = d;
   dr.D = d.D / 4;
-  e = launch_router_gemm(dr, feats, w_out, logits, s);
+  e = launch_router_gemm(dr, feats, w_out, logits, nullptr, s);
   if (e != hipSuccess) return e;
-  return launch_topk(d, logits, b_out, ids, weights, s);
+  return launch_topk(d, logits, b_out, ids, weights, nullptr, s);
 }
 
 // Block-scaled FP8 weight stack: codes and scales present and 16-byte aligned.
@@ -254,8 +255,6 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
 moe_status moe_route(const moe_problem* p, const uint16_t* x, const float* w_router,
                      const float* expert_bias, float* logits, int32_t* topk_ids,
                      float* topk_weights, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   Dims d;
   moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
@@ -264,11 +263,16 @@ moe_status moe_route(const moe_problem* p, const uint16_t* x, const float* w_rou
   if (d.N == 0) return MOE_OK;
   (void)hipGetLastError();  // report only this call's launch errors
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // an optional workspace lets a small router run in its split form (the
+  // same logits bit for bit); it is ignored when missing, small or unaligned
+  const size_t need = router_ws_bytes(d);
+  float* parts = (x && need > 0 && ws && aligned16(ws) && ws_bytes >= need)
+                     ? static_cast<float*>(ws) : nullptr;
   if (x) {
-    st = hip_status(launch_router_gemm(d, x, w_router, logits, s));
+    st = hip_status(launch_router_gemm(d, x, w_router, logits, parts, s));
     if (st != MOE_OK) return st;
   }
-  return hip_status(launch_topk(d, logits, expert_bias, topk_ids, topk_weights, s));
+  return hip_status(launch_topk(d, logits, expert_bias, topk_ids, topk_weights, parts, s));
 }
 
 moe_status moe_permute(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
@@ -382,10 +386,14 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
                        aligned16(w_down);
   return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
                       expert_offsets, ws, ws_bytes, stream, kGatherBf16,
-                      [&](const Dims& d, float* lg, int32_t* ids, float* w, char*,
-                          const ForwardWs&, hipStream_t s) {
-                        const hipError_t e = launch_router_gemm(d, x, w_router, lg, s);
-                        return e != hipSuccess ? e : launch_topk(d, lg, expert_bias, ids, w, s);
+                      [&](const Dims& d, float* lg, int32_t* ids, float* w, char* base,
+                          const ForwardWs& L, hipStream_t s) {
+                        float* parts = router_ws_bytes(d) > 0
+                                           ? reinterpret_cast<float*>(base + L.rpart)
+                                           : nullptr;
+                        const hipError_t e = launch_router_gemm(d, x, w_router, lg, parts, s);
+                        return e != hipSuccess ? e
+                                               : launch_topk(d, lg, expert_bias, ids, w, parts, s);
                       },
                       [&](const Dims& d, const uint16_t* xp, const int32_t* rt,
                           const int32_t* offs, uint16_t* op, void* fws, hipStream_t s) {
@@ -544,10 +552,14 @@ moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float*
       wd{w_down_codes, w_down_scales};
   return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
                       expert_offsets, ws, ws_bytes, stream, kGatherFp8,
-                      [&](const Dims& d, float* lg, int32_t* ids, float* w, char*,
-                          const ForwardWs&, hipStream_t s) {
-                        const hipError_t e = launch_router_gemm(d, x, w_router, lg, s);
-                        return e != hipSuccess ? e : launch_topk(d, lg, expert_bias, ids, w, s);
+                      [&](const Dims& d, float* lg, int32_t* ids, float* w, char* base,
+                          const ForwardWs& L, hipStream_t s) {
+                        float* parts = router_ws_bytes(d) > 0
+                                           ? reinterpret_cast<float*>(base + L.rpart)
+                                           : nullptr;
+                        const hipError_t e = launch_router_gemm(d, x, w_router, lg, parts, s);
+                        return e != hipSuccess ? e
+                                               : launch_topk(d, lg, expert_bias, ids, w, parts, s);
                       },
                       [&](const Dims& d, const uint16_t* xp, const int32_t* rt,
                           const int32_t* offs, uint16_t* op, void* fws, hipStream_t s) {
@@ -754,9 +766,10 @@ moe_status moe_forward_fused(const moe_problem* p, const uint16_t* x, const floa
   int32_t* slot_row = reinterpret_cast<int32_t*>(base + L.slot_row);
   uint16_t* out_perm = reinterpret_cast<uint16_t*>(base + L.out_perm);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(launch_router_gemm(d, x, w_router, logits, s));
+  float* parts = router_ws_bytes(d) > 0 ? reinterpret_cast<float*>(base + L.rpart) : nullptr;
+  st = hip_status(launch_router_gemm(d, x, w_router, logits, parts, s));
   if (st != MOE_OK) return st;
-  st = hip_status(launch_topk(d, logits, expert_bias, topk_ids, topk_weights, s));
+  st = hip_status(launch_topk(d, logits, expert_bias, topk_ids, topk_weights, parts, s));
   if (st != MOE_OK) return st;
   st = hip_status(launch_permute(d, x, topk_ids, expert_counts, expert_offsets, row_token,
                                  slot_row, nullptr, base + L.perm, s));

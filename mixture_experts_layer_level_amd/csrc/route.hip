@@ -63,25 +63,39 @@ __device__ __forceinline__ void split3(const float4& a, const float4& b, bf16x8_
 
 // Launch bounds follow the largest workgroup the launcher uses for each tile
 // size (4 waves at 64x64, 8 at 32x32), which sets the register budget.
+//
+// Split form (partials != NULL, 32x32 tiles only): the S waves of a tile run
+// as S one-wave workgroups, wave s of tile t in workgroup t * S + s, each
+// writing its partial tile to partials[s] ([S][N][E] fp32); the top-K kernel
+// then adds the partials in wave order, the order of the LDS reduction here.
+// Every logit is the same sum of the same terms in the same order: the two
+// forms give bit-identical logits, the split one on S times as many compute
+// units (a decode-sized router has only a few tiles).
 template <int WT>
 __global__ void __launch_bounds__(WT == 64 ? 256 : 512)
 router_mfma_kernel(int64_t N, int D, int E, int vec4, const uint16_t* __restrict__ x,
-                   const float* __restrict__ w, float* __restrict__ logits) {
+                   const float* __restrict__ w, float* __restrict__ logits, int split_waves,
+                   float* __restrict__ partials) {
   constexpr int TB = WT / 32;                   // 32-row blocks per tile side
   constexpr int LD = WT + 4;                    // LDS row stride (floats)
   extern __shared__ float red[];                // [S-1][WT][LD] partial tiles
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int S = blockDim.x >> 6;
+  const bool split = partials != nullptr;
+  const int S = split ? split_waves : (int)(blockDim.x >> 6);
   // This workgroup's tile.  Tiles are numbered token tile by token tile (the
   // expert tiles of one token tile are consecutive) and cut into eight
   // contiguous parts, one per XCD (workgroup b runs on XCD b % 8), so the
   // workgroups that read the same x rows run together and share them in one
   // L2.  The grid is a multiple of 8; workgroups past the last tile leave.
   const int ne = (E + WT - 1) / WT;
-  const int64_t total = ((N + WT - 1) / WT) * ne;
-  const int64_t v = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t total = ((N + WT - 1) / WT) * ne * (split ? S : 1);
+  int64_t v = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   if (v >= total) return;
+  int wave = threadIdx.x >> 6;
+  if (split) {   // workgroup = (tile, wave)
+    wave = (int)(v % S);
+    v /= S;
+  }
   const int64_t n0 = (v / ne) * WT;
   const int e0 = (int)(v % ne) * WT;
   const int r = lane & 31, kh = lane >> 5;
@@ -206,7 +220,36 @@ router_mfma_kernel(int64_t N, int D, int E, int vec4, const uint16_t* __restrict
   // Block (i, j): lane l, register v holds expert 8*(v/4) + 4*(l/32) + v%4 of
   // expert block i and token l%32 of token block j; four consecutive
   // registers are four consecutive experts.  Waves 1..S-1 leave their partial
-  // tiles in LDS; wave 0 adds them to its own in wave order and stores.
+  // tiles in LDS; wave 0 adds them to its own in wave order and stores.  In
+  // the split form every wave stores its partial tile to partials[wave].
+  if (split) {
+    float* dst0 = partials + (size_t)wave * N * E;
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        const int64_t n = n0 + j * 32 + r;
+        if (n >= N) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int el = i * 32 + 8 * g + 4 * kh;
+          float4 v4;
+          v4.x = acc_hi[i][j][4 * g + 0] + acc_lo[i][j][4 * g + 0];
+          v4.y = acc_hi[i][j][4 * g + 1] + acc_lo[i][j][4 * g + 1];
+          v4.z = acc_hi[i][j][4 * g + 2] + acc_lo[i][j][4 * g + 2];
+          v4.w = acc_hi[i][j][4 * g + 3] + acc_lo[i][j][4 * g + 3];
+          float* dst = dst0 + n * E + e0 + el;
+          if (vec4 && e0 + el + 3 < E) {
+            *reinterpret_cast<float4*>(dst) = v4;
+          } else {
+            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+            for (int c = 0; c < 4; ++c)
+              if (e0 + el + c < E) dst[c] = vv[c];
+          }
+        }
+      }
+    return;
+  }
   if (wave > 0) {
     float* mine = red + (size_t)(wave - 1) * WT * LD;
 #pragma unroll
@@ -273,21 +316,28 @@ __device__ __forceinline__ float from_orderable(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+// With partials (the split router), each logit is first summed from its
+// nparts partials in order and written to logits.
 template <int EPL>
 __global__ void __launch_bounds__(256)
-topk_kernel(int64_t N, int E, int K, int gating, const float* __restrict__ logits,
+topk_kernel(int64_t N, int E, int K, int gating, float* __restrict__ logits,
             const float* __restrict__ bias, int32_t* __restrict__ ids,
-            float* __restrict__ weights) {
+            float* __restrict__ weights, const float* __restrict__ partials, int nparts) {
   const int lane = threadIdx.x & 63;
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
-  const float* row = logits + n * E;
+  float* row = logits + n * E;
   uint64_t pk[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
     pk[j] = 0;
     if (e < E) {
+      if (partials) {
+        float lg = partials[n * E + e];
+        for (int q = 1; q < nparts; ++q) lg += partials[(size_t)q * N * E + n * E + e];
+        row[e] = lg;
+      }
       float key = row[e];
       if (bias) key = key + bias[e];
       if (key == 0.f) key = 0.f;                  // -0.0 -> +0.0
@@ -335,42 +385,81 @@ topk_kernel(int64_t N, int E, int K, int gating, const float* __restrict__ logit
 
 }  // namespace
 
-hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, float* logits,
-                              hipStream_t s) {
-  // 64x64 tiles with 4 waves when they alone give the chip at least one
-  // workgroup per CU; otherwise 32x32 tiles and as many waves per tile
-  // (up to 8, at most one per 64-deep k block) as bring the grid to about
-  // 512 waves.  LDS: (S-1) partial tiles, at most 52 KB.
+namespace {
+
+// Router tiling: 64x64 tiles with 4 waves when they alone give the chip at
+// least one workgroup per CU; otherwise 32x32 tiles and as many waves per
+// tile (up to 8, at most one per 64-deep k block) as bring the grid to about
+// 512 waves.  S = waves per tile (0 for the 64x64 tiles, which never split).
+// 32x32 tiles: waves per tile.
+int router_waves32(const Dims& d) {
   const int nkb = d.D / 64;
-  // 16-byte stores of four logits when every row start is 16-byte aligned
-  const int vec4 = (d.E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0);
-  const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
-  if (t64 >= device_cu_count()) {
-    const int S = nkb < 4 ? nkb : 4;
-    dim3 grid((unsigned)((t64 + 7) / 8 * 8));
-    hipLaunchKernelGGL(router_mfma_kernel<64>, grid, dim3(64 * S),
-                       (S - 1) * 64 * 68 * sizeof(float), s, d.N, d.D, d.E, vec4, x, w,
-                       logits);
-    return hipGetLastError();
-  }
   const int64_t t32 = ((d.N + 31) / 32) * ((d.E + 31) / 32);
+  if (t32 <= 0) return 1;
   int S = (int)((512 + t32 - 1) / t32);
   if (S > 8) S = 8;
   if (S > nkb) S = nkb;
   if (S < 1) S = 1;
+  return S;
+}
+
+int router_split_waves(const Dims& d) {
+  const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
+  if (t64 >= device_cu_count()) return 0;
+  return router_waves32(d);
+}
+
+}  // namespace
+
+// Sized without asking the device (workspace sizes are host-only): the 32x32
+// tiles are taken only when the 64x64 ones number fewer than the CUs, and no
+// device has more than 1024.
+size_t router_ws_bytes(const Dims& d) {
+  const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
+  const int S = t64 < 1024 ? router_waves32(d) : 1;
+  return S > 1 ? align_up((size_t)S * d.N * d.E * sizeof(float)) : 0;
+}
+
+hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, float* logits,
+                              float* partials, hipStream_t s) {
+  // LDS: (S-1) partial tiles, at most 52 KB (none in the split form).
+  const int nkb = d.D / 64;
+  // 16-byte stores of four logits when every row start is 16-byte aligned
+  const int vec4 = (d.E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(partials) & 15u) == 0);
+  const int S = router_split_waves(d);
+  if (S == 0) {
+    const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
+    const int S64 = nkb < 4 ? nkb : 4;
+    dim3 grid((unsigned)((t64 + 7) / 8 * 8));
+    hipLaunchKernelGGL(router_mfma_kernel<64>, grid, dim3(64 * S64),
+                       (S64 - 1) * 64 * 68 * sizeof(float), s, d.N, d.D, d.E, vec4, x, w,
+                       logits, 0, (float*)nullptr);
+    return hipGetLastError();
+  }
+  const int64_t t32 = ((d.N + 31) / 32) * ((d.E + 31) / 32);
+  if (partials && S > 1) {
+    // split form: one one-wave workgroup per (tile, wave)
+    dim3 grid((unsigned)((t32 * S + 7) / 8 * 8));
+    hipLaunchKernelGGL(router_mfma_kernel<32>, grid, dim3(64), 0, s, d.N, d.D, d.E, vec4, x, w,
+                       logits, S, partials);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((t32 + 7) / 8 * 8));
   hipLaunchKernelGGL(router_mfma_kernel<32>, grid, dim3(64 * S), (S - 1) * 32 * 36 * sizeof(float), s,
-                     d.N, d.D, d.E, vec4, x, w, logits);
+                     d.N, d.D, d.E, vec4, x, w, logits, 0, (float*)nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const Dims& d, const float* logits, const float* bias, int32_t* ids,
-                       float* weights, hipStream_t s) {
+hipError_t launch_topk(const Dims& d, float* logits, const float* bias, int32_t* ids,
+                       float* weights, const float* partials, hipStream_t s) {
   dim3 grid((unsigned)((d.N + 3) / 4));
   const int epl = (d.E + 63) / 64;
+  const int nparts = partials ? router_split_waves(d) : 0;
+  if (nparts <= 1) partials = nullptr;
 #define MOE_TOPK_CASE(V)                                                                   \
   hipLaunchKernelGGL(topk_kernel<V>, grid, dim3(256), 0, s, d.N, d.E, d.K, d.gating, logits, \
-                     bias, ids, weights)
+                     bias, ids, weights, partials, nparts)
   if (epl <= 1) MOE_TOPK_CASE(1);
   else if (epl <= 2) MOE_TOPK_CASE(2);
   else if (epl <= 4) MOE_TOPK_CASE(4);

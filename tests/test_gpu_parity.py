@@ -15,7 +15,7 @@ from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
 
-from gpu_layer import (DEV, SMALL, Layer, assert_fp_close, bits,  # noqa: E402
+from gpu_layer import (DEV, SMALL, Layer, assert_fp_close, assert_logits_bound, bits,  # noqa: E402
                        check_permutation, check_routing, np_, sample_tokens,
                        check_sampled_outputs)
 import mixture_experts_layer_level_amd as moe  # noqa: E402
@@ -186,3 +186,28 @@ def test_routing_stats_from_a_layer():
         ema, bias = O.routing_stats(counts, ema, bias)
     assert np.allclose(np_(ema_d), ema, rtol=1e-5, atol=1e-9)
     assert np.allclose(np_(bias_d), bias, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("N,D,E,K,gating", [(64, 2048, 128, 8, "softmax"), (17, 640, 45, 3, "sigmoid"),
+                                            (100, 1088, 48, 4, "softmax"), (1, 64, 8, 2, "softmax"),
+                                            (300, 4096, 8, 2, "softmax")])
+def test_route_split_form_is_bit_identical(N, D, E, K, gating):
+    """moe_route given a workspace runs a small router's GEMM split over more
+    workgroups and sums the partial logits in the unsplit kernel's order:
+    logits, ids and weights bit for bit those of the call without one, and
+    logits within the fp32 bound of the exact dot products."""
+    cfg = ms.MoEConfig("r", N=N, D=D, E=E, K=K, F=64, gating=gating, seed=N + D + E)
+    inp = ms.make_inputs(cfg, device=DEV, with_experts=False)
+    p = moe.problem(N, D, 64, E, K, gating)
+    out = []
+    for ws in (None, torch.empty(moe.workspace_size(p), dtype=torch.uint8, device=DEV)):
+        lg = torch.full((N, E), float("nan"), device=DEV)
+        ids = torch.empty(N, K, dtype=torch.int32, device=DEV)
+        w = torch.empty(N, K, device=DEV)
+        moe.route(p, inp["x"], inp["w_router"], None, lg, ids, w, ws)
+        torch.cuda.synchronize()
+        out.append((lg, ids, w))
+    for a, b in zip(*out):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b)
+    assert_logits_bound(np_(out[1][0]), bits(inp["x"]), np_(inp["w_router"]))

@@ -144,6 +144,19 @@ __device__ __forceinline__ int swz(int r) {
   return (r / (128 / BK)) % (BK / 8);
 }
 
+// Whether to fill a persistent launch's last round with extra row tiles
+// (below): only when that round already holds at least an eighth of a round
+// of tiles.  Every extra row tile streams its weight panels once more; with a
+// nearly empty last round the extras cost more than the short tail they
+// remove (DeepSeek-V3-shape down GEMM: 2.44 ms with them, 2.37 without, its
+// last round holding 4 of 256 tiles), with a fuller one they pay (its gate/up
+// GEMM, last round 44% full: 4.03 against 4.14 ms; the Mixtral-shape down
+// GEMM, 25% full: 0.89 against 1.03 ms).
+__device__ __forceinline__ bool fill_last_round(int64_t tiles, int grid) {
+  const int64_t last = tiles - (tiles - 1) / grid * grid;   // tiles in the last round
+  return last * 8 >= grid;
+}
+
 // Work list prologue (wave 0): mstart[e] = row tiles of experts before e,
 // mstart[E] = all row tiles.  Expert e gets at least ceil(m_e / BM) row tiles.
 // With grid > 0 (a launch of grid workgroups that each take every grid-th
@@ -173,7 +186,8 @@ __device__ __forceinline__ void build_work_list(const GemmArgs& p, int32_t* msta
     for (int d = 32; d >= 1; d >>= 1) total += __shfl_xor(total, d, 64);
     const int64_t t0 = (int64_t)total * p.n_tiles;
     const int64_t rounds = (t0 + grid - 1) / grid;
-    for (int64_t extra = (rounds * grid - t0) / p.n_tiles; extra > 0; --extra) {
+    for (int64_t extra = fill_last_round(t0, grid) ? (rounds * grid - t0) / p.n_tiles : 0;
+         extra > 0; --extra) {
       // this lane's candidate: most blocks per row tile, lower expert on ties
       int bb = 0, bt = 1, be = -1;
       for (int i = 0; i < per; ++i) {
@@ -305,7 +319,8 @@ __device__ __forceinline__ int build_work_list_regs(const GemmArgs& p, int (&ms)
     for (int d = 32; d >= 1; d >>= 1) total += __shfl_xor(total, d, 64);
     const int64_t t0 = (int64_t)total * p.n_tiles;
     const int64_t rounds = (t0 + grid - 1) / grid;
-    for (int64_t extra = (rounds * grid - t0) / p.n_tiles; extra > 0; --extra) {
+    for (int64_t extra = fill_last_round(t0, grid) ? (rounds * grid - t0) / p.n_tiles : 0;
+         extra > 0; --extra) {
       int bb = 0, bt = 1, be = -1;
 #pragma unroll
       for (int i = 0; i < PER; ++i) {

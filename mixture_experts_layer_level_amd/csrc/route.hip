@@ -301,6 +301,191 @@ router_mfma_kernel(int64_t N, int D, int E, int vec4, const uint16_t* __restrict
     }
 }
 
+// ------------------------------------------------------------------ router GEMM, LDS-staged
+// For many tokens and E a multiple of 256: a workgroup of 8 waves takes 128
+// tokens x 256 experts and one part of k, and stages both operands through LDS
+// (LDS-DMA, global_load_lds_dwordx4), so each x and weight byte leaves memory
+// once per workgroup instead of once per wave: per 64-deep stage 16 KB of x
+// (bf16) and 64 KB of weights (fp32) feed 128 x 256 x 64 x 3 MACs.  Wave
+// (th, eq) computes tokens [64 th, +64) x experts [64 eq, +64) with the same
+// exact three-way weight split and the same hi / mid+lo accumulators as the
+// kernel above.  Two LDS slots: stage kt+2 is fetched once every wave is done
+// with stage kt.  k is cut into `parts` contiguous parts; a part's partial
+// tile is hi + lo of its accumulators.  Split form (partials != NULL): one
+// workgroup per (tile, part), partial tiles to partials[part] and summed by
+// the top-K kernel in part order.  Otherwise one workgroup per tile runs the
+// parts in order and adds each into logits (part 0 writes it): the same sums
+// in the same order, so both forms give the same logits bit for bit.
+constexpr int kRT = 128, kRE = 256, kRBK = 64;
+constexpr int kRXU4 = kRT * kRBK * 2 / 16;   // x stage: 16 KB
+constexpr int kRWU4 = kRE * kRBK * 4 / 16;   // weight stage: 64 KB
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// One LDS-DMA instruction: lane i moves 16 bytes from base + voff into LDS at
+// lds_addr + 16 i.  Issued through inline asm (the builtin would make the
+// compiler wait for every outstanding DMA before each LDS read); completion
+// is tracked with explicit vmcnt waits.  base must be wave-uniform.
+__device__ __forceinline__ void router_dma16(uint32_t lds_addr, const void* base, uint32_t voff) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  base = reinterpret_cast<const void*>((uint64_t)lo | ((uint64_t)hi << 32));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               ::"s"(lds_addr), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// XOR swizzles of the 16-byte chunks of an LDS row: x rows are 128 bytes (two
+// rows per 256-byte bank window), weight rows 256 bytes; 16 consecutive rows
+// read at one logical chunk hit 16 distinct bank groups.
+__device__ __forceinline__ int rswz_x(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int rswz_w(int r) { return r & 15; }
+
+__global__ void __launch_bounds__(512)
+router_lds_kernel(int64_t N, int D, int E, int parts, int vec4, const uint16_t* __restrict__ x,
+                  const float* __restrict__ w, float* __restrict__ logits,
+                  float* __restrict__ partials) {
+  __shared__ uint4 lx[2][kRXU4];
+  __shared__ uint4 lw[2][kRWU4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool split = partials != nullptr;
+  const int ne = E / kRE;
+  const int64_t tiles = ((N + kRT - 1) / kRT) * ne;
+  const int64_t total = tiles * (split ? parts : 1);
+  int64_t v = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (v >= total) return;
+  int part0 = 0, part1 = parts;
+  if (split) {
+    part0 = (int)(v % parts);
+    part1 = part0 + 1;
+    v /= parts;
+  }
+  const int64_t n0 = (v / ne) * kRT;
+  const int e0 = (int)(v % ne) * kRE;
+  const int th = wave >> 2, eq = wave & 3;
+  const int r = lane & 31, kh = lane >> 5;
+  const int nkb = D / kRBK;
+  const uint32_t ax = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&lx[0][0];
+  const uint32_t aw = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&lw[0][0];
+  const uint16_t* xb = x + n0 * D;          // the tile's first token row
+  const float* wb = w + (int64_t)e0 * D;    // the tile's first expert row
+  // DMA lanes: x instruction q (2 per wave) moves tile rows 8q .. 8q+7, weight
+  // instruction q (8 per wave) rows 4q .. 4q+3; the lane writing LDS chunk p
+  // of row rr fetches global chunk p ^ swizzle(rr).  Rows past N or E read
+  // the last row (their results are not stored).
+  uint32_t offx[2], offw[8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = wave * 2 + j, rr = q * 8 + (lane >> 3), p = lane & 7;
+    const int row = (int)min<int64_t>(rr, N - 1 - n0);
+    offx[j] = ((uint32_t)row * D + (uint32_t)(p ^ rswz_x(rr)) * 8) * 2u;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = wave * 8 + j, rr = q * 4 + (lane >> 4), p = lane & 15;
+    const int row = min(rr, E - 1 - e0);
+    offw[j] = ((uint32_t)row * D + (uint32_t)(p ^ rswz_w(rr)) * 4) * 4u;
+  }
+  auto dma = [&](int slot, int kb) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      router_dma16(ax + (uint32_t)slot * (kRXU4 * 16) + (uint32_t)(wave * 2 + j) * 1024, xb,
+                   offx[j] + (uint32_t)kb * (kRBK * 2));
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      router_dma16(aw + (uint32_t)slot * (kRWU4 * 16) + (uint32_t)(wave * 8 + j) * 1024, wb,
+                   offw[j] + (uint32_t)kb * (kRBK * 4));
+  };
+
+  for (int part = part0; part < part1; ++part) {
+    const int kb0 = (int)((int64_t)part * nkb / parts), kb1 = (int)((int64_t)(part + 1) * nkb / parts);
+    const int nk = kb1 - kb0;
+    f32x16_t acc_hi[2][2], acc_lo[2][2];   // [expert block][token block]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc_hi[i][j][q] = acc_lo[i][j][q] = 0.f;
+    // every wave is past its LDS reads of the previous part
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    dma(0, kb0);
+    if (nk > 1) {
+      dma(1, kb0 + 1);
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");   // stage 0 landed
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_barrier" ::: "memory");
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint4* sx = lx[kt & 1];
+      const uint4* sw = lw[kt & 1];
+#pragma unroll
+      for (int ks = 0; ks < kRBK / 16; ++ks) {
+        const int c = 2 * ks + kh;               // this lane's 8 k: chunk c of x, 2c and 2c+1 of w
+        bf16x8_t xa[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int rr = th * 64 + j * 32 + r;
+          xa[j] = __builtin_bit_cast(bf16x8_t, sx[rr * 8 + (c ^ rswz_x(rr))]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int rr = eq * 64 + i * 32 + r;
+          const uint4 a = sw[rr * 16 + ((2 * c) ^ rswz_w(rr))];
+          const uint4 b = sw[rr * 16 + ((2 * c + 1) ^ rswz_w(rr))];
+          bf16x8_t hi, mid, lo;
+          split3(__builtin_bit_cast(float4, a), __builtin_bit_cast(float4, b), hi, mid, lo);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, xa[j], acc_hi[i][j], 0, 0, 0);
+            acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, xa[j], acc_lo[i][j], 0, 0, 0);
+            acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, xa[j], acc_lo[i][j], 0, 0, 0);
+          }
+        }
+      }
+      // this wave is done with stage kt, and stage kt+1 has landed (nothing
+      // was issued after it)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");
+      if (kt + 2 < nk) dma(kt & 1, kb0 + kt + 2);
+    }
+    // Block (i, j): lane l, register q holds expert 8*(q/4) + 4*(l/32) + q%4
+    // of expert block i and token l%32 of token block j.
+    float* out = split ? partials + (size_t)part * N * E : logits;
+    const bool add = !split && part > 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + th * 64 + j * 32 + r;
+        if (n >= N) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int el = eq * 64 + i * 32 + 8 * g + 4 * kh;
+          float vv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) vv[q] = acc_hi[i][j][4 * g + q] + acc_lo[i][j][4 * g + q];
+          float* dst = out + n * E + e0 + el;
+          if (vec4) {
+            float4 o = make_float4(vv[0], vv[1], vv[2], vv[3]);
+            if (add) {
+              const float4 pv = *reinterpret_cast<const float4*>(dst);
+              o = make_float4(pv.x + o.x, pv.y + o.y, pv.z + o.z, pv.w + o.w);
+            }
+            *reinterpret_cast<float4*>(dst) = o;
+          } else {
+            for (int q = 0; q < 4; ++q) dst[q] = add ? dst[q] + vv[q] : vv[q];
+          }
+        }
+      }
+  }
+}
+
 // ------------------------------------------------------------------ top-K
 // One wave per token.  Lane l holds the keys of experts l, l+64, ... packed as
 // (orderable(key) << 32) | (0xffffffff - e): the unsigned maximum is the
@@ -387,10 +572,33 @@ topk_kernel(int64_t N, int E, int K, int gating, float* __restrict__ logits,
 
 namespace {
 
-// Router tiling: 64x64 tiles with 4 waves when they alone give the chip at
-// least one workgroup per CU; otherwise 32x32 tiles and as many waves per
-// tile (up to 8, at most one per 64-deep k block) as bring the grid to about
-// 512 waves.  S = waves per tile (0 for the 64x64 tiles, which never split).
+// Router tiling.
+//  - E a multiple of 256 and at least 1024 tokens: the LDS-staged kernel, 128
+//    tokens x 256 experts per workgroup, k cut into `parts` parts so that the
+//    launch has about one workgroup per CU of a 256-CU device (the part count
+//    depends on the shape only, so the logits do too).
+//  - else 64x64 tiles with 4 waves when they alone give the chip at least one
+//    workgroup per CU; otherwise 32x32 tiles and as many waves per tile (up to
+//    8, at most one per 64-deep k block) as bring the grid to about 512 waves.
+struct RouterPlan {
+  int kind;    // 0: 64x64 tiles, 1: 32x32 tiles, 2: LDS-staged 128 x 256 tiles
+  int parts;   // kind 1: waves per tile; kind 2: k parts
+};
+
+bool router_lds_ok(const Dims& d) {
+  return d.E % kRE == 0 && d.N >= 1024 && (uint64_t)d.E * d.D * 4 < (1ull << 32);
+}
+
+int router_lds_parts(const Dims& d) {
+  const int nkb = d.D / kRBK;
+  const int64_t tiles = ((d.N + kRT - 1) / kRT) * (d.E / kRE);
+  int p = (int)((256 + tiles - 1) / tiles);
+  if (p > 8) p = 8;
+  if (p > nkb) p = nkb;
+  if (p < 1) p = 1;
+  return p;
+}
+
 // 32x32 tiles: waves per tile.
 int router_waves32(const Dims& d) {
   const int nkb = d.D / 64;
@@ -403,10 +611,11 @@ int router_waves32(const Dims& d) {
   return S;
 }
 
-int router_split_waves(const Dims& d) {
+RouterPlan router_plan(const Dims& d) {
+  if (router_lds_ok(d)) return {2, router_lds_parts(d)};
   const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
-  if (t64 >= device_cu_count()) return 0;
-  return router_waves32(d);
+  if (t64 >= device_cu_count()) return {0, 1};
+  return {1, router_waves32(d)};
 }
 
 }  // namespace
@@ -415,20 +624,34 @@ int router_split_waves(const Dims& d) {
 // tiles are taken only when the 64x64 ones number fewer than the CUs, and no
 // device has more than 1024.
 size_t router_ws_bytes(const Dims& d) {
-  const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
-  const int S = t64 < 1024 ? router_waves32(d) : 1;
+  int S = 1;
+  if (router_lds_ok(d)) {
+    S = router_lds_parts(d);
+  } else {
+    const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
+    if (t64 < 1024) S = router_waves32(d);
+  }
   return S > 1 ? align_up((size_t)S * d.N * d.E * sizeof(float)) : 0;
 }
 
 hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, float* logits,
                               float* partials, hipStream_t s) {
-  // LDS: (S-1) partial tiles, at most 52 KB (none in the split form).
   const int nkb = d.D / 64;
   // 16-byte stores of four logits when every row start is 16-byte aligned
   const int vec4 = (d.E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0) &&
                    ((reinterpret_cast<uintptr_t>(partials) & 15u) == 0);
-  const int S = router_split_waves(d);
-  if (S == 0) {
+  const RouterPlan plan = router_plan(d);
+  if (plan.kind == 2) {
+    const int64_t tiles = ((d.N + kRT - 1) / kRT) * (d.E / kRE);
+    const bool split = partials && plan.parts > 1;
+    const int64_t wgs = tiles * (split ? plan.parts : 1);
+    hipLaunchKernelGGL(router_lds_kernel, dim3((unsigned)((wgs + 7) / 8 * 8)), dim3(512), 0, s,
+                       d.N, d.D, d.E, plan.parts, vec4, x, w, logits,
+                       split ? partials : (float*)nullptr);
+    return hipGetLastError();
+  }
+  if (plan.kind == 0) {
+    // LDS: (S-1) partial tiles, at most 52 KB
     const int64_t t64 = ((d.N + 63) / 64) * ((d.E + 63) / 64);
     const int S64 = nkb < 4 ? nkb : 4;
     dim3 grid((unsigned)((t64 + 7) / 8 * 8));
@@ -437,6 +660,7 @@ hipError_t launch_router_gemm(const Dims& d, const uint16_t* x, const float* w, 
                        logits, 0, (float*)nullptr);
     return hipGetLastError();
   }
+  const int S = plan.parts;
   const int64_t t32 = ((d.N + 31) / 32) * ((d.E + 31) / 32);
   if (partials && S > 1) {
     // split form: one one-wave workgroup per (tile, wave)
@@ -455,7 +679,8 @@ hipError_t launch_topk(const Dims& d, float* logits, const float* bias, int32_t*
                        float* weights, const float* partials, hipStream_t s) {
   dim3 grid((unsigned)((d.N + 3) / 4));
   const int epl = (d.E + 63) / 64;
-  const int nparts = partials ? router_split_waves(d) : 0;
+  const RouterPlan plan = router_plan(d);
+  const int nparts = partials && plan.kind != 0 ? plan.parts : 0;
   if (nparts <= 1) partials = nullptr;
 #define MOE_TOPK_CASE(V)                                                                   \
   hipLaunchKernelGGL(topk_kernel<V>, grid, dim3(256), 0, s, d.N, d.E, d.K, d.gating, logits, \

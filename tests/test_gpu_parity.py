@@ -190,9 +190,14 @@ def test_routing_stats_from_a_layer():
 
 @pytest.mark.parametrize("N,D,E,K,gating", [(64, 2048, 128, 8, "softmax"), (17, 640, 45, 3, "sigmoid"),
                                             (100, 1088, 48, 4, "softmax"), (1, 64, 8, 2, "softmax"),
-                                            (300, 4096, 8, 2, "softmax")])
+                                            (300, 4096, 8, 2, "softmax"),
+                                            # LDS-staged 128 x 256 tiles: a ragged last token
+                                            # tile, two expert tiles, a single k part
+                                            (1100, 640, 256, 8, "sigmoid"),
+                                            (2048, 1088, 512, 6, "softmax"),
+                                            (1024, 64, 256, 2, "softmax")])
 def test_route_split_form_is_bit_identical(N, D, E, K, gating):
-    """moe_route given a workspace runs a small router's GEMM split over more
+    """moe_route given a workspace runs the router GEMM split over more
     workgroups and sums the partial logits in the unsplit kernel's order:
     logits, ids and weights bit for bit those of the call without one, and
     logits within the fp32 bound of the exact dot products."""

@@ -53,10 +53,19 @@ perm_scan_kernel(int NB, int E, int64_t cap, int padded, int32_t* __restrict__ t
   const int e = threadIdx.x;
   int32_t total = 0;
   if (e < E) {
-    for (int b = 0; b < NB; ++b) {
-      const int32_t t = table[(int64_t)b * E + e];
-      table[(int64_t)b * E + e] = total;
-      total += t;
+    // 16 block counts loaded together, then their exclusive prefix stored: the
+    // loads of a group do not wait for one another (with one load and one
+    // store per block the loads went out one round trip apart)
+    constexpr int G = 16;
+    for (int b0 = 0; b0 < NB; b0 += G) {
+      int32_t t[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) t[i] = b0 + i < NB ? table[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        if (b0 + i < NB) table[(int64_t)(b0 + i) * E + e] = total;
+        total += t[i];
+      }
     }
     counts[e] = total;
   }

@@ -56,6 +56,14 @@ SMALL = {
     # k blocks (one takes three), ragged token and expert tiles
     "wide_router": C("wide_router", N=40, D=1088, E=48, K=4, F=128, gating="sigmoid",
                      seed=115),
+    # 1100 tokens of D = 1024: the combine runs one workgroup per token with
+    # the slot rows and weights in scalar registers (padded: with drops)
+    "wide_rows": C("wide_rows", N=1100, D=1024, E=8, K=3, F=128, gating="softmax", seed=116),
+    "wide_rows_padded": C("wide_rows_padded", N=1100, D=1024, E=8, K=3, F=128, gating="sigmoid",
+                          seed=117, zipf_s=1.2, zipf_alpha=1.0, capacity=(1, 2)),
+    # 1040 chunks of 8 values per row: more than one chunk per combine thread
+    "very_wide_rows": C("very_wide_rows", N=1024, D=8320, E=4, K=2, F=64, gating="softmax",
+                        seed=118),
     "padded": C("padded", N=200, D=256, E=8, K=2, F=320, gating="softmax", seed=107,
                 zipf_s=1.2, zipf_alpha=1.0, capacity=(5, 4)),
     "padded_small_rows": C("padded_small_rows", N=60, D=128, E=16, K=2, F=128,

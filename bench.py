@@ -12,8 +12,12 @@ Timing: W untimed warm-up steps, then K timed steps.  Before every timed step
 512 MiB of scratch are written and then read back outside its events (twice
 the 256 MB memory-side cache): no activation or weight of the previous step is
 still cached, and the caches hold clean lines, so the step pays for no
-write-back of the flush's own data.  ``ms_per_step`` is the mean of the K cold
-steps.  K more steps run back to back afterwards and give
+write-back of the flush's own data.  The K cold steps run twice: first as the
+five library calls issued one by one (``eager_ms_per_step``; HIP events
+between the calls give the stage times), then as one HIP graph of those same
+calls captured once and replayed (``graph_ms_per_step``, whose y must equal
+the eager steps' bit for bit).  ``ms_per_step`` is the graph's mean (the
+eager one with ``--eager``).  More steps run back to back afterwards and give
 ``warm_ms_per_step``.
 
 The headline workload is the DeepSeek-V3 layer shape (N=8192, D=7168,
@@ -91,8 +95,9 @@ def roofline(flop, nbytes, ms):
 
 
 class Opts:
-    def __init__(self, padded=False, fused=False, xperm=False, weights="bf16"):
+    def __init__(self, padded=False, fused=False, xperm=False, weights="bf16", graph=True):
         self.padded, self.fused, self.xperm, self.weights = padded, fused, xperm, weights
+        self.graph = graph
 
 
 def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
@@ -155,23 +160,23 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
 
     def rec(ev, i):
         if ev is not None:
-            ev[i].record(stream)
+            ev[i].record(torch.cuda.current_stream())
 
     def gateup():
         if gelu:
             if gather:
                 moe.expert_up_gelu_gathered(p, x, row_token, offsets, inp["w1"], inp["b1"], h,
-                                            stream=stream)
+                                            stream=torch.cuda.current_stream())
             else:
-                moe.expert_up_gelu(p, x_perm, offsets, inp["w1"], inp["b1"], h, stream=stream)
+                moe.expert_up_gelu(p, x_perm, offsets, inp["w1"], inp["b1"], h, stream=torch.cuda.current_stream())
         elif gather and fp8:
-            moe.expert_gateup_fp8_gathered(p, x, row_token, offsets, qg, qu, h, stream=stream)
+            moe.expert_gateup_fp8_gathered(p, x, row_token, offsets, qg, qu, h, stream=torch.cuda.current_stream())
         elif gather:
-            moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=stream)
+            moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=torch.cuda.current_stream())
         elif fp8:
-            moe.expert_gateup_fp8(p, x_perm, offsets, qg, qu, h, stream=stream)
+            moe.expert_gateup_fp8(p, x_perm, offsets, qg, qu, h, stream=torch.cuda.current_stream())
         else:
-            moe.expert_gateup(p, x_perm, offsets, wg, wu, h, stream=stream)
+            moe.expert_gateup(p, x_perm, offsets, wg, wu, h, stream=torch.cuda.current_stream())
 
     # ev: six events per step, recorded on the launch stream before the route
     # and after the route, permute, gate/up (or fused FFN), down and combine
@@ -179,28 +184,28 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         rec(ev, 0)
         if gelu:
             moe.route_mlp(p, x, inp["w_proj"], inp["b_proj"], inp["w_out"], inp["b_out"],
-                          logits, ids, w, ws, features=feats, stream=stream)
+                          logits, ids, w, ws, features=feats, stream=torch.cuda.current_stream())
         else:
-            moe.route(p, x, wr, bias, logits, ids, w, ws, stream=stream)
+            moe.route(p, x, wr, bias, logits, ids, w, ws, stream=torch.cuda.current_stream())
         rec(ev, 1)
         moe.permute(p, x, ids, counts, offsets, row_token, slot_row,
-                    None if (gather or o.fused) else x_perm, ws, stream=stream)
+                    None if (gather or o.fused) else x_perm, ws, stream=torch.cuda.current_stream())
         rec(ev, 2)
         if o.fused:
-            moe.fused_ffn(p, x, row_token, offsets, wg, wu, wd, out_perm, ws, stream=stream)
+            moe.fused_ffn(p, x, row_token, offsets, wg, wu, wd, out_perm, ws, stream=torch.cuda.current_stream())
             rec(ev, 3)
         else:
             gateup()
             rec(ev, 3)
             if gelu:
                 moe.expert_down_bias(p, h, offsets, inp["w2"], inp["b2"], out_perm,
-                                     stream=stream)
+                                     stream=torch.cuda.current_stream())
             elif fp8:
-                moe.expert_down_fp8(p, h, offsets, qd, out_perm, stream=stream)
+                moe.expert_down_fp8(p, h, offsets, qd, out_perm, stream=torch.cuda.current_stream())
             else:
-                moe.expert_down(p, h, offsets, wd, out_perm, stream=stream)
+                moe.expert_down(p, h, offsets, wd, out_perm, stream=torch.cuda.current_stream())
         rec(ev, 4)
-        moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=stream)
+        moe.unpermute_combine(p, out_perm, slot_row, w, y, stream=torch.cuda.current_stream())
         rec(ev, 5)
 
     if gather:
@@ -238,13 +243,47 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         step(evs[i])
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
+
+    def check_fused(when):
+        if o.fused:
+            off = moe.fused_error_offset(p, whole_layer=False)
+            err_word = int(ws[off:off + 4].view(torch.int32).item())
+            if err_word != 0:
+                raise SystemExit(f"fused FFN: a bounded wait ran out during the {when} "
+                                 f"(error word {err_word}); its results are wrong")
+    check_fused("timed steps")
+
+    # The same step captured once as a HIP graph (every library call of the
+    # step, nothing else; the library allocates nothing and issues no memset
+    # or host synchronisation), replayed cold like the eager steps.  y of the
+    # replays must equal y of the eager steps bit for bit.
+    graph_ms = None
+    post_steps = 0
+    if o.graph:
+        y_eager = y.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        y.zero_()
+        for _ in range(2):
+            g.replay()
+        gevs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+                for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            flush()
+            gevs[i][0].record(stream)
+            g.replay()
+            gevs[i][1].record(stream)
+        torch.cuda.synchronize()
+        graph_ms = sum(a_.elapsed_time(b_) for a_, b_ in gevs) / steps
+        if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+            raise SystemExit(f"{cfg.name}: y of the graph replays differs from the eager steps")
+        check_fused("graph replays")
+        post_steps = 2 + steps
+        del y_eager
     del scratch, sink
-    if o.fused:
-        off = moe.fused_error_offset(p, whole_layer=False)
-        err_word = int(ws[off:off + 4].view(torch.int32).item())
-        if err_word != 0:
-            raise SystemExit(f"fused FFN: a bounded wait ran out during the timed steps "
-                             f"(error word {err_word}); its results are wrong")
 
     def stage_ms(i, j):
         return sum(ev[i].elapsed_time(ev[j]) for ev in evs) / steps
@@ -258,10 +297,17 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(warm_steps):
-            step()
+            if o.graph:
+                g.replay()
+            else:
+                step()
         b.record(stream)
         torch.cuda.synchronize()
         warm_ms = a.elapsed_time(b) / warm_steps
+        post_steps += warm_steps
+    eager_ms = ms_step
+    if graph_ms is not None:
+        ms_step = graph_ms
 
     counts_h = counts.cpu().numpy().astype(np.int64)
     kept = int(np.minimum(counts_h, capv).sum()) if capv else cfg.S
@@ -336,6 +382,8 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                                       if fp8 else "bf16"),
                    "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
                               else "SwiGLU"),
+                   "launch": ("the step's library calls captured once as a HIP graph and "
+                              "replayed" if o.graph else "eager library calls"),
                    "ffn_launch": ("fused (one persistent launch)" if o.fused else
                                   "two grouped GEMMs, rows of the first gathered from x"
                                   if gather else "two grouped GEMMs")},
@@ -343,6 +391,8 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         "unit": "tokens/s",
         "ms_per_step": ms_step,
         "warm_ms_per_step": warm_ms,
+        "eager_ms_per_step": eager_ms,
+        "graph_ms_per_step": graph_ms,
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "weight_stream_gbps": weight_bytes / (ms_step * 1e-3) / 1e9,
@@ -353,10 +403,13 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         "stages": stages,
         "roofline": roof,
         "timed_wall_s": wall_s,
-        "pre_steps": pre_steps,
+        # whole steps of this run before the eager timed ones, and after them
+        # (graph replays and warm steps), for kernel-trace summaries
+        "trace_layout": {"pre_steps": pre_steps, "timed_steps": steps,
+                         "post_steps": post_steps},
     }
-    log(f"{cfg.name}{suffix}: {ms_step:.3f} ms/step cold (warm {warm_ms or 0:.3f}), "
-        f"gate/up {gateup_ms:.3f} ms, down {down_ms:.3f} ms")
+    log(f"{cfg.name}{suffix}: {ms_step:.3f} ms/step cold (eager {eager_ms:.3f}, warm "
+        f"{warm_ms or 0:.3f}), gate/up {gateup_ms:.3f} ms, down {down_ms:.3f} ms")
     return res, inp
 
 
@@ -383,6 +436,9 @@ def main():
                     help="write the permuted copy of x and run the first expert GEMM on it; by "
                          "default that GEMM reads its rows of x through row_token wherever the "
                          "library takes the shape")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager steps only (by default the step is also captured as "
+                         "a HIP graph and ms_per_step is the graph's cold replay)")
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
@@ -396,8 +452,11 @@ def main():
                          "kernel, the launches of the timed steps (after --pre-steps whole "
                          "steps, --steps of them); prints a markdown table")
     ap.add_argument("--pre-steps", type=int, default=None,
-                    help="with --trace-summary: whole steps before the timed ones (the trial "
-                         "step plus the warm-up steps: 1 + --warmup of the profiled run)")
+                    help="with --trace-summary: whole steps before the timed ones "
+                         "(trace_layout.pre_steps of the profiled run)")
+    ap.add_argument("--post-steps", type=int, default=None,
+                    help="with --trace-summary: whole steps after the timed ones "
+                         "(trace_layout.post_steps of the profiled run)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
                                                        "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="only summarise four rocprofv3 --pmc runs (the workload's FETCH_SIZE "
@@ -406,8 +465,10 @@ def main():
     ap.add_argument("--label", default=None, help="kernel label for --pmc-summary's traffic line")
     args = ap.parse_args()
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.pre_steps, args.steps,
-                      args.steps if args.warm_steps is None else args.warm_steps)
+        if args.pre_steps is None or args.post_steps is None:
+            raise SystemExit("--trace-summary needs --pre-steps and --post-steps (the "
+                             "trace_layout of the profiled run's JSON line)")
+        trace_summary(args.trace_summary, args.pre_steps, args.steps, args.post_steps)
         return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, label=args.label)
@@ -432,7 +493,8 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     cfg = ms.CONFIGS[args.config]
-    head, inp = run_layer(cfg, Opts(args.padded, args.fused, args.xperm, args.weights),
+    head, inp = run_layer(cfg, Opts(args.padded, args.fused, args.xperm, args.weights,
+                                    not args.eager),
                           args.steps, args.warmup, warm_steps, log)
     line = {
         "metric": "MoE-layer tokens/sec + TFLOPS (% bf16 MFMA peak) / HBM GB/s (% peak), 1 GPU",
@@ -449,9 +511,12 @@ def main():
         "data": "synthetic (seeded counter-based draws, random-init weights)",
         "config": head["config"],
         "timing": "each timed step cold: 512 MiB scratch written then read outside its HIP "
-                  "events; warm_ms_per_step: the same steps back to back",
+                  "events; ms_per_step: the step as one HIP graph replay (eager_ms_per_step: "
+                  "the library calls issued one by one); warm_ms_per_step: steps back to back",
+        "trace_layout": head["trace_layout"],
     }
-    for k in ("warm_ms_per_step", "tflops", "pct_bf16_mfma_peak", "weight_stream_gbps",
+    for k in ("warm_ms_per_step", "eager_ms_per_step", "graph_ms_per_step", "tflops",
+              "pct_bf16_mfma_peak", "weight_stream_gbps",
               "pct_hbm_peak_weights", "ffn_weight_stream_gbps", "max_expert_rows",
               "dropped_slots", "stages", "roofline"):
         line[k] = head[k]
@@ -472,11 +537,13 @@ def main():
             name, _, mode = item.partition(":")
             if name == cfg.name and (mode == "padded") == args.padded:
                 continue
-            res, inp = run_layer(ms.CONFIGS[name], Opts(padded=mode == "padded"), args.steps,
+            res, inp = run_layer(ms.CONFIGS[name],
+                                 Opts(padded=mode == "padded", graph=not args.eager), args.steps,
                                  args.warmup, warm_steps, log)
             del inp
             torch.cuda.empty_cache()
-            keep = ("workload", "value", "unit", "ms_per_step", "warm_ms_per_step", "tflops",
+            keep = ("workload", "value", "unit", "ms_per_step", "warm_ms_per_step",
+                    "eager_ms_per_step", "graph_ms_per_step", "tflops",
                     "pct_bf16_mfma_peak", "weight_stream_gbps", "pct_hbm_peak_weights",
                     "max_expert_rows", "dropped_slots", "stages", "roofline")
             extras[name + ("_padded" if mode == "padded" else "")] = {k: res[k] for k in keep}
@@ -597,9 +664,10 @@ def _short(name: str) -> str:
     return n.strip()
 
 
-def trace_summary(d: str, pre_steps, steps: int, warm_steps: int):
-    """Per libmoe kernel: the launches of the timed steps of a profiled run
-    (pre_steps whole steps, then the `steps` timed ones, then `warm_steps`).
+def trace_summary(d: str, pre_steps, steps: int, post_steps: int):
+    """Per libmoe kernel: the launches of the eager timed steps of a profiled
+    run (pre_steps whole steps, then the `steps` timed ones, then post_steps
+    more: graph replays and warm steps).
     A kernel launched c times per step has its first pre_steps * c launches
     skipped and the next steps * c taken; c = its launches / all steps."""
     files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
@@ -616,7 +684,7 @@ def trace_summary(d: str, pre_steps, steps: int, warm_steps: int):
     if pre_steps is None:
         raise SystemExit("--pre-steps is needed")
     counts = {k: len(v) for k, v in launches.items()}
-    total_steps = pre_steps + steps + warm_steps
+    total_steps = pre_steps + steps + post_steps
     out = []
     layer = 0.0
     for name, v in launches.items():

@@ -501,6 +501,10 @@ __device__ __forceinline__ float from_orderable(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+// Parts of a split router: waves per 32x32 tile or k parts of the LDS
+// tiles, both capped at 8.
+constexpr int kMaxParts = 8;
+
 // With partials (the split router), each logit is first summed from its
 // nparts partials in order and written to logits.
 template <int EPL>
@@ -519,8 +523,16 @@ topk_kernel(int64_t N, int E, int K, int gating, float* __restrict__ logits,
     pk[j] = 0;
     if (e < E) {
       if (partials) {
-        float lg = partials[n * E + e];
-        for (int q = 1; q < nparts; ++q) lg += partials[(size_t)q * N * E + n * E + e];
+        // all parts' loads go out before the first add (at most kMaxParts
+        // parts); the sum then runs in part order
+        float pv[kMaxParts];
+#pragma unroll
+        for (int q = 0; q < kMaxParts; ++q)
+          pv[q] = q < nparts ? partials[(size_t)q * N * E + n * E + e] : 0.f;
+        float lg = pv[0];
+#pragma unroll
+        for (int q = 1; q < kMaxParts; ++q)
+          if (q < nparts) lg += pv[q];
         row[e] = lg;
       }
       float key = row[e];
@@ -593,7 +605,7 @@ int router_lds_parts(const Dims& d) {
   const int nkb = d.D / kRBK;
   const int64_t tiles = ((d.N + kRT - 1) / kRT) * (d.E / kRE);
   int p = (int)((256 + tiles - 1) / tiles);
-  if (p > 8) p = 8;
+  if (p > kMaxParts) p = kMaxParts;
   if (p > nkb) p = nkb;
   if (p < 1) p = 1;
   return p;
@@ -605,7 +617,7 @@ int router_waves32(const Dims& d) {
   const int64_t t32 = ((d.N + 31) / 32) * ((d.E + 31) / 32);
   if (t32 <= 0) return 1;
   int S = (int)((512 + t32 - 1) / t32);
-  if (S > 8) S = 8;
+  if (S > kMaxParts) S = kMaxParts;
   if (S > nkb) S = nkb;
   if (S < 1) S = 1;
   return S;

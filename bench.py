@@ -253,17 +253,34 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                                  f"(error word {err_word}); its results are wrong")
     check_fused("timed steps")
 
-    # The same step captured once as a HIP graph (every library call of the
-    # step, nothing else; the library allocates nothing and issues no memset
-    # or host synchronisation), replayed cold like the eager steps.  y of the
-    # replays must equal y of the eager steps bit for bit.
+    # The layer as the library's one-call forward (moe_forward, or its FP8,
+    # fused or GELU form), captured once as a HIP graph (the library allocates
+    # nothing and issues no memset or host synchronisation) and replayed cold
+    # like the eager steps.  It computes the same sums in the same order as
+    # the staged calls: y of the replays must equal y of the eager steps bit
+    # for bit.  (--xperm: the staged calls themselves, since moe_forward
+    # skips the permuted copy wherever it can.)
+    def layer():
+        s_ = torch.cuda.current_stream()
+        if o.xperm:
+            step()
+        elif o.fused:
+            moe.forward_fused(p, x, wr, bias, wg, wu, wd, y, ws, stream=s_)
+        elif gelu:
+            moe.forward_gelu(p, x, inp["w_proj"], inp["b_proj"], inp["w_out"], inp["b_out"],
+                             inp["w1"], inp["b1"], inp["w2"], inp["b2"], y, ws, stream=s_)
+        elif fp8:
+            moe.forward_fp8(p, x, wr, bias, qg, qu, qd, y, ws, stream=s_)
+        else:
+            moe.forward(p, x, wr, bias, wg, wu, wd, y, ws, stream=s_)
+
     graph_ms = None
     post_steps = 0
     if o.graph:
         y_eager = y.clone()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step()
+            layer()
         torch.cuda.synchronize()
         y.zero_()
         for _ in range(2):
@@ -279,7 +296,8 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         torch.cuda.synchronize()
         graph_ms = sum(a_.elapsed_time(b_) for a_, b_ in gevs) / steps
         if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
-            raise SystemExit(f"{cfg.name}: y of the graph replays differs from the eager steps")
+            raise SystemExit(f"{cfg.name}: y of the graph replays differs from the eager "
+                             f"staged steps")
         check_fused("graph replays")
         post_steps = 2 + steps
         del y_eager
@@ -382,8 +400,8 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                                       if fp8 else "bf16"),
                    "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
                               else "SwiGLU"),
-                   "launch": ("the step's library calls captured once as a HIP graph and "
-                              "replayed" if o.graph else "eager library calls"),
+                   "launch": ("moe_forward (one call) captured once as a HIP graph and replayed"
+                              if o.graph else "the five staged library calls, eager"),
                    "ffn_launch": ("fused (one persistent launch)" if o.fused else
                                   "two grouped GEMMs, rows of the first gathered from x"
                                   if gather else "two grouped GEMMs")},

@@ -54,10 +54,20 @@ def test_staged_path_small(name):
     ref = O.forward(x_bits, wr, bias, wg, wu, wd, cfg.K, cfg.gating,
                     cap=(L.cap if padded else None), logits=np_(L.logits))
     assert_fp_close(y, ref["y"], "y (layer)")
-    # moe_forward runs the same kernels: bit-identical to the staged calls
+    # moe_forward runs the same kernels (the router in its split form on the
+    # workspace, bit-identical by construction): bit-identical to the staged
+    # calls, routing outputs included
     y2 = torch.empty_like(L.y)
     L.forward(y2)
     assert torch.equal(y2.view(torch.int16), L.y.view(torch.int16))
+    outs = {k: torch.full_like(getattr(L, k), -7) for k in ("logits", "ids", "w", "counts",
+                                                            "offsets")}
+    moe.forward(L.p, L.x, L.w_router, L.bias, L.w_gate, L.w_up, L.w_down, y2, L.ws,
+                logits=outs["logits"], topk_ids=outs["ids"], topk_weights=outs["w"],
+                counts=outs["counts"], offsets=outs["offsets"])
+    torch.cuda.synchronize()
+    for k, v in outs.items():
+        assert torch.equal(v.view(torch.uint8), getattr(L, k).view(torch.uint8)), k
 
 
 @pytest.mark.parametrize("E,K,kind", [(3, 1, "ties"), (8, 2, "ties"), (64, 8, "zeros_nan"),

@@ -244,14 +244,16 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
 
-    def check_fused(when):
+    def check_fused(when, whole_layer):
+        # the error word of moe_fused_ffn (staged) or moe_forward_fused (whole
+        # layer), at its offset in the workspace
         if o.fused:
-            off = moe.fused_error_offset(p, whole_layer=False)
+            off = moe.fused_error_offset(p, whole_layer=whole_layer)
             err_word = int(ws[off:off + 4].view(torch.int32).item())
             if err_word != 0:
                 raise SystemExit(f"fused FFN: a bounded wait ran out during the {when} "
                                  f"(error word {err_word}); its results are wrong")
-    check_fused("timed steps")
+    check_fused("timed steps", False)
 
     # The layer as the library's one-call forward (moe_forward, or its FP8,
     # fused or GELU form), captured once as a HIP graph (the library allocates
@@ -298,7 +300,7 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
             raise SystemExit(f"{cfg.name}: y of the graph replays differs from the eager "
                              f"staged steps")
-        check_fused("graph replays")
+        check_fused("graph replays", True)
         post_steps = 2 + steps
         del y_eager
     del scratch, sink
@@ -323,6 +325,7 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         torch.cuda.synchronize()
         warm_ms = a.elapsed_time(b) / warm_steps
         post_steps += warm_steps
+        check_fused("warm steps", o.graph)
     eager_ms = ms_step
     if graph_ms is not None:
         ms_step = graph_ms
@@ -481,6 +484,10 @@ def main():
                          "and WRITE_SIZE, then those of --calib-copy-mib 1024) into HBM bytes "
                          "per launch; prints a markdown table and the traffic line")
     ap.add_argument("--label", default=None, help="kernel label for --pmc-summary's traffic line")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="only summarise rocprofv3 --pmc runs (one or more output folders): "
+                         "per libmoe kernel, each counter's average over its dispatches, and "
+                         "the derived fractions named in the table's notes; prints markdown")
     args = ap.parse_args()
     if args.trace_summary:
         if args.pre_steps is None or args.post_steps is None:
@@ -490,6 +497,9 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, label=args.label)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.calib_copy_mib > 0:
         calib_copy(args.calib_copy_mib)
@@ -740,6 +750,53 @@ def _pmc_avg(d: str, counter: str):
             name = _short(r.get("Kernel_Name", ""))
             acc.setdefault(name, []).append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def counter_summary(dirs, cus=256, xcds=8):
+    """Average of every counter per libmoe kernel over the runs under dirs,
+    plus derived fractions where their counters are present:
+      - SQ_* / SQ_WAVE_CYCLES (shares of the cycles waves are resident);
+      - TA/TD busy = xcds * *_BUSY_sum / (cus * GRBM_GUI_ACTIVE) (GRBM_GUI_ACTIVE
+        reads the kernel's cycles summed over the XCDs);
+      - L2 hit = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)."""
+    vals = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            for r in _rows(f):
+                name = _short(r.get("Kernel_Name", ""))
+                if not _is_libmoe(name):
+                    continue
+                vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    counters = sorted({c for v in vals.values() for c in v})
+    derived = []
+    if "SQ_WAVE_CYCLES" in counters:
+        derived += [(f"{c} / SQ_WAVE_CYCLES", (lambda a, c=c: a[c] / a["SQ_WAVE_CYCLES"]))
+                    for c in counters if c.startswith("SQ_") and c not in
+                    ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES") and not c.startswith("SQ_INSTS")]
+    if "GRBM_GUI_ACTIVE" in counters:
+        for c in ("TA_TA_BUSY_sum", "TD_TD_BUSY_sum"):
+            if c in counters:
+                derived.append((c.split("_")[0] + " busy",
+                                (lambda a, c=c: xcds * a[c] / (cus * a["GRBM_GUI_ACTIVE"]))))
+    if "TCC_HIT_sum" in counters and "TCC_MISS_sum" in counters:
+        derived.append(("L2 hit", lambda a: a["TCC_HIT_sum"] /
+                        max(1.0, a["TCC_HIT_sum"] + a["TCC_MISS_sum"])))
+    cols = counters + [n for n, _ in derived]
+    print("| kernel | " + " | ".join(cols) + " |")
+    print("|---|" + "---|" * len(cols))
+    for name in sorted(vals, key=lambda k: -max(sum(v) / len(v) for v in vals[k].values())):
+        avg = {c: sum(v) / len(v) for c, v in vals[name].items()}
+        cells = [f"{avg[c]:.4g}" if c in avg else "" for c in counters]
+        for _, fn in derived:
+            try:
+                cells.append(f"{fn(avg):.3f}")
+            except (KeyError, ZeroDivisionError):
+                cells.append("")
+        print(f"| `{name}` | " + " | ".join(cells) + " |")
 
 
 def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, label=None):

@@ -82,3 +82,59 @@ def test_staged_graph_replays_match_eager(name, padded):
             assert torch.equal(getattr(L, k).view(torch.uint8), v.view(torch.uint8)), \
                 f"replay {rep}: {k} differs from the eager staged path"
         L.staged()   # eager work between the replays
+
+
+def _quantize(w):
+    rows, cols = w.shape[-2], w.shape[-1]
+    codes = torch.empty(w.shape, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(w.shape[0], rows // 32, cols // 32, 32, dtype=torch.uint8, device=DEV)
+    moe.quantize_fp8(w.numel() // cols, cols, w, codes, scales)
+    return codes, scales
+
+
+@pytest.mark.parametrize("kind", ["fp8", "fused", "gelu"])
+def test_forward_variants_graph_replays_match_eager(kind):
+    """moe_forward_fp8 (split-ring-sized rows), moe_forward_fused and
+    moe_forward_gelu captured once and replayed with eager calls between."""
+    if kind == "gelu":
+        from gpu_layer import GeluLayer
+        L = GeluLayer(ms.CONFIGS["gelu_tiny"])
+        i = L.inp
+
+        def call(out):
+            moe.forward_gelu(L.p, i["x"], i["w_proj"], i["b_proj"], i["w_out"], i["b_out"],
+                             i["w1"], i["b1"], i["w2"], i["b2"], out, L.ws)
+        N, D = L.cfg.N, L.cfg.D
+    else:
+        L = Layer(SMALL["mid_tiles" if kind == "fused" else "large_tiles"])
+        if kind == "fp8":
+            q = [_quantize(w) for w in (L.w_gate, L.w_up, L.w_down)]
+
+            def call(out):
+                moe.forward_fp8(L.p, L.x, L.w_router, L.bias, q[0], q[1], q[2], out, L.ws)
+        else:
+            def call(out):
+                moe.forward_fused(L.p, L.x, L.w_router, L.bias, L.w_gate, L.w_up, L.w_down,
+                                  out, L.ws)
+        N, D = L.cfg.N, L.cfg.D
+    y_eager = torch.empty(N, D, dtype=torch.bfloat16, device=DEV)
+    call(y_eager)
+    torch.cuda.synchronize()
+    ref = bits(y_eager)
+    y = torch.zeros(N, D, dtype=torch.bfloat16, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(y)
+    torch.cuda.synchronize()
+    other = torch.empty_like(y)
+    for rep in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y), ref), f"{kind}: replay {rep} differs from eager"
+        call(other)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(other), ref)
+    if kind == "fused":
+        off = moe.fused_error_offset(L.p, whole_layer=True)
+        assert int(L.ws[off:off + 4].view(torch.int32).item()) == 0

@@ -367,6 +367,58 @@ __device__ __forceinline__ int build_work_list_regs(const GemmArgs& p, int (&ms)
   return __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
 }
 
+// XCD parts of about equal cost, in whole rounds.  A tile costs about
+// kTileFixedBlocks 32-row blocks' worth of time whatever its rows plus its
+// row blocks; an expert's tiles cost n_tiles * (kTileFixedBlocks * mt + nbk)
+// in all.  The list is cut where the running cost crosses x/8 of the total
+// (proportionally inside that expert), and each cut is then rounded to a
+// multiple of the XCD's workgroup count, so that every workgroup of an XCD
+// still runs the same number of tiles.  Which workgroup runs a tile changes
+// no result.
+constexpr int kTileFixedBlocks = 4;
+
+// First tile of XCD x's part (x in [0, 8]) from the register work list of
+// build_work_list_regs; wgs: workgroups per XCD.
+template <int BM, int PER>
+__device__ __forceinline__ int xcd_begin_regs(const GemmArgs& p, const int (&ms)[PER], int total,
+                                              int lane, int x, int wgs) {
+  const int e0 = lane * PER;
+  const int next = __shfl_down(ms[0], 1, 64);           // mstart of the next lane's first
+  int mt[PER], c[PER];
+  int64_t local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = e0 + i;
+    int nb = 0;
+    if (e < p.E) nb = (p.offsets[e + 1] - p.offsets[e] + 31) / 32;
+    const int ms1 = i + 1 < PER ? ms[i + 1] : (lane == 63 ? total : next);
+    mt[i] = e < p.E ? (e + 1 < p.E ? ms1 : total) - ms[i] : 0;
+    c[i] = kTileFixedBlocks * mt[i] + nb;
+    local += c[i];
+  }
+  int64_t incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
+  }
+  const int64_t all = __shfl(incl, 63, 64);
+  const int tiles = p.n_tiles * total;
+  if (x >= 8 || all == 0) return x >= 8 ? tiles : 0;
+  const int64_t T = all * x / 8;
+  int64_t run = incl - local;
+  int pos = -1;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (c[i] > 0 && run <= T && T < run + c[i])
+      pos = p.n_tiles * ms[i] + (int)((T - run) * (int64_t)(p.n_tiles * mt[i]) / c[i]);
+    run += c[i];
+  }
+  const uint64_t hit = __ballot(pos >= 0);
+  pos = __shfl(pos, __ffsll((unsigned long long)hit) - 1, 64);
+  return min(tiles, (pos + wgs / 2) / wgs * wgs);
+}
+
 // mstart[e] from the registers of build_work_list_regs (e <= E, uniform).
 template <int PER>
 __device__ __forceinline__ int mstart_at(const int (&ms)[PER], int e, int E, int total) {
@@ -1205,10 +1257,12 @@ grouped_gemm_split(GemmArgs p) {
   const uint32_t addr_b = (uint32_t)(uintptr_t)(lds_void_t*)&lb[0][0];
   int ms[PER];
   const int mt_total = build_work_list_regs<BM, PER>(p, ms, lane, gridDim.x);
-  const int total = p.n_tiles * mt_total;
   const int xcd = blockIdx.x & 7, P8 = gridDim.x >> 3, j0 = blockIdx.x >> 3;
-  const int begin = (int)((int64_t)total * xcd / 8);
-  const int end = (int)((int64_t)total * (xcd + 1) / 8);
+  // (the same value in every lane; readfirstlane lets the compiler see it)
+  const int begin = __builtin_amdgcn_readfirstlane(
+      xcd_begin_regs<BM, PER>(p, ms, mt_total, lane, xcd, P8));
+  const int end = __builtin_amdgcn_readfirstlane(
+      xcd_begin_regs<BM, PER>(p, ms, mt_total, lane, xcd + 1, P8));
   for (int l = begin + j0; l < end; l += P8)
     split_tile<BM, BN, WM, WN, BK, SB, EPI>(p, decode_tile_regs<BM, PER>(p, ms, mt_total, lane, l),
                                             la, lb, addr_a, addr_b, wave, lane);

@@ -377,6 +377,57 @@ __device__ __forceinline__ int build_work_list_regs(const GemmArgs& p, int (&ms)
 // no result.
 constexpr int kTileFixedBlocks = 4;
 
+// The cut for XCD x (x in [0, 8]) from this lane's experts: ms = their first
+// row tile, mt = their row tiles, c = their cost, local = sum of c.
+template <int N>
+__device__ __forceinline__ int xcd_cut(int n_tiles, int total, const int (&ms)[N],
+                                       const int (&mt)[N], const int (&c)[N], int64_t local,
+                                       int lane, int x, int wgs) {
+  int64_t incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
+  }
+  const int64_t all = __shfl(incl, 63, 64);
+  const int tiles = n_tiles * total;
+  if (x >= 8 || all == 0) return x >= 8 ? tiles : 0;
+  const int64_t T = all * x / 8;
+  int64_t run = incl - local;
+  int pos = -1;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (c[i] > 0 && run <= T && T < run + c[i])
+      pos = n_tiles * ms[i] + (int)((T - run) * (int64_t)(n_tiles * mt[i]) / c[i]);
+    run += c[i];
+  }
+  const uint64_t hit = __ballot(pos >= 0);
+  pos = __shfl(pos, __ffsll((unsigned long long)hit) - 1, 64);
+  return min(tiles, (pos + wgs / 2) / wgs * wgs);
+}
+
+// First tile of XCD x's part (x in [0, 8]) from the LDS work list of
+// build_work_list (mstart[e], e <= E <= 1024); wgs: workgroups per XCD.
+__device__ __forceinline__ int xcd_begin_lds(const GemmArgs& p, const int32_t* mstart, int lane,
+                                             int x, int wgs) {
+  constexpr int N = 16;                     // experts per lane, E <= 1024
+  const int per = (p.E + 63) / 64;
+  int ms[N], mt[N], c[N];
+  int64_t local = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int e = lane * per + i;
+    ms[i] = mt[i] = c[i] = 0;
+    if (i < per && e < p.E) {
+      ms[i] = mstart[e];
+      mt[i] = mstart[e + 1] - mstart[e];
+      c[i] = kTileFixedBlocks * mt[i] + (p.offsets[e + 1] - p.offsets[e] + 31) / 32;
+      local += c[i];
+    }
+  }
+  return xcd_cut<N>(p.n_tiles, mstart[p.E], ms, mt, c, local, lane, x, wgs);
+}
+
 // First tile of XCD x's part (x in [0, 8]) from the register work list of
 // build_work_list_regs; wgs: workgroups per XCD.
 template <int BM, int PER>
@@ -396,27 +447,7 @@ __device__ __forceinline__ int xcd_begin_regs(const GemmArgs& p, const int (&ms)
     c[i] = kTileFixedBlocks * mt[i] + nb;
     local += c[i];
   }
-  int64_t incl = local;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int64_t t = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += t;
-  }
-  const int64_t all = __shfl(incl, 63, 64);
-  const int tiles = p.n_tiles * total;
-  if (x >= 8 || all == 0) return x >= 8 ? tiles : 0;
-  const int64_t T = all * x / 8;
-  int64_t run = incl - local;
-  int pos = -1;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (c[i] > 0 && run <= T && T < run + c[i])
-      pos = p.n_tiles * ms[i] + (int)((T - run) * (int64_t)(p.n_tiles * mt[i]) / c[i]);
-    run += c[i];
-  }
-  const uint64_t hit = __ballot(pos >= 0);
-  pos = __shfl(pos, __ffsll((unsigned long long)hit) - 1, 64);
-  return min(tiles, (pos + wgs / 2) / wgs * wgs);
+  return xcd_cut<PER>(p.n_tiles, total, ms, mt, c, local, lane, x, wgs);
 }
 
 // mstart[e] from the registers of build_work_list_regs (e <= E, uniform).
@@ -1012,10 +1043,21 @@ grouped_gemm_ring(GemmArgs p) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0];
   if (wave == 0) build_work_list<BM>(p, mstart, lane, gridDim.x);
   __syncthreads();
-  const int total = p.n_tiles * __builtin_amdgcn_readfirstlane(mstart[p.E]);
   const int xcd = blockIdx.x & 7, P8 = gridDim.x >> 3, j0 = blockIdx.x >> 3;
-  const int begin = (int)((int64_t)total * xcd / 8);
-  const int end = (int)((int64_t)total * (xcd + 1) / 8);
+  // Prefill tiles: XCD parts of equal cost in whole rounds (the same value in
+  // every lane; readfirstlane lets the compiler see it).  Decode tiles all
+  // cost the same and keep parts of equal counts (the cost cut, rounded to
+  // whole rounds, put every XCD exactly 16 experts apart and made the decode
+  // gate/up GEMM 14% slower).
+  int begin, end;
+  if constexpr (BM >= 128) {
+    begin = __builtin_amdgcn_readfirstlane(xcd_begin_lds(p, mstart, lane, xcd, P8));
+    end = __builtin_amdgcn_readfirstlane(xcd_begin_lds(p, mstart, lane, xcd + 1, P8));
+  } else {
+    const int total = p.n_tiles * __builtin_amdgcn_readfirstlane(mstart[p.E]);
+    begin = (int)((int64_t)total * xcd / 8);
+    end = (int)((int64_t)total * (xcd + 1) / 8);
+  }
   for (int l = begin + j0; l < end; l += P8)
     ring_tile<BM, BN, WM, WN, BK, S, EPI, FP8, false, SPREAD>(p, decode_tile<BM>(p, mstart, l),
                                                               lds, lds_addr, wave, lane);

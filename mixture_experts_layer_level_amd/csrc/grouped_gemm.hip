@@ -17,10 +17,11 @@
 // Tiles are ordered expert-major; within an expert, row tiles go in bands of
 // up to eight, and a band runs panel by panel with the row tile fastest, so
 // consecutive tiles share a weight panel and nearby ones share A rows.  The
-// grid is persistent (a multiple
-// of 8 workgroups); workgroup b runs on XCD b % 8 and each XCD walks its own
-// contiguous eighth of the list, so the row tiles that share a weight panel
-// meet in the same L2.
+// grid is persistent (a multiple of 8 workgroups); workgroup b runs on XCD
+// b % 8 and each XCD walks its own contiguous part of the list (of equal
+// modelled cost, in whole rounds, for the 128- and 256-row tiles; of equal
+// tile counts for the 32-row ones), so the row tiles that share a weight
+// panel meet in the same L2.
 //
 // Three kernels:
 //   grouped_gemm_split (256 x 256 tiles, bf16 weights, E <= 256): separate

@@ -28,9 +28,13 @@ shape -- run after it in the same process and are reported under
 ``cpu_baseline`` is the C++ oracle on a bounded sample of the headline
 workload's tokens, on the host's cores.
 
-``--config gelu_mlp`` runs the pages' other layer (MLP router, GELU experts);
-``--weights fp8`` reads block-scaled FP8 expert weights; ``--fused`` runs the
-expert FFN as one persistent launch.
+The SwiGLU layers read their expert weights packed by moe_pack_weights (the
+same bf16 values in the order the GEMMs stream them, written once when the
+weights are loaded; the outputs are bit for bit those of the unpacked calls);
+``--weights bf16`` reads the nn.Linear stacks in place and ``--weights fp8``
+block-scaled FP8 copies.  ``--config gelu_mlp`` runs the pages' other layer
+(MLP router, GELU experts, bf16 weights in place); ``--fused`` runs the
+expert FFN as one persistent launch (bf16 weights in place).
 
 Also: ``--trace-summary DIR`` and ``--pmc-summary ...`` turn rocprofv3 output
 of a profiled run of this script into the tables kept under profiles/.
@@ -151,6 +155,16 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
             return c, sc
         qg, qu, qd = quant(wg), quant(wu), quant(wd)
         torch.cuda.synchronize()
+    packed = o.weights == "packed"
+    if packed:
+        # the same bf16 weights in the library's packed stage-image order
+        def pack(kind, w0, w1=None):
+            buf = torch.empty(moe.packed_weight_size(p, kind) // 2, dtype=torch.bfloat16,
+                              device=dev)
+            moe.pack_weights(p, kind, w0, w1, buf, stream=stream)
+            return buf
+        pgu, pdn = pack(moe.PACK_GATEUP, wg, wu), pack(moe.PACK_DOWN, wd)
+        torch.cuda.synchronize()
 
     # The first expert GEMM reads its rows of x through row_token wherever the
     # library takes the shape; it refuses, before any launch, the shapes whose
@@ -171,6 +185,11 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                 moe.expert_up_gelu(p, x_perm, offsets, inp["w1"], inp["b1"], h, stream=torch.cuda.current_stream())
         elif gather and fp8:
             moe.expert_gateup_fp8_gathered(p, x, row_token, offsets, qg, qu, h, stream=torch.cuda.current_stream())
+        elif gather and packed:
+            moe.expert_gateup_packed_gathered(p, x, row_token, offsets, pgu, h,
+                                              stream=torch.cuda.current_stream())
+        elif packed:
+            moe.expert_gateup_packed(p, x_perm, offsets, pgu, h, stream=torch.cuda.current_stream())
         elif gather:
             moe.expert_gateup_gathered(p, x, row_token, offsets, wg, wu, h, stream=torch.cuda.current_stream())
         elif fp8:
@@ -202,6 +221,9 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                                      stream=torch.cuda.current_stream())
             elif fp8:
                 moe.expert_down_fp8(p, h, offsets, qd, out_perm, stream=torch.cuda.current_stream())
+            elif packed:
+                moe.expert_down_packed(p, h, offsets, pdn, out_perm,
+                                       stream=torch.cuda.current_stream())
             else:
                 moe.expert_down(p, h, offsets, wd, out_perm, stream=torch.cuda.current_stream())
         rec(ev, 4)
@@ -273,6 +295,8 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                              inp["w1"], inp["b1"], inp["w2"], inp["b2"], y, ws, stream=s_)
         elif fp8:
             moe.forward_fp8(p, x, wr, bias, qg, qu, qd, y, ws, stream=s_)
+        elif packed:
+            moe.forward_packed(p, x, wr, bias, pgu, pdn, y, ws, stream=s_)
         else:
             moe.forward(p, x, wr, bias, wg, wu, wd, y, ws, stream=s_)
 
@@ -348,6 +372,7 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
     gu_flops = 2.0 * gu_mats * D * F * kept
     gu_bytes = gu_mats * touched * F * D * wb + kept * D * 2 + kept * F * 2
     suffix = ("_padded" if capv else "") + ("_fp8" if fp8 else "") + \
+        ("_packed" if packed else "") + \
              ("_xperm" if o.xperm else "")
     if o.fused:
         # the one fused launch: gate/up, SwiGLU and down of every expert
@@ -400,7 +425,8 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                    "tokens": N, "hidden": D, "experts": E, "top_k": K, "ffn": F,
                    "gating": cfg.gating, "capacity": capv or None,
                    "expert_weights": ("fp8 e4m3, power-of-two scale per 32 values"
-                                      if fp8 else "bf16"),
+                                      if fp8 else "bf16, packed stage images" if packed
+                                      else "bf16"),
                    "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
                               else "SwiGLU"),
                    "launch": ("moe_forward (one call) captured once as a HIP graph and replayed"
@@ -460,8 +486,10 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="time the eager steps only (by default the step is also captured as "
                          "a HIP graph and ms_per_step is the graph's cold replay)")
-    ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
-                    help="expert weight storage: bf16, or block-scaled FP8 (E4M3 + E8M0)")
+    ap.add_argument("--weights", choices=("bf16", "fp8", "packed"), default=None,
+                    help="expert weight storage: bf16 stacks read in place, block-scaled FP8 "
+                         "(E4M3 + E8M0), or the same bf16 values packed as the GEMMs' stage "
+                         "images (default; bf16 for the GELU layer and --fused)")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the CPU-oracle sample (-1: a per-workload default of about "
                          "10-30 s of CPU work; 0: skip the CPU baseline)")
@@ -521,6 +549,8 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     cfg = ms.CONFIGS[args.config]
+    if args.weights is None:
+        args.weights = "bf16" if (cfg.expert == "gelu" or args.fused) else "packed"
     head, inp = run_layer(cfg, Opts(args.padded, args.fused, args.xperm, args.weights,
                                     not args.eager),
                           args.steps, args.warmup, warm_steps, log)
@@ -560,13 +590,14 @@ def main():
     torch.cuda.empty_cache()
 
     extras = {}
-    if args.extra and args.extra != "none" and not (args.fused or args.weights != "bf16"):
+    if args.extra and args.extra != "none" and not (args.fused or args.weights == "fp8"):
         for item in args.extra.split(","):
             name, _, mode = item.partition(":")
             if name == cfg.name and (mode == "padded") == args.padded:
                 continue
             res, inp = run_layer(ms.CONFIGS[name],
-                                 Opts(padded=mode == "padded", graph=not args.eager), args.steps,
+                                 Opts(padded=mode == "padded", weights=args.weights,
+                                      graph=not args.eager), args.steps,
                                  args.warmup, warm_steps, log)
             del inp
             torch.cuda.empty_cache()

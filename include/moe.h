@@ -405,6 +405,63 @@ moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float*
                            int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
                            int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------ packed bf16 weights */
+/* Expert weights in this library's packed layout: the same bf16 values as
+ * the nn.Linear stacks, reordered once (at load time) so that the grouped
+ * GEMMs of "MoE 推理完整机制" (zoe.im) 第二层 范式 A ("关键 kernel: Grouped
+ * GEMM") stream every weight stage as one contiguous block.  The pages fix no
+ * storage order; this one is the image each 256-row, 64-deep weight stage
+ * has in the kernels' LDS:
+ *   - a stack is cut into column panels: gate/up panels of 128 columns of h
+ *     (the 128 gate rows and the matching 128 up rows, interleaved in blocks
+ *     of 32: gate rows for even blocks, up rows for odd ones), down panels
+ *     of 256 output columns;
+ *   - each panel into 64-deep stages along the contraction dimension;
+ *   - each stage is 32768 bytes: row r of the panel (0..255) at bytes
+ *     [128 r, 128 r + 128), its 8 chunks of 8 values stored with chunk c at
+ *     position c ^ ((r / 2) % 8);
+ *   - stages in the order (expert, panel, stage).  Rows past the matrix
+ *     (F % 128 != 0 for gate/up, D % 256 != 0 for down) repeat its last row.
+ * The layout is an internal format: write it with moe_pack_weights only.  The
+ * packed entry points give bit-identical results to the bf16 ones on the
+ * weights that were packed. */
+typedef enum { MOE_PACK_GATEUP = 0, MOE_PACK_DOWN = 1 } moe_pack_kind;
+
+/* Bytes of a packed stack of `kind` for problem p (host; N is ignored):
+ * E * ceil(F / 128) * (D / 64) * 32768 for MOE_PACK_GATEUP,
+ * E * ceil(D / 256) * (F / 64) * 32768 for MOE_PACK_DOWN. */
+moe_status moe_packed_weight_size(const moe_problem* p, int32_t kind, size_t* bytes);
+
+/* Pack a stack: MOE_PACK_GATEUP reads w0 = W_gate and w1 = W_up [E, F, D]
+ * bf16, MOE_PACK_DOWN reads w0 = W_down [E, D, F] (w1 unused, may be NULL).
+ * packed: moe_packed_weight_size bytes, written whole.  All pointers 16-byte
+ * aligned (MOE_ERR_UNSUPPORTED else).  A copy: the output depends only on
+ * the input bits.  Needs no workspace; runs whatever num_tokens is. */
+moe_status moe_pack_weights(const moe_problem* p, int32_t kind, const uint16_t* w0,
+                            const uint16_t* w1, uint16_t* packed, void* stream);
+
+/* moe_expert_gateup / moe_expert_gateup_gathered / moe_expert_down /
+ * moe_forward with packed stacks in place of the bf16 ones: w_gateup_packed
+ * from MOE_PACK_GATEUP, w_down_packed from MOE_PACK_DOWN, both 16-byte
+ * aligned.  Everything else -- shapes, layouts, row coverage, workspace,
+ * errors -- as in the bf16 calls, and the outputs are bit for bit theirs. */
+moe_status moe_expert_gateup_packed(const moe_problem* p, const uint16_t* x_perm,
+                                    const int32_t* expert_offsets,
+                                    const uint16_t* w_gateup_packed, uint16_t* h, void* stream);
+moe_status moe_expert_gateup_packed_gathered(const moe_problem* p, const uint16_t* x,
+                                             const int32_t* row_token,
+                                             const int32_t* expert_offsets,
+                                             const uint16_t* w_gateup_packed, uint16_t* h,
+                                             void* stream);
+moe_status moe_expert_down_packed(const moe_problem* p, const uint16_t* h,
+                                  const int32_t* expert_offsets, const uint16_t* w_down_packed,
+                                  uint16_t* out_perm, void* stream);
+moe_status moe_forward_packed(const moe_problem* p, const uint16_t* x, const float* w_router,
+                              const float* expert_bias, const uint16_t* w_gateup_packed,
+                              const uint16_t* w_down_packed, uint16_t* y, float* logits,
+                              int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                              int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------ routing statistics */
 
 /* Router load statistics and dynamic expert bias ("MoE 大规模分布式推理工程实战"

@@ -16,15 +16,19 @@ from ._lib import (  # noqa: F401
     expert_down,
     expert_down_bias,
     expert_down_fp8,
+    expert_down_packed,
     expert_gateup,
     expert_gateup_gathered,
     expert_gateup_fp8,
     expert_gateup_fp8_gathered,
+    expert_gateup_packed,
+    expert_gateup_packed_gathered,
     expert_up_gelu,
     expert_up_gelu_gathered,
     forward,
     forward_fp8,
     forward_fused,
+    forward_packed,
     forward_static,
     forward_gelu,
     fused_error_offset,
@@ -34,6 +38,10 @@ from ._lib import (  # noqa: F401
     grouped_ffn_gelu,
     lib,
     library_path,
+    pack_weights,
+    packed_weight_size,
+    PACK_DOWN,
+    PACK_GATEUP,
     permute,
     permuted_rows,
     problem,

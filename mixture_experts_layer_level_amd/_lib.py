@@ -104,6 +104,18 @@ def _load():
     L.moe_forward_fp8.restype = ctypes.c_int
     L.moe_forward_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, sz, vp]
+    L.moe_packed_weight_size.restype = ctypes.c_int
+    L.moe_packed_weight_size.argtypes = [P, ctypes.c_int32, ctypes.POINTER(sz)]
+    L.moe_pack_weights.restype = ctypes.c_int
+    L.moe_pack_weights.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp]
+    L.moe_expert_gateup_packed.restype = ctypes.c_int
+    L.moe_expert_gateup_packed.argtypes = [P, vp, vp, vp, vp, vp]
+    L.moe_expert_gateup_packed_gathered.restype = ctypes.c_int
+    L.moe_expert_gateup_packed_gathered.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_down_packed.restype = ctypes.c_int
+    L.moe_expert_down_packed.argtypes = [P, vp, vp, vp, vp, vp]
+    L.moe_forward_packed.restype = ctypes.c_int
+    L.moe_forward_packed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     return L
 
 
@@ -284,6 +296,52 @@ def forward_fp8(p, x, w_router, bias, w_gate, w_up, w_down, y, ws, logits=None, 
                                _ptr(w_down[0]), _ptr(w_down[1]), _ptr(y), _ptr(logits),
                                _ptr(topk_ids), _ptr(topk_weights), _ptr(counts), _ptr(offsets),
                                _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+# Packed bf16 weights (moe_pack_weights): the same values in the kernels'
+# stage-image order; kind PACK_GATEUP (gate and up) or PACK_DOWN.
+
+PACK_GATEUP, PACK_DOWN = 0, 1       # moe_pack_kind
+
+
+def packed_weight_size(p, kind) -> int:
+    n = ctypes.c_size_t()
+    _check("moe_packed_weight_size",
+           lib.moe_packed_weight_size(ctypes.byref(p), int(kind), ctypes.byref(n)))
+    return n.value
+
+
+def pack_weights(p, kind, w0, w1, packed, stream=None):
+    _check("moe_pack_weights", lib.moe_pack_weights(ctypes.byref(p), int(kind), _ptr(w0), _ptr(w1),
+                                                    _ptr(packed), _stream(stream)))
+
+
+def expert_gateup_packed(p, x_perm, offsets, w_gateup, h, stream=None):
+    _check("moe_expert_gateup_packed",
+           lib.moe_expert_gateup_packed(ctypes.byref(p), _ptr(x_perm), _ptr(offsets),
+                                        _ptr(w_gateup), _ptr(h), _stream(stream)))
+
+
+def expert_gateup_packed_gathered(p, x, row_token, offsets, w_gateup, h, stream=None):
+    _check("moe_expert_gateup_packed_gathered",
+           lib.moe_expert_gateup_packed_gathered(ctypes.byref(p), _ptr(x), _ptr(row_token),
+                                                 _ptr(offsets), _ptr(w_gateup), _ptr(h),
+                                                 _stream(stream)))
+
+
+def expert_down_packed(p, h, offsets, w_down, out_perm, stream=None):
+    _check("moe_expert_down_packed",
+           lib.moe_expert_down_packed(ctypes.byref(p), _ptr(h), _ptr(offsets), _ptr(w_down),
+                                      _ptr(out_perm), _stream(stream)))
+
+
+def forward_packed(p, x, w_router, bias, w_gateup, w_down, y, ws, logits=None, topk_ids=None,
+                   topk_weights=None, counts=None, offsets=None, stream=None):
+    _check("moe_forward_packed",
+           lib.moe_forward_packed(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
+                                  _ptr(w_gateup), _ptr(w_down), _ptr(y), _ptr(logits),
+                                  _ptr(topk_ids), _ptr(topk_weights), _ptr(counts),
+                                  _ptr(offsets), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 # GELU experts and the MLP router.

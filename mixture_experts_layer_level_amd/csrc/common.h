@@ -66,21 +66,30 @@ hipError_t launch_permute(const Dims& d, const uint16_t* x, const int32_t* ids, 
                           int32_t* offsets, int32_t* row_token, int32_t* slot_row,
                           uint16_t* x_perm, void* ws, hipStream_t s);
 
-// grouped_gemm.hip
+// grouped_gemm.hip.  packed: wg (gate/up) or wd (down) is a packed stack
+// from launch_pack_weights (wu unused).
 size_t ffn_ws_bytes(const Dims& d);  // h when the caller gives none
 hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                 const uint16_t* wg, const uint16_t* wu, uint16_t* h,
-                                hipStream_t s);
+                                hipStream_t s, bool packed = false);
 hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
-                              const uint16_t* wd, uint16_t* out_perm, hipStream_t s);
+                              const uint16_t* wd, uint16_t* out_perm, hipStream_t s,
+                              bool packed = false);
 bool gateup_gather_supported(const Dims& d, bool fp8 = false);
 hipError_t launch_expert_gateup_gathered(const Dims& d, const uint16_t* x,
                                          const int32_t* row_token, const int32_t* offsets,
                                          const uint16_t* wg, const uint16_t* wu, uint16_t* h,
-                                         hipStream_t s);
+                                         hipStream_t s, bool packed = false);
 hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                               const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
-                              uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s);
+                              uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s,
+                              bool packed = false);
+// Packed bf16 weight stacks: gate/up (w0 = W_gate, w1 = W_up, [E, F, D]) or
+// down (w0 = W_down [E, D, F]) as the 32 KB LDS images of their 256-row,
+// 64-deep weight stages, in (expert, column tile, stage) order.
+size_t packed_weight_bytes(const Dims& d, bool gateup);
+hipError_t launch_pack_weights(const Dims& d, bool gateup, const uint16_t* w0, const uint16_t* w1,
+                               uint16_t* out, hipStream_t s);
 
 // Block-scaled FP8 weights of one matrix stack [E, rows, cols]: E4M3 codes
 // [E, rows, cols] and scale bytes [E, rows/32, cols/32, 32].

@@ -71,7 +71,23 @@ struct GemmArgs {
   const uint8_t* S1;        // FP8 only: scales of B1
   const float* bias;        // bias epilogues: [E, Nout] fp32
   const int32_t* gather;    // ring kernels: A row r is A[gather[r]] (NULL: A[r])
+  int wpack;                // bf16 only: B0 holds the packed weight panels (B1 unused)
 };
+
+// Packed bf16 weights: for each expert e, column tile nt and 64-deep stage kt
+// (in that order) the 32 KB image that a 256-row weight stage has in LDS.
+// Byte 1024 q + 16 l of a stage image holds tile row 8 q + l / 8, chunk
+// (l % 8) ^ swz(row) of its 64 k values, so every LDS-DMA instruction of a
+// stage reads 1 KB of contiguous memory and a stage 32 KB: HBM streams long
+// runs at a higher rate than 128-byte pieces of rows 2D bytes apart (on one
+// MI355X: 4.83 TB/s for 128-byte pieces of 256 rows, 6.13 for 512-byte
+// pieces, 6.35 for whole rows).  Gate/up panels hold the interleaved gate
+// and up rows of weight_row.  Rows past Nout repeat the last row, as the
+// unpacked DMA clamps them.
+constexpr uint32_t kPackStage = 32768;   // bytes of one stage image (256 rows x 64 k)
+__device__ __forceinline__ size_t packed_panel(const GemmArgs& p, int e, int nt, int nk) {
+  return ((size_t)e * p.n_tiles + nt) * (size_t)nk * kPackStage;
+}
 
 // Epilogues: what a tile writes to C.
 constexpr int kEpiSwiglu = 0;    // gate/up tile (interleaved Wg/Wu rows): bf16(silu(g) * u)
@@ -945,7 +961,13 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
     bool up;
     const int wrow = min(weight_row<BN, GATEUP>(t.nt, g0, up) + lrb, p.Nout - 1);
     const char* b = static_cast<const char*>(up ? p.B1 : p.B0);
-    if (FP8) {
+    if constexpr (!FP8) {
+      static_assert(R::B_U4 * 16 == kPackStage && R::RPIB * R::CHB == 64, "packed stage image");
+    }
+    if (!FP8 && p.wpack) {
+      base[PWA + jb] = static_cast<const char*>(p.B0) + packed_panel(p, t.e, t.nt, nk);
+      off[PWA + jb] = q * 1024 + lane * 16;
+    } else if (FP8) {
       base[PWA + jb] = b + (size_t)t.e * wmat;
       off[PWA + jb] = (uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz_rows<R::BRB>(trow)) * 16;
     } else {
@@ -971,11 +993,14 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
   }
   // lds_addr: LDS byte address of lds[0][0] (taken where the array is
   // declared, so no generic-pointer conversion is needed here)
+  // per-stage advance of a weight DMA source (a packed stage image, or BRB
+  // bytes of a row)
+  const uint32_t badv = !FP8 && p.wpack ? kPackStage : R::BRB;
   auto dma = [&](int s, int kt) {
     const uint32_t l0 = lds_addr + (uint32_t)s * (R::STAGE_U4 * 16);
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
-      const uint32_t adv = j < PWA ? BK * 2 : j < PWA + PWB ? R::BRB : R::KB * 32;
+      const uint32_t adv = j < PWA ? BK * 2 : j < PWA + PWB ? badv : R::KB * 32;
       const uint32_t la = __builtin_amdgcn_readfirstlane(l0 + ldso[j]);
       if (FP8 && j == PW - 1) {
         if (lane < R::LS) lds_dma16<UNIFORM>(la, base[j], off[j] + (uint32_t)kt * adv);
@@ -1000,7 +1025,7 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
 #pragma unroll
       for (int i = 0; i < PW; ++i) {
         if (i != j) continue;
-        const uint32_t adv = i < PWA ? BK * 2 : i < PWA + PWB ? R::BRB : R::KB * 32;
+        const uint32_t adv = i < PWA ? BK * 2 : i < PWA + PWB ? badv : R::KB * 32;
         const uint32_t la = __builtin_amdgcn_readfirstlane(l0 + ldso[i]);
         if (FP8 && i == PW - 1) {
           if (lane < R::LS) lds_dma16<UNIFORM>(la, base[i], off[i] + (uint32_t)kt * adv);
@@ -1219,14 +1244,23 @@ __device__ __forceinline__ void split_tile(const GemmArgs& p, const Tile& t,
     offa[j] = (src * p.Kd + (uint32_t)(lca ^ swz<BK>(trow)) * 8) * 2u;
     ldsa[j] = q * 1024;
   }
+  static_assert(R::B_U4 * 16 == kPackStage && R::RPIB * R::CHB == 64, "packed stage image");
+  // per-stage advance of a weight DMA source: 64 k values of a row, or a
+  // packed stage image
+  const uint32_t bstep = p.wpack ? kPackStage : BK * 2;
 #pragma unroll
   for (int jb = 0; jb < PWB; ++jb) {
     const int q = wave * PWB + jb;
     const int g0 = q * R::RPIB, trow = g0 + lrb;
-    bool up;
-    const int wrow = min(weight_row<BN, GATEUP>(t.nt, g0, up) + lrb, p.Nout - 1);
-    baseb[jb] = static_cast<const char*>(up ? p.B1 : p.B0) + (size_t)t.e * wmat * 2;
-    offb[jb] = ((uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz<BK>(trow)) * 8) * 2u;
+    if (p.wpack) {
+      baseb[jb] = static_cast<const char*>(p.B0) + packed_panel(p, t.e, t.nt, nk);
+      offb[jb] = q * 1024 + lane * 16;
+    } else {
+      bool up;
+      const int wrow = min(weight_row<BN, GATEUP>(t.nt, g0, up) + lrb, p.Nout - 1);
+      baseb[jb] = static_cast<const char*>(up ? p.B1 : p.B0) + (size_t)t.e * wmat * 2;
+      offb[jb] = ((uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz<BK>(trow)) * 8) * 2u;
+    }
     ldsb[jb] = q * 1024;
   }
   auto dma_a = [&](int s, int kt) {
@@ -1241,7 +1275,7 @@ __device__ __forceinline__ void split_tile(const GemmArgs& p, const Tile& t,
 #pragma unroll
     for (int jb = 0; jb < PWB; ++jb)
       lds_dma16<UNIFORM>(__builtin_amdgcn_readfirstlane(l0 + ldsb[jb]), baseb[jb],
-                offb[jb] + (uint32_t)kt * (BK * 2));
+                offb[jb] + (uint32_t)kt * bstep);
   };
 
   // single instructions: A instruction j, weight instruction jb (the callers
@@ -1260,7 +1294,7 @@ __device__ __forceinline__ void split_tile(const GemmArgs& p, const Tile& t,
     for (int i = 0; i < PWB; ++i)
       if (i == jb)
         lds_dma16<UNIFORM>(__builtin_amdgcn_readfirstlane(l0 + ldsb[i]), baseb[i],
-                  offb[i] + (uint32_t)kt * (BK * 2));
+                  offb[i] + (uint32_t)kt * bstep);
   };
 
   f32x16_t acc[MB][NB];
@@ -1546,7 +1580,7 @@ __device__ __forceinline__ void stage_gload(uint4 (&ra)[NA], uint4 (&rb)[NB_], u
                                             const char* b0_base, const char* b1_base,
                                             const uint32_t (&b_off)[NB_], const uint8_t* s0_base,
                                             const uint8_t* s1_base, const uint32_t (&s_off)[NB_],
-                                            uint32_t b_up, int kt) {
+                                            uint32_t b_up, uint32_t bstep, int kt) {
 #pragma unroll
   for (int i = 0; i < NA; ++i)
     ra[i] = *reinterpret_cast<const uint4*>(a_base + a_off[i] + kt * RBK);
@@ -1557,7 +1591,7 @@ __device__ __forceinline__ void stage_gload(uint4 (&ra)[NA], uint4 (&rb)[NB_], u
       rb[i] = *reinterpret_cast<const uint4*>((up ? b1_base : b0_base) + b_off[i] + kt * RBK);
       rs[i] = (up ? s1_base : s0_base)[s_off[i] + kt * (RBK / 32) * 32];
     } else {
-      rb[i] = *reinterpret_cast<const uint4*>((up ? b1_base : b0_base) + b_off[i] + kt * RBK * 2);
+      rb[i] = *reinterpret_cast<const uint4*>((up ? b1_base : b0_base) + b_off[i] + kt * bstep);
     }
   }
 }
@@ -1636,8 +1670,20 @@ grouped_gemm_regs(GemmArgs p) {
     }
     uint32_t a_off[A_LD], b_off[B_LD], s_off[B_LD];
     uint32_t b_up = 0;                               // bit i: load i reads the up matrix
+    const int nk = p.Kd / RBK;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) a_off[i] = (uint32_t)min(lrow + i * RPP, t.rows - 1) * p.Kd;
+    // per-stage advance of a weight load: 64 k values of a row, or a packed
+    // stage image (whose row r holds, at chunk c ^ swz(r), the row's chunk c)
+    uint32_t bstep = RBK * 2;
+    if constexpr (!FP8) {
+      static_assert(BN * RCH * 16 == (int)kPackStage, "packed stage image");
+      if (p.wpack) {
+        bstep = kPackStage;
+        b0_base = static_cast<const char*>(p.B0) + packed_panel(p, t.e, t.nt, nk);
+        b1_base = b0_base;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       bool up;
@@ -1646,6 +1692,10 @@ grouped_gemm_regs(GemmArgs p) {
               p.Nout - 1);
       b_up |= (uint32_t)up << i;
       b_off[i] = (uint32_t)wrow * p.Kd * ebytes;
+      if (!FP8 && p.wpack) {
+        const int r = lrow + i * RPP;
+        b_off[i] = (uint32_t)(r * RCH + (lchunk ^ swz<RBK>(r))) * 16;
+      }
       s_off[i] = (uint32_t)(wrow >> 5) * (uint32_t)p.Kd + (uint32_t)(wrow & 31);
     }
 
@@ -1653,17 +1703,16 @@ grouped_gemm_regs(GemmArgs p) {
     zero(acc);
     uint4 ra[A_LD], rb[B_LD];
     uint32_t rs[B_LD];
-    const int nk = p.Kd / RBK;
     // Stage 0 is rewritten below: wait until every wave is done with the
     // previous tile's last stage.
     __syncthreads();
     stage_gload<A_LD, B_LD, FP8>(ra, rb, rs, a_base, a_off, b0_base, b1_base, b_off, s0_base,
-                                 s1_base, s_off, b_up, 0);
+                                 s1_base, s_off, b_up, bstep, 0);
     stage_lstore<A_LD, B_LD, RPP, QRPP, BM, FP8>(lds[0], ra, rb, rs, lrow, lchunk, qrow, qchunk);
     __syncthreads();
     for (int kt = 0; kt + 1 < nk; ++kt) {
       stage_gload<A_LD, B_LD, FP8>(ra, rb, rs, a_base, a_off, b0_base, b1_base, b_off, s0_base,
-                                   s1_base, s_off, b_up, kt + 1);
+                                   s1_base, s_off, b_up, bstep, kt + 1);
       bf16x8_t af[MB], bfr[NB];
 #pragma unroll
       for (int ks = 0; ks < RBK / 16; ++ks) {
@@ -1802,9 +1851,10 @@ hipError_t launch_gemm(const Dims& d, const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                 const uint16_t* wg, const uint16_t* wu, uint16_t* h,
-                                hipStream_t s) {
-  return launch_gemm<kEpiSwiglu, false>(d, GemmArgs{x_perm, wg, wu, h, offsets, d.E, d.D, d.F, 0,
-                                   nullptr, nullptr}, s);
+                                hipStream_t s, bool packed) {
+  GemmArgs a{x_perm, wg, wu, h, offsets, d.E, d.D, d.F, 0, nullptr, nullptr};
+  a.wpack = packed;
+  return launch_gemm<kEpiSwiglu, false>(d, a, s);
 }
 
 // The LDS-DMA ring and split-ring tiles can read A rows through row_token;
@@ -1817,25 +1867,81 @@ bool gateup_gather_supported(const Dims& d, bool fp8) {
 hipError_t launch_expert_gateup_gathered(const Dims& d, const uint16_t* x,
                                          const int32_t* row_token, const int32_t* offsets,
                                          const uint16_t* wg, const uint16_t* wu, uint16_t* h,
-                                         hipStream_t s) {
+                                         hipStream_t s, bool packed) {
   if (!gateup_gather_supported(d)) return hipErrorNotSupported;
-  return launch_gemm<kEpiSwiglu, false>(d, GemmArgs{x, wg, wu, h, offsets, d.E, d.D, d.F, 0,
-                                   nullptr, nullptr, nullptr, row_token}, s);
+  GemmArgs a{x, wg, wu, h, offsets, d.E, d.D, d.F, 0, nullptr, nullptr, nullptr, row_token};
+  a.wpack = packed;
+  return launch_gemm<kEpiSwiglu, false>(d, a, s);
 }
 
 hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
-                              const uint16_t* wd, uint16_t* out_perm, hipStream_t s) {
-  return launch_gemm<kEpiStore, false>(d, GemmArgs{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D,
-                                 0, nullptr, nullptr}, s);
+                              const uint16_t* wd, uint16_t* out_perm, hipStream_t s,
+                              bool packed) {
+  GemmArgs a{h, wd, nullptr, out_perm, offsets, d.E, d.F, d.D, 0, nullptr, nullptr};
+  a.wpack = packed;
+  return launch_gemm<kEpiStore, false>(d, a, s);
 }
 
 hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                               const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
-                              uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s) {
+                              uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s,
+                              bool packed) {
   if (!h) h = static_cast<uint16_t*>(ws);
-  hipError_t e = launch_expert_gateup(d, x_perm, offsets, wg, wu, h, s);
+  hipError_t e = launch_expert_gateup(d, x_perm, offsets, wg, wu, h, s, packed);
   if (e != hipSuccess) return e;
-  return launch_expert_down(d, h, offsets, wd, out_perm, s);
+  return launch_expert_down(d, h, offsets, wd, out_perm, s, packed);
+}
+
+namespace {
+// One 16-byte chunk of the packed image per item, grid-stride: the chunk that
+// the unpacked weight DMA fetches for that LDS position (see kPackStage).
+template <bool GATEUP>
+__global__ void __launch_bounds__(256)
+pack_weights_kernel(const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, int Nout,
+                    int Kd, int n_tiles, int64_t chunks, uint4* __restrict__ out) {
+  const int nk = Kd / 64;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * 256) {
+    const int64_t stage = c >> 11;                     // 2048 chunks per stage image
+    const int w = (int)(c & 2047), q = w >> 6, l = w & 63;
+    const int kt = (int)(stage % nk);
+    const int64_t panel = stage / nk;
+    const int nt = (int)(panel % n_tiles);
+    const int64_t e = panel / n_tiles;
+    const int trow = q * 8 + (l >> 3);
+    bool up;
+    const int wrow = min(weight_row<256, GATEUP>(nt, q * 8, up) + (l >> 3), Nout - 1);
+    const uint16_t* src = (up ? w1 : w0) + (e * Nout + wrow) * (int64_t)Kd + kt * 64 +
+                          ((l & 7) ^ swz<64>(trow)) * 8;
+    out[c] = *reinterpret_cast<const uint4*>(src);
+  }
+}
+
+// Column tiles of a packed stack: 128 columns of h per gate/up panel, 256
+// output columns per down panel.
+inline int64_t pack_tiles(const Dims& d, bool gateup) {
+  return gateup ? (d.F + 127) / 128 : (d.D + 255) / 256;
+}
+}  // namespace
+
+size_t packed_weight_bytes(const Dims& d, bool gateup) {
+  const int64_t kd = gateup ? d.D : d.F;
+  return (size_t)d.E * pack_tiles(d, gateup) * (kd / 64) * kPackStage;
+}
+
+hipError_t launch_pack_weights(const Dims& d, bool gateup, const uint16_t* w0, const uint16_t* w1,
+                               uint16_t* out, hipStream_t s) {
+  const int Nout = gateup ? d.F : d.D, Kd = gateup ? d.D : d.F;
+  const int64_t chunks = (int64_t)(packed_weight_bytes(d, gateup) / 16);
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, (int64_t)device_cu_count() * 8);
+  if (gateup)
+    hipLaunchKernelGGL(pack_weights_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, w0, w1,
+                       Nout, Kd, (int)pack_tiles(d, true), chunks, reinterpret_cast<uint4*>(out));
+  else
+    hipLaunchKernelGGL(pack_weights_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, w0,
+                       w0, Nout, Kd, (int)pack_tiles(d, false), chunks,
+                       reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_expert_gateup_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,

@@ -575,6 +575,112 @@ moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float*
                       });
 }
 
+moe_status moe_packed_weight_size(const moe_problem* p, int32_t kind, size_t* bytes) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!bytes || (kind != MOE_PACK_GATEUP && kind != MOE_PACK_DOWN)) return MOE_ERR_INVALID_ARG;
+  *bytes = packed_weight_bytes(d, kind == MOE_PACK_GATEUP);
+  return MOE_OK;
+}
+
+moe_status moe_pack_weights(const moe_problem* p, int32_t kind, const uint16_t* w0,
+                            const uint16_t* w1, uint16_t* packed, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  const bool gateup = kind == MOE_PACK_GATEUP;
+  if ((!gateup && kind != MOE_PACK_DOWN) || !w0 || (gateup && !w1) || !packed)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w0) || (gateup && !aligned16(w1)) || !aligned16(packed))
+    return MOE_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_pack_weights(d, gateup, w0, gateup ? w1 : w0, packed,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_gateup_packed(const moe_problem* p, const uint16_t* x_perm,
+                                    const int32_t* expert_offsets,
+                                    const uint16_t* w_gateup_packed, uint16_t* h, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !w_gateup_packed || !h) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w_gateup_packed) || !aligned16(h))
+    return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_gateup(d, x_perm, expert_offsets, w_gateup_packed, nullptr, h,
+                                         static_cast<hipStream_t>(stream), true));
+}
+
+moe_status moe_expert_gateup_packed_gathered(const moe_problem* p, const uint16_t* x,
+                                             const int32_t* row_token,
+                                             const int32_t* expert_offsets,
+                                             const uint16_t* w_gateup_packed, uint16_t* h,
+                                             void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !row_token || !expert_offsets || !w_gateup_packed || !h) return MOE_ERR_INVALID_ARG;
+  if (d.padded || (uint64_t)d.N * d.D * 2 >= (1ull << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_gateup_packed) || !aligned16(h)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  if (!gateup_gather_supported(d)) return MOE_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_gateup_gathered(d, x, row_token, expert_offsets,
+                                                  w_gateup_packed, nullptr, h,
+                                                  static_cast<hipStream_t>(stream), true));
+}
+
+moe_status moe_expert_down_packed(const moe_problem* p, const uint16_t* h,
+                                  const int32_t* expert_offsets, const uint16_t* w_down_packed,
+                                  uint16_t* out_perm, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!h || !expert_offsets || !w_down_packed || !out_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w_down_packed) || !aligned16(out_perm))
+    return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_down(d, h, expert_offsets, w_down_packed, out_perm,
+                                       static_cast<hipStream_t>(stream), true));
+}
+
+moe_status moe_forward_packed(const moe_problem* p, const uint16_t* x, const float* w_router,
+                              const float* expert_bias, const uint16_t* w_gateup_packed,
+                              const uint16_t* w_down_packed, uint16_t* y, float* logits,
+                              int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                              int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream) {
+  const bool present = w_router && w_gateup_packed && w_down_packed;
+  const bool aligned =
+      aligned16(w_router) && aligned16(w_gateup_packed) && aligned16(w_down_packed);
+  return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
+                      expert_offsets, ws, ws_bytes, stream, kGatherBf16,
+                      [&](const Dims& d, float* lg, int32_t* ids, float* w, char* base,
+                          const ForwardWs& L, hipStream_t s) {
+                        float* parts = router_ws_bytes(d) > 0
+                                           ? reinterpret_cast<float*>(base + L.rpart)
+                                           : nullptr;
+                        const hipError_t e = launch_router_gemm(d, x, w_router, lg, parts, s);
+                        return e != hipSuccess ? e
+                                               : launch_topk(d, lg, expert_bias, ids, w, parts, s);
+                      },
+                      [&](const Dims& d, const uint16_t* xp, const int32_t* rt,
+                          const int32_t* offs, uint16_t* op, void* fws, hipStream_t s) {
+                        if (!rt)
+                          return launch_grouped_ffn(d, xp, offs, w_gateup_packed, nullptr,
+                                                    w_down_packed, op, nullptr, fws, s, true);
+                        uint16_t* h = static_cast<uint16_t*>(fws);
+                        const hipError_t e = launch_expert_gateup_gathered(
+                            d, xp, rt, offs, w_gateup_packed, nullptr, h, s, true);
+                        return e != hipSuccess
+                                   ? e
+                                   : launch_expert_down(d, h, offs, w_down_packed, op, s, true);
+                      });
+}
+
 moe_status moe_route_mlp(const moe_problem* p, const uint16_t* x, const uint16_t* w_proj,
                          const float* b_proj, const float* w_out, const float* b_out,
                          uint16_t* features, float* logits, int32_t* topk_ids,

@@ -210,6 +210,54 @@ def test_fp8_argument_checks():
     assert fw(ctypes.byref(P(N=0)), *args[1:], None, 0, None) == OK
 
 
+def test_packed_weight_argument_checks():
+    L = moe.lib
+    n = ctypes.c_size_t()
+    # sizes: E * ceil(F / 128) * (D / 64) * 32 KB (gate/up), E * ceil(D / 256) * (F / 64) * 32 KB
+    for D, F in ((256, 512), (320, 192), (7168, 2048)):
+        bp = ctypes.byref(P(D=D, F=F))
+        assert L.moe_packed_weight_size(bp, 0, ctypes.byref(n)) == OK
+        assert n.value == 8 * math.ceil(F / 128) * (D // 64) * 32768
+        assert L.moe_packed_weight_size(bp, 1, ctypes.byref(n)) == OK
+        assert n.value == 8 * math.ceil(D / 256) * (F // 64) * 32768
+    bp = ctypes.byref(P())
+    assert L.moe_packed_weight_size(bp, 2, ctypes.byref(n)) == INVALID
+    assert L.moe_packed_weight_size(bp, 0, None) == INVALID
+    assert L.moe_packed_weight_size(ctypes.byref(P(D=100)), 0, ctypes.byref(n)) == UNSUPPORTED
+    pk = L.moe_pack_weights
+    assert pk(bp, 2, FAKE, FAKE, FAKE, None) == INVALID          # no such kind
+    assert pk(bp, 0, FAKE, None, FAKE, None) == INVALID          # gate/up needs both stacks
+    assert pk(bp, 1, None, None, FAKE, None) == INVALID
+    assert pk(bp, 1, FAKE, None, None, None) == INVALID
+    assert pk(bp, 0, FAKE, FAKE + 2, FAKE, None) == UNSUPPORTED
+    assert pk(bp, 1, FAKE, None, FAKE + 8, None) == UNSUPPORTED
+    g = L.moe_expert_gateup_packed
+    assert g(bp, FAKE, FAKE, None, FAKE, None) == INVALID
+    assert g(bp, FAKE, FAKE, FAKE + 4, FAKE, None) == UNSUPPORTED
+    assert g(ctypes.byref(P(N=0)), FAKE, FAKE, FAKE, FAKE, None) == OK
+    gg = L.moe_expert_gateup_packed_gathered
+    big = ctypes.byref(P(N=4096))
+    assert gg(big, FAKE, None, FAKE, FAKE, FAKE, None) == INVALID
+    assert gg(ctypes.byref(P(N=4096, cn=5, cd=4)), *([FAKE] * 5), None) == UNSUPPORTED
+    assert gg(bp, *([FAKE] * 5), None) == UNSUPPORTED             # register-staged tiles
+    assert gg(ctypes.byref(P(N=0)), *([FAKE] * 5), None) == OK
+    d = L.moe_expert_down_packed
+    assert d(bp, FAKE, None, FAKE, FAKE, None) == INVALID
+    assert d(bp, FAKE, FAKE, FAKE, FAKE + 2, None) == UNSUPPORTED
+    assert d(ctypes.byref(P(N=0)), FAKE, FAKE, FAKE, FAKE, None) == OK
+    fw = L.moe_forward_packed
+    need = moe.workspace_size(P())
+    args = [bp, FAKE, FAKE, None, FAKE, FAKE, FAKE] + [None] * 5
+    bad = list(args)
+    bad[5] = None                                                 # down stack missing
+    assert fw(*bad, FAKE, need, None) == INVALID
+    bad = list(args)
+    bad[4] = FAKE + 2                                             # gate/up stack misaligned
+    assert fw(*bad, FAKE, need, None) == UNSUPPORTED
+    assert fw(*args, FAKE, need - 1, None) == WORKSPACE
+    assert fw(ctypes.byref(P(N=0)), *args[1:], None, 0, None) == OK
+
+
 def test_gelu_layer_argument_checks():
     L = moe.lib
     p = P(D=256)

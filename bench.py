@@ -371,9 +371,11 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
     gu_mats = nmat - 1
     gu_flops = 2.0 * gu_mats * D * F * kept
     gu_bytes = gu_mats * touched * F * D * wb + kept * D * 2 + kept * F * 2
+    # profile tag: packed weights are the SwiGLU layers' default, the bf16
+    # stacks read in place are the "unpacked" variant
+    unpacked = o.weights == "bf16" and not (gelu or o.fused)
     suffix = ("_padded" if capv else "") + ("_fp8" if fp8 else "") + \
-        ("_packed" if packed else "") + \
-             ("_xperm" if o.xperm else "")
+        ("_unpacked" if unpacked else "") + ("_xperm" if o.xperm else "")
     if o.fused:
         # the one fused launch: gate/up, SwiGLU and down of every expert
         f_flops = 6.0 * D * F * kept

@@ -516,27 +516,53 @@ topk_kernel(int64_t N, int E, int K, int gating, float* __restrict__ logits,
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
   float* row = logits + n * E;
+  // Every load of the token goes out before the first use: the partials of
+  // all its experts (part index clamped to nparts - 1, so no load sits behind
+  // a branch), or its logits, and the bias.  The logit that a split router's
+  // partials sum to (in part order) is written out and used as it is.
+  // (without a bias the bias loads read the logits row instead, and are not used)
+  const float* bsrc = bias ? bias : row;
+  float lg[EPL], bv[EPL];
+  // (with more than 256 experts, a group of 64 experts at a time: all groups
+  // at once would not fit in registers)
+  constexpr int JB = EPL <= 4 ? EPL : 1;
+  if (partials) {
+#pragma unroll
+    for (int j0 = 0; j0 < EPL; j0 += JB) {
+      float pv[JB][kMaxParts];
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int q = 0; q < kMaxParts; ++q)
+          pv[j][q] = partials[(size_t)min(q, nparts - 1) * N * E + n * E +
+                              min(lane + 64 * (j0 + j), E - 1)];
+#pragma unroll
+      for (int j = 0; j < JB; ++j) bv[j0 + j] = bsrc[min(lane + 64 * (j0 + j), E - 1)];
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        float v = pv[j][0];
+#pragma unroll
+        for (int q = 1; q < kMaxParts; ++q)
+          if (q < nparts) v += pv[j][q];
+        lg[j0 + j] = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      lg[j] = row[min(lane + 64 * j, E - 1)];
+      bv[j] = bsrc[min(lane + 64 * j, E - 1)];
+    }
+  }
   uint64_t pk[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
     pk[j] = 0;
     if (e < E) {
-      if (partials) {
-        // all parts' loads go out before the first add (at most kMaxParts
-        // parts); the sum then runs in part order
-        float pv[kMaxParts];
-#pragma unroll
-        for (int q = 0; q < kMaxParts; ++q)
-          pv[q] = q < nparts ? partials[(size_t)q * N * E + n * E + e] : 0.f;
-        float lg = pv[0];
-#pragma unroll
-        for (int q = 1; q < kMaxParts; ++q)
-          if (q < nparts) lg += pv[q];
-        row[e] = lg;
-      }
-      float key = row[e];
-      if (bias) key = key + bias[e];
+      if (partials) row[e] = lg[j];
+      float key = lg[j];
+      if (bias) key = key + bv[j];
       if (key == 0.f) key = 0.f;                  // -0.0 -> +0.0
       if (key != key) key = -__builtin_inff();    // NaN ranks last
       pk[j] = ((uint64_t)orderable(key) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);

@@ -306,10 +306,12 @@ router_mfma_kernel(int64_t N, int D, int E, int vec4, const uint16_t* __restrict
 // tokens x 256 experts and one part of k, and stages both operands through LDS
 // (LDS-DMA, global_load_lds_dwordx4), so each x and weight byte leaves memory
 // once per workgroup instead of once per wave: per 64-deep stage 16 KB of x
-// (bf16) and 64 KB of weights (fp32) feed 128 x 256 x 64 x 3 MACs.  Wave
-// (th, eq) computes tokens [64 th, +64) x experts [64 eq, +64) with the same
-// exact three-way weight split and the same hi / mid+lo accumulators as the
-// kernel above.  Two LDS slots: stage kt+2 is fetched once every wave is done
+// (bf16) and 64 KB of weights (fp32) feed 128 x 256 x 64 x 3 MACs.  Wave w
+// computes all 128 tokens x experts [32 w, +32) with the same exact three-way
+// weight split and the same hi / mid+lo accumulators as the kernel above:
+// each weight value is split by one wave only (with 64 x 64 per wave, two
+// waves split every weight block, and the split, not the MFMAs, set the
+// kernel's pace).  Two LDS slots: stage kt+2 is fetched once every wave is done
 // with stage kt.  k is cut into `parts` contiguous parts; a part's partial
 // tile is hi + lo of its accumulators.  Split form (partials != NULL): one
 // workgroup per (tile, part), partial tiles to partials[part] and summed by
@@ -365,7 +367,6 @@ router_lds_kernel(int64_t N, int D, int E, int parts, int vec4, const uint16_t* 
   }
   const int64_t n0 = (v / ne) * kRT;
   const int e0 = (int)(v % ne) * kRE;
-  const int th = wave >> 2, eq = wave & 3;
   const int r = lane & 31, kh = lane >> 5;
   const int nkb = D / kRBK;
   const uint32_t ax = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&lx[0][0];
@@ -403,13 +404,11 @@ router_lds_kernel(int64_t N, int D, int E, int parts, int vec4, const uint16_t* 
   for (int part = part0; part < part1; ++part) {
     const int kb0 = (int)((int64_t)part * nkb / parts), kb1 = (int)((int64_t)(part + 1) * nkb / parts);
     const int nk = kb1 - kb0;
-    f32x16_t acc_hi[2][2], acc_lo[2][2];   // [expert block][token block]
+    f32x16_t acc_hi[4], acc_lo[4];   // [token block] of this wave's expert block
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc_hi[i][j][q] = acc_lo[i][j][q] = 0.f;
+      for (int q = 0; q < 16; ++q) acc_hi[j][q] = acc_lo[j][q] = 0.f;
     // every wave is past its LDS reads of the previous part
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     dma(0, kb0);
@@ -426,24 +425,23 @@ router_lds_kernel(int64_t N, int D, int E, int parts, int vec4, const uint16_t* 
 #pragma unroll
       for (int ks = 0; ks < kRBK / 16; ++ks) {
         const int c = 2 * ks + kh;               // this lane's 8 k: chunk c of x, 2c and 2c+1 of w
-        bf16x8_t xa[2];
+        bf16x8_t xa[4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int rr = th * 64 + j * 32 + r;
+        for (int j = 0; j < 4; ++j) {
+          const int rr = j * 32 + r;
           xa[j] = __builtin_bit_cast(bf16x8_t, sx[rr * 8 + (c ^ rswz_x(rr))]);
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int rr = eq * 64 + i * 32 + r;
+        {
+          const int rr = wave * 32 + r;
           const uint4 a = sw[rr * 16 + ((2 * c) ^ rswz_w(rr))];
           const uint4 b = sw[rr * 16 + ((2 * c + 1) ^ rswz_w(rr))];
           bf16x8_t hi, mid, lo;
           split3(__builtin_bit_cast(float4, a), __builtin_bit_cast(float4, b), hi, mid, lo);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, xa[j], acc_hi[i][j], 0, 0, 0);
-            acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, xa[j], acc_lo[i][j], 0, 0, 0);
-            acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, xa[j], acc_lo[i][j], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) {
+            acc_hi[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, xa[j], acc_hi[j], 0, 0, 0);
+            acc_lo[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, xa[j], acc_lo[j], 0, 0, 0);
+            acc_lo[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, xa[j], acc_lo[j], 0, 0, 0);
           }
         }
       }
@@ -454,35 +452,33 @@ router_lds_kernel(int64_t N, int D, int E, int parts, int vec4, const uint16_t* 
       asm volatile("s_barrier" ::: "memory");
       if (kt + 2 < nk) dma(kt & 1, kb0 + kt + 2);
     }
-    // Block (i, j): lane l, register q holds expert 8*(q/4) + 4*(l/32) + q%4
-    // of expert block i and token l%32 of token block j.
+    // Block j: lane l, register q holds expert 8*(q/4) + 4*(l/32) + q%4 of
+    // this wave's expert block and token l%32 of token block j.
     float* out = split ? partials + (size_t)part * N * E : logits;
     const bool add = !split && part > 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + j * 32 + r;
+      if (n >= N) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + th * 64 + j * 32 + r;
-        if (n >= N) continue;
+      for (int g = 0; g < 4; ++g) {
+        const int el = wave * 32 + 8 * g + 4 * kh;
+        float vv[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int el = eq * 64 + i * 32 + 8 * g + 4 * kh;
-          float vv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) vv[q] = acc_hi[i][j][4 * g + q] + acc_lo[i][j][4 * g + q];
-          float* dst = out + n * E + e0 + el;
-          if (vec4) {
-            float4 o = make_float4(vv[0], vv[1], vv[2], vv[3]);
-            if (add) {
-              const float4 pv = *reinterpret_cast<const float4*>(dst);
-              o = make_float4(pv.x + o.x, pv.y + o.y, pv.z + o.z, pv.w + o.w);
-            }
-            *reinterpret_cast<float4*>(dst) = o;
-          } else {
-            for (int q = 0; q < 4; ++q) dst[q] = add ? dst[q] + vv[q] : vv[q];
+        for (int q = 0; q < 4; ++q) vv[q] = acc_hi[j][4 * g + q] + acc_lo[j][4 * g + q];
+        float* dst = out + n * E + e0 + el;
+        if (vec4) {
+          float4 o = make_float4(vv[0], vv[1], vv[2], vv[3]);
+          if (add) {
+            const float4 pv = *reinterpret_cast<const float4*>(dst);
+            o = make_float4(pv.x + o.x, pv.y + o.y, pv.z + o.z, pv.w + o.w);
           }
+          *reinterpret_cast<float4*>(dst) = o;
+        } else {
+          for (int q = 0; q < 4; ++q) dst[q] = add ? dst[q] + vv[q] : vv[q];
         }
       }
+    }
   }
 }
 

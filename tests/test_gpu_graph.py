@@ -92,10 +92,17 @@ def _quantize(w):
     return codes, scales
 
 
-@pytest.mark.parametrize("kind", ["fp8", "fused", "gelu"])
+def _pack(p, kind, w0, w1=None):
+    buf = torch.empty(moe.packed_weight_size(p, kind) // 2, dtype=torch.bfloat16, device=DEV)
+    moe.pack_weights(p, kind, w0, w1, buf)
+    return buf
+
+
+@pytest.mark.parametrize("kind", ["fp8", "fused", "gelu", "packed", "packed_decode"])
 def test_forward_variants_graph_replays_match_eager(kind):
-    """moe_forward_fp8 (split-ring-sized rows), moe_forward_fused and
-    moe_forward_gelu captured once and replayed with eager calls between."""
+    """moe_forward_fp8 (split-ring-sized rows), moe_forward_fused,
+    moe_forward_gelu and moe_forward_packed (split-ring and decode-sized rows)
+    captured once and replayed with eager calls between."""
     if kind == "gelu":
         from gpu_layer import GeluLayer
         L = GeluLayer(ms.CONFIGS["gelu_tiny"])
@@ -104,6 +111,14 @@ def test_forward_variants_graph_replays_match_eager(kind):
         def call(out):
             moe.forward_gelu(L.p, i["x"], i["w_proj"], i["b_proj"], i["w_out"], i["b_out"],
                              i["w1"], i["b1"], i["w2"], i["b2"], out, L.ws)
+        N, D = L.cfg.N, L.cfg.D
+    elif kind.startswith("packed"):
+        L = Layer(ms.CONFIGS["qwen3_decode"] if kind == "packed_decode" else SMALL["large_tiles"])
+        gu = _pack(L.p, moe.PACK_GATEUP, L.w_gate, L.w_up)
+        dn = _pack(L.p, moe.PACK_DOWN, L.w_down)
+
+        def call(out):
+            moe.forward_packed(L.p, L.x, L.w_router, L.bias, gu, dn, out, L.ws)
         N, D = L.cfg.N, L.cfg.D
     else:
         L = Layer(SMALL["mid_tiles" if kind == "fused" else "large_tiles"])
@@ -138,3 +153,7 @@ def test_forward_variants_graph_replays_match_eager(kind):
     if kind == "fused":
         off = moe.fused_error_offset(L.p, whole_layer=True)
         assert int(L.ws[off:off + 4].view(torch.int32).item()) == 0
+    if kind.startswith("packed"):
+        y_unpacked = torch.empty_like(y)
+        L.forward(y_unpacked)
+        assert np.array_equal(bits(y_unpacked), ref), "packed and unpacked layers differ"

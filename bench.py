@@ -432,11 +432,12 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                    "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
                               else "SwiGLU"),
                    "launch": (("the five staged library calls" if o.xperm else
-                               "moe_forward_fused" if o.fused else
-                               "moe_forward_gelu" if gelu else
-                               "moe_forward_fp8" if fp8 else
-                               "moe_forward_packed" if packed else "moe_forward") +
-                              " (one call) captured once as a HIP graph and replayed"
+                               ("moe_forward_fused" if o.fused else
+                                "moe_forward_gelu" if gelu else
+                                "moe_forward_fp8" if fp8 else
+                                "moe_forward_packed" if packed else "moe_forward") +
+                               " (one call)") +
+                              " captured once as a HIP graph and replayed"
                               if o.graph else "the five staged library calls, eager"),
                    "ffn_launch": ("fused (one persistent launch)" if o.fused else
                                   "two grouped GEMMs, rows of the first gathered from x"

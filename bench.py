@@ -28,13 +28,12 @@ shape -- run after it in the same process and are reported under
 ``cpu_baseline`` is the C++ oracle on a bounded sample of the headline
 workload's tokens, on the host's cores.
 
-The SwiGLU layers read their expert weights packed by moe_pack_weights (the
-same bf16 values in the order the GEMMs stream them, written once when the
-weights are loaded; the outputs are bit for bit those of the unpacked calls);
-``--weights bf16`` reads the nn.Linear stacks in place and ``--weights fp8``
-block-scaled FP8 copies.  ``--config gelu_mlp`` runs the pages' other layer
-(MLP router, GELU experts, bf16 weights in place); ``--fused`` runs the
-expert FFN as one persistent launch (bf16 weights in place).
+The expert weights are the nn.Linear bf16 stacks, read in place.
+``--weights packed`` times the same values packed once by moe_pack_weights
+(the order the GEMMs stream them; outputs bit for bit those of the unpacked
+calls), ``--weights fp8`` block-scaled FP8 copies.  ``--config gelu_mlp``
+runs the pages' other layer (MLP router, GELU experts); ``--fused`` runs the
+expert FFN as one persistent launch.
 
 Also: ``--trace-summary DIR`` and ``--pmc-summary ...`` turn rocprofv3 output
 of a profiled run of this script into the tables kept under profiles/.
@@ -57,7 +56,7 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_level_amd", "csrc", "grouped_gemm.hip")
 FLUSH_BYTES = 512 << 20
-DEFAULT_EXTRA = "qwen3_decode,hot_skew,hot_skew:padded,mixtral"
+DEFAULT_EXTRA = "qwen3_decode,qwen3_decode:packed,hot_skew,hot_skew:padded,mixtral"
 # tokens of the CPU-oracle sample per workload (about 10-30 s of CPU work on
 # 16 host cores for the C++ oracle)
 CPU_TOKENS = {"deepseek_v3": 2048, "mixtral": 512, "hot_skew": 1024, "qwen3_decode": 64,
@@ -371,11 +370,8 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
     gu_mats = nmat - 1
     gu_flops = 2.0 * gu_mats * D * F * kept
     gu_bytes = gu_mats * touched * F * D * wb + kept * D * 2 + kept * F * 2
-    # profile tag: packed weights are the SwiGLU layers' default, the bf16
-    # stacks read in place are the "unpacked" variant
-    unpacked = o.weights == "bf16" and not (gelu or o.fused)
     suffix = ("_padded" if capv else "") + ("_fp8" if fp8 else "") + \
-        ("_unpacked" if unpacked else "") + ("_xperm" if o.xperm else "")
+        ("_packed" if packed else "") + ("_xperm" if o.xperm else "")
     if o.fused:
         # the one fused launch: gate/up, SwiGLU and down of every expert
         f_flops = 6.0 * D * F * kept
@@ -422,7 +418,8 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         stages["utilisation"] = kept / (E * capv)
         stages["executed_tflops"] = exec_flops / (ms_step * 1e-3) / 1e12
     res = {
-        "workload": cfg.note + (" [capacity-padded]" if capv else ""),
+        "workload": cfg.note + (" [capacity-padded]" if capv else "") +
+                    (" [packed weights]" if packed else ""),
         "config": {"workload": cfg.note + (" [capacity-padded]" if capv else ""),
                    "tokens": N, "hidden": D, "experts": E, "top_k": K, "ffn": F,
                    "gating": cfg.gating, "capacity": capv or None,
@@ -494,10 +491,10 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="time the eager steps only (by default the step is also captured as "
                          "a HIP graph and ms_per_step is the graph's cold replay)")
-    ap.add_argument("--weights", choices=("bf16", "fp8", "packed"), default=None,
-                    help="expert weight storage: bf16 stacks read in place, block-scaled FP8 "
-                         "(E4M3 + E8M0), or the same bf16 values packed as the GEMMs' stage "
-                         "images (default; bf16 for the GELU layer and --fused)")
+    ap.add_argument("--weights", choices=("bf16", "fp8", "packed"), default="bf16",
+                    help="expert weight storage: bf16 stacks read in place (default), "
+                         "block-scaled FP8 (E4M3 + E8M0), or the same bf16 values packed as "
+                         "the GEMMs' stage images (SwiGLU layers, not with --fused)")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the CPU-oracle sample (-1: a per-workload default of about "
                          "10-30 s of CPU work; 0: skip the CPU baseline)")
@@ -557,8 +554,6 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     cfg = ms.CONFIGS[args.config]
-    if args.weights is None:
-        args.weights = "bf16" if (cfg.expert == "gelu" or args.fused) else "packed"
     head, inp = run_layer(cfg, Opts(args.padded, args.fused, args.xperm, args.weights,
                                     not args.eager),
                           args.steps, args.warmup, warm_steps, log)
@@ -600,11 +595,14 @@ def main():
     extras = {}
     if args.extra and args.extra != "none" and not (args.fused or args.weights == "fp8"):
         for item in args.extra.split(","):
+            # name:padded (capacity-padded layout), name:packed (packed weights)
             name, _, mode = item.partition(":")
-            if name == cfg.name and (mode == "padded") == args.padded:
+            weights = "packed" if mode == "packed" else args.weights
+            if name == cfg.name and (mode == "padded") == args.padded and \
+                    weights == args.weights:
                 continue
             res, inp = run_layer(ms.CONFIGS[name],
-                                 Opts(padded=mode == "padded", weights=args.weights,
+                                 Opts(padded=mode == "padded", weights=weights,
                                       graph=not args.eager), args.steps,
                                  args.warmup, warm_steps, log)
             del inp
@@ -613,7 +611,7 @@ def main():
                     "eager_ms_per_step", "graph_ms_per_step", "tflops",
                     "pct_bf16_mfma_peak", "weight_stream_gbps", "pct_hbm_peak_weights",
                     "max_expert_rows", "dropped_slots", "stages", "roofline")
-            extras[name + ("_padded" if mode == "padded" else "")] = {k: res[k] for k in keep}
+            extras[name + ("_" + mode if mode else "")] = {k: res[k] for k in keep}
     line["workloads"] = extras
     print(json.dumps(line), flush=True)
 

@@ -157,6 +157,34 @@ perm_copy_kernel(int64_t N, int D, int K, const uint16_t* __restrict__ x,
   }
 }
 
+// Many tokens with wide rows: one workgroup per token (grid-stride over
+// tokens), as many threads as the row has chunks rounded up to a wave (at
+// most 1024).  The token's K slot rows are wave-uniform and come through
+// scalar loads, so the vector-memory path carries only the row itself, and a
+// token whose slots were all dropped (capacity) reads nothing.  Same bytes
+// written as perm_copy_kernel.
+__global__ void __launch_bounds__(1024)
+perm_copy_token_kernel(int64_t N, int D, int K, const uint16_t* __restrict__ x,
+                       const int32_t* __restrict__ slot_row, uint16_t* __restrict__ x_perm) {
+  const int cpr = D / 8;
+  for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+    int kept = 0;
+    for (int k = 0; k < K; ++k) kept |= slot_row[n * K + k] >= 0;
+    if (!kept) continue;   // the same for every thread of the workgroup
+    for (int c = threadIdx.x; c < cpr; c += blockDim.x) {
+      const uint4 v = reinterpret_cast<const uint4*>(x + n * D)[c];
+      for (int k0 = 0; k0 < K; k0 += 8) {
+        int32_t r[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = k0 + j < K ? slot_row[n * K + k0 + j] : -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (r[j] >= 0) reinterpret_cast<uint4*>(x_perm + (int64_t)r[j] * D)[c] = v;
+      }
+    }
+  }
+}
+
 // Small problems (N*K <= 1024 slots): histogram, scan and stable rank in one
 // workgroup of 16 waves; wave w ranks slots [64w, 64w + 64).  Same results as
 // count + scan + rank.
@@ -272,6 +300,14 @@ hipError_t launch_permute(const Dims& d, const uint16_t* x, const int32_t* ids, 
                        counts, row_token, x_perm);
   }
   if (!x_perm) return hipGetLastError();      // routing tables only
+  if (d.N >= 1024 && d.D >= 1024) {
+    const int cpr = d.D / 8;
+    const int threads = std::min(1024, (cpr + 63) / 64 * 64);
+    const int64_t blocks = std::min<int64_t>(d.N, 1 << 20);
+    hipLaunchKernelGGL(perm_copy_token_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, d.N,
+                       d.D, d.K, x, slot_row, x_perm);
+    return hipGetLastError();
+  }
   const int64_t items = d.N * (d.D / 8);
   const int64_t blocks = std::min<int64_t>((items + 255) / 256, 1 << 20);
   hipLaunchKernelGGL(perm_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, d.N, d.D, d.K, x,

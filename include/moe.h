@@ -221,7 +221,7 @@ moe_status moe_forward(const moe_problem* p, const uint16_t* x, const float* w_r
  *   Arguments, outputs and results as moe_forward (bit for bit the same).
  *   MOE_ERR_WORKSPACE, before any HIP call, when moe_workspace_size(p)
  *   exceeds MOE_STATIC_SCRATCH_BYTES (e.g. a decode step of the Qwen3-30B-A3B
- *   layer shape needs about 6 MB; prefill batches do not fit).
+ *   layer shape needs about 2.8 MB; prefill batches do not fit).
  *   The scratch is shared by every call on one GPU and keeps the last call's
  *   contents; nothing in it needs to start at zero.  Calls that overlap on
  *   one GPU (other streams, other threads) race on it and give undefined

@@ -1,5 +1,6 @@
 // C ABI of libmoe: argument checks, workspace layout and launch sequencing.
 // Every check runs on the host before the first HIP call of an entry point.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <mutex>
@@ -66,6 +67,17 @@ struct ForwardWs {
       ffn, feats, roff, fused, rpart, total;
 };
 
+// One layout serves every forward entry point.  Regions whose uses never
+// overlap in time share memory:
+//   - the routing scratch (the split router's partial logits, the MLP
+//     router's features and its GEMM's offsets) is dead once top-K has run,
+//     before the permutation writes x_perm;
+//   - x_perm is read only by the gate/up GEMM, which has finished before the
+//     down GEMM writes out_perm over it (the fused launch, which writes
+//     out_perm while it reads its rows, takes them from x, not x_perm);
+//   - the permutation's scratch, the FFN's h and the fused launch's h and
+//     counters belong to successive launches (the fused launch clears its
+//     counters itself).
 ForwardWs forward_layout(const Dims& d) {
   ForwardWs w;
   size_t o = 0;
@@ -81,14 +93,12 @@ ForwardWs forward_layout(const Dims& d) {
   w.offsets = take((size_t)(d.E + 1) * 4);
   w.row_token = take((size_t)d.R * 4);
   w.slot_row = take((size_t)d.S * 4);
-  w.x_perm = take((size_t)d.R * d.D * 2);
-  w.out_perm = take((size_t)d.R * d.D * 2);
-  w.perm = take(permute_ws_bytes(d));
-  w.ffn = take(ffn_ws_bytes(d));
-  w.feats = take((size_t)d.N * (d.D / 4) * 2);   // MLP router: compressed features
-  w.roff = take(2 * 4);                          // MLP router: offsets {0, N} of its GEMM
-  w.fused = take(fused_ws_bytes(d));             // fused FFN: h and its counters
-  w.rpart = take(router_ws_bytes(d));            // split router: partial logits
+  const size_t feats = align_up((size_t)d.N * (d.D / 4) * 2);   // MLP router features
+  const size_t rows = std::max({(size_t)d.R * d.D * 2, router_ws_bytes(d), feats + align_up(2 * 4)});
+  w.x_perm = w.out_perm = w.rpart = w.feats = take(rows);
+  w.roff = w.feats + feats;
+  w.perm = w.ffn = w.fused = take(std::max({permute_ws_bytes(d), ffn_ws_bytes(d),
+                                            fused_ws_bytes(d)}));
   w.total = o;
   return w;
 }

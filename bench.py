@@ -31,7 +31,8 @@ workload's tokens, on the host's cores.
 The expert weights are the nn.Linear bf16 stacks, read in place.
 ``--weights packed`` times the same values packed once by moe_pack_weights
 (the order the GEMMs stream them; outputs bit for bit those of the unpacked
-calls), ``--weights fp8`` block-scaled FP8 copies.  ``--config gelu_mlp``
+calls), ``--weights fp8`` block-scaled FP8 copies, ``--weights fp8packed``
+those with their codes packed by moe_pack_weights_fp8.  ``--config gelu_mlp``
 runs the pages' other layer (MLP router, GELU experts); ``--fused`` runs the
 expert FFN as one persistent launch.
 
@@ -143,7 +144,8 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         wr, bias = inp["w_router"], inp["bias"]
         wg, wu, wd = inp["w_gate"], inp["w_up"], inp["w_down"]
     stream = torch.cuda.current_stream()
-    fp8 = o.weights == "fp8"
+    fp8 = o.weights in ("fp8", "fp8packed")
+    fp8p = o.weights == "fp8packed"
     if fp8:
         def quant(wt):
             rows, cols = wt.shape[-2], wt.shape[-1]
@@ -153,6 +155,14 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
             moe.quantize_fp8(wt.numel() // cols, cols, wt, c, sc, stream=stream)
             return c, sc
         qg, qu, qd = quant(wg), quant(wu), quant(wd)
+        if fp8p:
+            # the codes in the library's packed stage-image order (scales as they are)
+            def pack8(kind, c0, c1=None):
+                buf = torch.empty(moe.packed_weight_size(p, kind), dtype=torch.uint8, device=dev)
+                moe.pack_weights_fp8(p, kind, c0, c1, buf, stream=stream)
+                return buf
+            pgu8 = pack8(moe.PACK_GATEUP_FP8, qg[0], qu[0])
+            pdn8 = pack8(moe.PACK_DOWN_FP8, qd[0])
         torch.cuda.synchronize()
     packed = o.weights == "packed"
     if packed:
@@ -182,6 +192,12 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                                             stream=torch.cuda.current_stream())
             else:
                 moe.expert_up_gelu(p, x_perm, offsets, inp["w1"], inp["b1"], h, stream=torch.cuda.current_stream())
+        elif gather and fp8p:
+            moe.expert_gateup_fp8_packed_gathered(p, x, row_token, offsets, pgu8, qg[1], qu[1], h,
+                                                  stream=torch.cuda.current_stream())
+        elif fp8p:
+            moe.expert_gateup_fp8_packed(p, x_perm, offsets, pgu8, qg[1], qu[1], h,
+                                         stream=torch.cuda.current_stream())
         elif gather and fp8:
             moe.expert_gateup_fp8_gathered(p, x, row_token, offsets, qg, qu, h, stream=torch.cuda.current_stream())
         elif gather and packed:
@@ -218,6 +234,9 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
             if gelu:
                 moe.expert_down_bias(p, h, offsets, inp["w2"], inp["b2"], out_perm,
                                      stream=torch.cuda.current_stream())
+            elif fp8p:
+                moe.expert_down_fp8_packed(p, h, offsets, pdn8, qd[1], out_perm,
+                                           stream=torch.cuda.current_stream())
             elif fp8:
                 moe.expert_down_fp8(p, h, offsets, qd, out_perm, stream=torch.cuda.current_stream())
             elif packed:
@@ -292,6 +311,9 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         elif gelu:
             moe.forward_gelu(p, x, inp["w_proj"], inp["b_proj"], inp["w_out"], inp["b_out"],
                              inp["w1"], inp["b1"], inp["w2"], inp["b2"], y, ws, stream=s_)
+        elif fp8p:
+            moe.forward_fp8_packed(p, x, wr, bias, pgu8, qg[1], qu[1], pdn8, qd[1], y, ws,
+                                   stream=s_)
         elif fp8:
             moe.forward_fp8(p, x, wr, bias, qg, qu, qd, y, ws, stream=s_)
         elif packed:
@@ -371,7 +393,7 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
     gu_flops = 2.0 * gu_mats * D * F * kept
     gu_bytes = gu_mats * touched * F * D * wb + kept * D * 2 + kept * F * 2
     suffix = ("_padded" if capv else "") + ("_fp8" if fp8 else "") + \
-        ("_packed" if packed else "") + ("_xperm" if o.xperm else "")
+        ("_packed" if packed or fp8p else "") + ("_xperm" if o.xperm else "")
     if o.fused:
         # the one fused launch: gate/up, SwiGLU and down of every expert
         f_flops = 6.0 * D * F * kept
@@ -419,11 +441,12 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
         stages["executed_tflops"] = exec_flops / (ms_step * 1e-3) / 1e12
     res = {
         "workload": cfg.note + (" [capacity-padded]" if capv else "") +
-                    (" [packed weights]" if packed else ""),
+                    (" [packed weights]" if packed or fp8p else ""),
         "config": {"workload": cfg.note + (" [capacity-padded]" if capv else ""),
                    "tokens": N, "hidden": D, "experts": E, "top_k": K, "ffn": F,
                    "gating": cfg.gating, "capacity": capv or None,
-                   "expert_weights": ("fp8 e4m3, power-of-two scale per 32 values"
+                   "expert_weights": ("fp8 e4m3, power-of-two scale per 32 values" +
+                                      (", codes packed as stage images" if fp8p else "")
                                       if fp8 else "bf16, packed stage images" if packed
                                       else "bf16"),
                    "expert": ("Linear-GELU-Linear with biases, MLP router" if gelu
@@ -431,6 +454,7 @@ def run_layer(cfg, o: Opts, steps: int, warmup: int, warm_steps: int, log):
                    "launch": (("the five staged library calls" if o.xperm else
                                ("moe_forward_fused" if o.fused else
                                 "moe_forward_gelu" if gelu else
+                                "moe_forward_fp8_packed" if fp8p else
                                 "moe_forward_fp8" if fp8 else
                                 "moe_forward_packed" if packed else "moe_forward") +
                                " (one call)") +
@@ -491,10 +515,12 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="time the eager steps only (by default the step is also captured as "
                          "a HIP graph and ms_per_step is the graph's cold replay)")
-    ap.add_argument("--weights", choices=("bf16", "fp8", "packed"), default="bf16",
+    ap.add_argument("--weights", choices=("bf16", "fp8", "packed", "fp8packed"),
+                    default="bf16",
                     help="expert weight storage: bf16 stacks read in place (default), "
-                         "block-scaled FP8 (E4M3 + E8M0), or the same bf16 values packed as "
-                         "the GEMMs' stage images (SwiGLU layers, not with --fused)")
+                         "block-scaled FP8 (E4M3 + E8M0), the same bf16 values packed as "
+                         "the GEMMs' stage images, or the FP8 codes so packed (SwiGLU layers, "
+                         "not with --fused)")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the CPU-oracle sample (-1: a per-workload default of about "
                          "10-30 s of CPU work; 0: skip the CPU baseline)")
@@ -588,16 +614,19 @@ def main():
         line["cpu_baseline"] = (cpu_baseline_gelu(cfg, inp, min(ntok, cfg.N))
                                 if cfg.expert == "gelu" else
                                 cpu_baseline(cfg, inp, min(ntok, cfg.N),
-                                             head["config"]["capacity"], args.weights == "fp8"))
+                                             head["config"]["capacity"],
+                                             args.weights in ("fp8", "fp8packed")))
     del inp
     torch.cuda.empty_cache()
 
     extras = {}
-    if args.extra and args.extra != "none" and not (args.fused or args.weights == "fp8"):
+    if args.extra and args.extra != "none" and not (args.fused or
+                                                    args.weights in ("fp8", "fp8packed")):
         for item in args.extra.split(","):
-            # name:padded (capacity-padded layout), name:packed (packed weights)
+            # name:padded (capacity-padded layout), name:packed (packed weights),
+            # name:fp8packed (FP8 weights, codes packed)
             name, _, mode = item.partition(":")
-            weights = "packed" if mode == "packed" else args.weights
+            weights = mode if mode in ("packed", "fp8packed") else args.weights
             if name == cfg.name and (mode == "padded") == args.padded and \
                     weights == args.weights:
                 continue

@@ -425,11 +425,20 @@ moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float*
  * The layout is an internal format: write it with moe_pack_weights only.  The
  * packed entry points give bit-identical results to the bf16 ones on the
  * weights that were packed. */
-typedef enum { MOE_PACK_GATEUP = 0, MOE_PACK_DOWN = 1 } moe_pack_kind;
+typedef enum {
+  MOE_PACK_GATEUP = 0,
+  MOE_PACK_DOWN = 1,
+  MOE_PACK_GATEUP_FP8 = 2,  /* FP8 codes: see moe_pack_weights_fp8 */
+  MOE_PACK_DOWN_FP8 = 3
+} moe_pack_kind;
 
 /* Bytes of a packed stack of `kind` for problem p (host; N is ignored):
  * E * ceil(F / 128) * (D / 64) * 32768 for MOE_PACK_GATEUP,
- * E * ceil(D / 256) * (F / 64) * 32768 for MOE_PACK_DOWN. */
+ * E * ceil(D / 256) * (F / 64) * 32768 for MOE_PACK_DOWN,
+ * E * ceil(F / 128) * (D / 128) * 32768 for MOE_PACK_GATEUP_FP8 (D a
+ * multiple of 128, MOE_ERR_UNSUPPORTED else),
+ * E * ceil(D / 256) * (F / 128) * 32768 for MOE_PACK_DOWN_FP8 (F a multiple
+ * of 128). */
 moe_status moe_packed_weight_size(const moe_problem* p, int32_t kind, size_t* bytes);
 
 /* Pack a stack: MOE_PACK_GATEUP reads w0 = W_gate and w1 = W_up [E, F, D]
@@ -461,6 +470,53 @@ moe_status moe_forward_packed(const moe_problem* p, const uint16_t* x, const flo
                               const uint16_t* w_down_packed, uint16_t* y, float* logits,
                               int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
                               int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream);
+
+/* Packed FP8 codes.  The codes of a block-scaled FP8 stack (the format of
+ * moe_quantize_fp8) in the same layout with stages 128 codes deep: a stage
+ * is row r of the panel at bytes [128 r, 128 r + 128), its 16-byte chunk c
+ * (codes 16c .. 16c + 15 of the stage) at position c ^ ((r / 2) % 8).  The
+ * scales are not packed: the calls below take them in their own layout.
+ * moe_pack_weights_fp8: MOE_PACK_GATEUP_FP8 reads c0 = the W_gate codes and
+ * c1 = the W_up codes [E, F, D], MOE_PACK_DOWN_FP8 reads c0 = the W_down
+ * codes [E, D, F] (c1 unused, may be NULL); packed: moe_packed_weight_size
+ * bytes, written whole.  The contraction length (D, resp. F) must be a
+ * multiple of 128, all pointers 16-byte aligned (MOE_ERR_UNSUPPORTED else).
+ * A copy; needs no workspace; runs whatever num_tokens is. */
+moe_status moe_pack_weights_fp8(const moe_problem* p, int32_t kind, const uint8_t* c0,
+                                const uint8_t* c1, uint8_t* packed, void* stream);
+
+/* moe_expert_gateup_fp8 / moe_expert_gateup_fp8_gathered / moe_expert_down_fp8
+ * / moe_forward_fp8 with packed codes: w_gateup_packed from
+ * MOE_PACK_GATEUP_FP8 with the gate and up scales of the stacks it was packed
+ * from, w_down_packed from MOE_PACK_DOWN_FP8 with the down scales.  D (gate/up)
+ * and F (down) multiples of 128 (MOE_ERR_UNSUPPORTED else); the gathered
+ * gate/up then takes every D.  Everything else as in the FP8 calls, and the
+ * outputs are bit for bit theirs. */
+moe_status moe_expert_gateup_fp8_packed(const moe_problem* p, const uint16_t* x_perm,
+                                        const int32_t* expert_offsets,
+                                        const uint8_t* w_gateup_packed,
+                                        const uint8_t* w_gate_scales, const uint8_t* w_up_scales,
+                                        uint16_t* h, void* stream);
+moe_status moe_expert_gateup_fp8_packed_gathered(const moe_problem* p, const uint16_t* x,
+                                                 const int32_t* row_token,
+                                                 const int32_t* expert_offsets,
+                                                 const uint8_t* w_gateup_packed,
+                                                 const uint8_t* w_gate_scales,
+                                                 const uint8_t* w_up_scales, uint16_t* h,
+                                                 void* stream);
+moe_status moe_expert_down_fp8_packed(const moe_problem* p, const uint16_t* h,
+                                      const int32_t* expert_offsets,
+                                      const uint8_t* w_down_packed,
+                                      const uint8_t* w_down_scales, uint16_t* out_perm,
+                                      void* stream);
+moe_status moe_forward_fp8_packed(const moe_problem* p, const uint16_t* x, const float* w_router,
+                                  const float* expert_bias, const uint8_t* w_gateup_packed,
+                                  const uint8_t* w_gate_scales, const uint8_t* w_up_scales,
+                                  const uint8_t* w_down_packed, const uint8_t* w_down_scales,
+                                  uint16_t* y, float* logits, int32_t* topk_ids,
+                                  float* topk_weights, int32_t* expert_counts,
+                                  int32_t* expert_offsets, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* ------------------------------------------------------ routing statistics */
 

@@ -116,6 +116,17 @@ def _load():
     L.moe_expert_down_packed.argtypes = [P, vp, vp, vp, vp, vp]
     L.moe_forward_packed.restype = ctypes.c_int
     L.moe_forward_packed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_pack_weights_fp8.restype = ctypes.c_int
+    L.moe_pack_weights_fp8.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp]
+    L.moe_expert_gateup_fp8_packed.restype = ctypes.c_int
+    L.moe_expert_gateup_fp8_packed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_gateup_fp8_packed_gathered.restype = ctypes.c_int
+    L.moe_expert_gateup_fp8_packed_gathered.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_down_fp8_packed.restype = ctypes.c_int
+    L.moe_expert_down_fp8_packed.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.moe_forward_fp8_packed.restype = ctypes.c_int
+    L.moe_forward_fp8_packed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, sz, vp]
     return L
 
 
@@ -301,7 +312,7 @@ def forward_fp8(p, x, w_router, bias, w_gate, w_up, w_down, y, ws, logits=None, 
 # Packed bf16 weights (moe_pack_weights): the same values in the kernels'
 # stage-image order; kind PACK_GATEUP (gate and up) or PACK_DOWN.
 
-PACK_GATEUP, PACK_DOWN = 0, 1       # moe_pack_kind
+PACK_GATEUP, PACK_DOWN, PACK_GATEUP_FP8, PACK_DOWN_FP8 = 0, 1, 2, 3   # moe_pack_kind
 
 
 def packed_weight_size(p, kind) -> int:
@@ -342,6 +353,50 @@ def forward_packed(p, x, w_router, bias, w_gateup, w_down, y, ws, logits=None, t
                                   _ptr(w_gateup), _ptr(w_down), _ptr(y), _ptr(logits),
                                   _ptr(topk_ids), _ptr(topk_weights), _ptr(counts),
                                   _ptr(offsets), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+# Packed FP8 codes (moe_pack_weights_fp8): the codes of an FP8 stack in the
+# same stage-image order, 128 codes deep; the scales stay as quantize_fp8
+# wrote them and are passed beside the packed codes.
+
+def pack_weights_fp8(p, kind, c0, c1, packed, stream=None):
+    _check("moe_pack_weights_fp8",
+           lib.moe_pack_weights_fp8(ctypes.byref(p), int(kind), _ptr(c0), _ptr(c1), _ptr(packed),
+                                    _stream(stream)))
+
+
+def expert_gateup_fp8_packed(p, x_perm, offsets, w_gateup, gate_scales, up_scales, h,
+                             stream=None):
+    _check("moe_expert_gateup_fp8_packed",
+           lib.moe_expert_gateup_fp8_packed(ctypes.byref(p), _ptr(x_perm), _ptr(offsets),
+                                            _ptr(w_gateup), _ptr(gate_scales), _ptr(up_scales),
+                                            _ptr(h), _stream(stream)))
+
+
+def expert_gateup_fp8_packed_gathered(p, x, row_token, offsets, w_gateup, gate_scales,
+                                      up_scales, h, stream=None):
+    _check("moe_expert_gateup_fp8_packed_gathered",
+           lib.moe_expert_gateup_fp8_packed_gathered(ctypes.byref(p), _ptr(x), _ptr(row_token),
+                                                     _ptr(offsets), _ptr(w_gateup),
+                                                     _ptr(gate_scales), _ptr(up_scales), _ptr(h),
+                                                     _stream(stream)))
+
+
+def expert_down_fp8_packed(p, h, offsets, w_down, down_scales, out_perm, stream=None):
+    _check("moe_expert_down_fp8_packed",
+           lib.moe_expert_down_fp8_packed(ctypes.byref(p), _ptr(h), _ptr(offsets), _ptr(w_down),
+                                          _ptr(down_scales), _ptr(out_perm), _stream(stream)))
+
+
+def forward_fp8_packed(p, x, w_router, bias, w_gateup, gate_scales, up_scales, w_down,
+                       down_scales, y, ws, logits=None, topk_ids=None, topk_weights=None,
+                       counts=None, offsets=None, stream=None):
+    _check("moe_forward_fp8_packed",
+           lib.moe_forward_fp8_packed(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
+                                      _ptr(w_gateup), _ptr(gate_scales), _ptr(up_scales),
+                                      _ptr(w_down), _ptr(down_scales), _ptr(y), _ptr(logits),
+                                      _ptr(topk_ids), _ptr(topk_weights), _ptr(counts),
+                                      _ptr(offsets), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 # GELU experts and the MLP router.

@@ -75,7 +75,9 @@ hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int
 hipError_t launch_expert_down(const Dims& d, const uint16_t* h, const int32_t* offsets,
                               const uint16_t* wd, uint16_t* out_perm, hipStream_t s,
                               bool packed = false);
-bool gateup_gather_supported(const Dims& d, bool fp8 = false);
+// fp8 / packed: FP8 weight stacks, packed ones (which the 128- and 64-deep
+// rings read at any D that is a multiple of 128)
+bool gateup_gather_supported(const Dims& d, bool fp8 = false, bool packed = false);
 hipError_t launch_expert_gateup_gathered(const Dims& d, const uint16_t* x,
                                          const int32_t* row_token, const int32_t* offsets,
                                          const uint16_t* wg, const uint16_t* wu, uint16_t* h,
@@ -84,12 +86,13 @@ hipError_t launch_grouped_ffn(const Dims& d, const uint16_t* x_perm, const int32
                               const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                               uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s,
                               bool packed = false);
-// Packed bf16 weight stacks: gate/up (w0 = W_gate, w1 = W_up, [E, F, D]) or
-// down (w0 = W_down [E, D, F]) as the 32 KB LDS images of their 256-row,
-// 64-deep weight stages, in (expert, column tile, stage) order.
-size_t packed_weight_bytes(const Dims& d, bool gateup);
+// Packed weight stacks: gate/up (w0 = W_gate, w1 = W_up, [E, F, D]) or
+// down (w0 = W_down [E, D, F]) as the 32 KB LDS images of their 256-row
+// weight stages, in (expert, column tile, stage) order: stages of 64 bf16
+// values, or (fp8) of 128 FP8 codes, passed here as pairs of codes.
+size_t packed_weight_bytes(const Dims& d, bool gateup, bool fp8 = false);
 hipError_t launch_pack_weights(const Dims& d, bool gateup, const uint16_t* w0, const uint16_t* w1,
-                               uint16_t* out, hipStream_t s);
+                               uint16_t* out, hipStream_t s, bool fp8 = false);
 
 // Block-scaled FP8 weights of one matrix stack [E, rows, cols]: E4M3 codes
 // [E, rows, cols] and scale bytes [E, rows/32, cols/32, 32].
@@ -97,18 +100,22 @@ struct Fp8Weight {
   const uint8_t* codes;
   const uint8_t* scales;
 };
+// packed: wg.codes (gate/up) or wd.codes (down) is a packed FP8 stack (its
+// D, resp. F, a multiple of 128; wu.codes unused); the scales stay in place.
 hipError_t launch_expert_gateup_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                     const Fp8Weight& wg, const Fp8Weight& wu, uint16_t* h,
-                                    hipStream_t s);
+                                    hipStream_t s, bool packed = false);
 hipError_t launch_expert_gateup_fp8_gathered(const Dims& d, const uint16_t* x,
                                              const int32_t* row_token, const int32_t* offsets,
                                              const Fp8Weight& wg, const Fp8Weight& wu,
-                                             uint16_t* h, hipStream_t s);
+                                             uint16_t* h, hipStream_t s, bool packed = false);
 hipError_t launch_expert_down_fp8(const Dims& d, const uint16_t* h, const int32_t* offsets,
-                                  const Fp8Weight& wd, uint16_t* out_perm, hipStream_t s);
+                                  const Fp8Weight& wd, uint16_t* out_perm, hipStream_t s,
+                                  bool packed = false);
 hipError_t launch_grouped_ffn_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                   const Fp8Weight& wg, const Fp8Weight& wu, const Fp8Weight& wd,
-                                  uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s);
+                                  uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s,
+                                  bool packed = false);
 
 // GELU-expert layer: up GEMM with bias + GELU epilogue, down GEMM with bias,
 // and the router's compression GEMM (one group of N rows).

@@ -943,6 +943,11 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
   // PWA + PWB) B rows and, for FP8, the last one (lanes < LS only) scales.
   const void* base[PW];
   uint32_t off[PW], ldso[PW];
+  // packed FP8 codes read by 64-deep stages: two stages per 128-deep stage
+  // image; dlt = where a lane's piece of an odd stage sits relative to that
+  // of the even stage before it
+  const bool pk64 = FP8 && BK == 64 && p.wpack;
+  uint32_t dlt[PWB];
 #pragma unroll
   for (int j = 0; j < PWA; ++j) {
     const int q = wave * PWA + j;
@@ -963,10 +968,27 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
     const char* b = static_cast<const char*>(up ? p.B1 : p.B0);
     if constexpr (!FP8) {
       static_assert(R::B_U4 * 16 == kPackStage && R::RPIB * R::CHB == 64, "packed stage image");
+    } else {
+      static_assert(BN == 256 && (BK == 64 || BK == 128), "packed FP8 stage image");
     }
+    dlt[jb] = 0;
     if (!FP8 && p.wpack) {
       base[PWA + jb] = static_cast<const char*>(p.B0) + packed_panel(p, t.e, t.nt, nk);
       off[PWA + jb] = q * 1024 + lane * 16;
+    } else if (FP8 && p.wpack) {
+      // stage images of 256 rows x 128 codes: row r at byte 128 r, its
+      // 16-byte chunk c at position c ^ ((r / 2) % 8)
+      base[PWA + jb] = static_cast<const char*>(p.B0) + packed_panel(p, t.e, t.nt, p.Kd / 128);
+      if (BK == 128) {
+        off[PWA + jb] = q * 1024 + lane * 16;
+      } else {
+        // LDS chunk lcb of this 64-code row holds chunk g of the row's 64
+        // codes of the stage: chunk g (even stage) or 4 + g (odd stage) of
+        // the image row
+        const int g = lcb ^ swz_rows<R::BRB>(trow), sw = (trow >> 1) & 7;
+        off[PWA + jb] = (uint32_t)(trow * 128 + ((g ^ sw) << 4));
+        dlt[jb] = (uint32_t)(trow * 128 + (((4 + g) ^ sw) << 4)) - off[PWA + jb];
+      }
     } else if (FP8) {
       base[PWA + jb] = b + (size_t)t.e * wmat;
       off[PWA + jb] = (uint32_t)wrow * p.Kd + (uint32_t)(lcb ^ swz_rows<R::BRB>(trow)) * 16;
@@ -995,17 +1017,24 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
   // declared, so no generic-pointer conversion is needed here)
   // per-stage advance of a weight DMA source (a packed stage image, or BRB
   // bytes of a row)
-  const uint32_t badv = !FP8 && p.wpack ? kPackStage : R::BRB;
+  const uint32_t badv = p.wpack ? kPackStage : R::BRB;
+  // source offset of DMA instruction j for stage kt
+  auto src_off = [&](int j, int kt) -> uint32_t {
+    if (j < PWA) return off[j] + (uint32_t)kt * (BK * 2);
+    if (j >= PWA + PWB) return off[j] + (uint32_t)kt * (R::KB * 32);
+    if (pk64)
+      return off[j] + (uint32_t)(kt >> 1) * kPackStage + ((kt & 1) ? dlt[j - PWA] : 0u);
+    return off[j] + (uint32_t)kt * badv;
+  };
   auto dma = [&](int s, int kt) {
     const uint32_t l0 = lds_addr + (uint32_t)s * (R::STAGE_U4 * 16);
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
-      const uint32_t adv = j < PWA ? BK * 2 : j < PWA + PWB ? badv : R::KB * 32;
       const uint32_t la = __builtin_amdgcn_readfirstlane(l0 + ldso[j]);
       if (FP8 && j == PW - 1) {
-        if (lane < R::LS) lds_dma16<UNIFORM>(la, base[j], off[j] + (uint32_t)kt * adv);
+        if (lane < R::LS) lds_dma16<UNIFORM>(la, base[j], src_off(j, kt));
       } else {
-        lds_dma16<UNIFORM>(la, base[j], off[j] + (uint32_t)kt * adv);
+        lds_dma16<UNIFORM>(la, base[j], src_off(j, kt));
       }
     }
   };
@@ -1025,12 +1054,11 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& p, const Tile& t,
 #pragma unroll
       for (int i = 0; i < PW; ++i) {
         if (i != j) continue;
-        const uint32_t adv = i < PWA ? BK * 2 : i < PWA + PWB ? badv : R::KB * 32;
         const uint32_t la = __builtin_amdgcn_readfirstlane(l0 + ldso[i]);
         if (FP8 && i == PW - 1) {
-          if (lane < R::LS) lds_dma16<UNIFORM>(la, base[i], off[i] + (uint32_t)kt * adv);
+          if (lane < R::LS) lds_dma16<UNIFORM>(la, base[i], src_off(i, kt));
         } else {
-          lds_dma16<UNIFORM>(la, base[i], off[i] + (uint32_t)kt * adv);
+          lds_dma16<UNIFORM>(la, base[i], src_off(i, kt));
         }
       }
     };
@@ -1823,7 +1851,8 @@ hipError_t launch_gemm(const Dims& d, const GemmArgs& a, hipStream_t s, Shape sh
       // the weight stream rules: a deep LDS-DMA ring (over 100 KB in flight
       // per CU) when k is long enough to fill it, else register staging
       if constexpr (FP8) {
-        if (a.Kd >= 512 && a.Kd % 128 == 0)
+        // (packed FP8 stacks are read by 128- or 64-deep stages only)
+        if ((a.Kd >= 512 || a.wpack) && a.Kd % 128 == 0)
           return launch_ring<32, 256, 1, 4, 128, 3, EPI, FP8>(d, a, s);
       }
       if (a.Kd >= 1024) return launch_ring<32, 256, 1, 4, 64, FP8 ? 6 : 4, EPI, FP8>(d, a, s);
@@ -1860,8 +1889,9 @@ hipError_t launch_expert_gateup(const Dims& d, const uint16_t* x_perm, const int
 // The LDS-DMA ring and split-ring tiles can read A rows through row_token;
 // the register-staged 32-row tiles (few rows per expert, short k) cannot.
 // With FP8 weights the 32-row ring also serves k >= 512 in steps of 128.
-bool gateup_gather_supported(const Dims& d, bool fp8) {
-  return pick(d) != Shape::Small || d.D >= 1024 || (fp8 && d.D >= 512 && d.D % 128 == 0);
+bool gateup_gather_supported(const Dims& d, bool fp8, bool packed) {
+  return pick(d) != Shape::Small || d.D >= 1024 ||
+         (fp8 && (d.D >= 512 || packed) && d.D % 128 == 0);
 }
 
 hipError_t launch_expert_gateup_gathered(const Dims& d, const uint16_t* x,
@@ -1924,15 +1954,16 @@ inline int64_t pack_tiles(const Dims& d, bool gateup) {
 }
 }  // namespace
 
-size_t packed_weight_bytes(const Dims& d, bool gateup) {
+size_t packed_weight_bytes(const Dims& d, bool gateup, bool fp8) {
   const int64_t kd = gateup ? d.D : d.F;
-  return (size_t)d.E * pack_tiles(d, gateup) * (kd / 64) * kPackStage;
+  return (size_t)d.E * pack_tiles(d, gateup) * (kd / (fp8 ? 128 : 64)) * kPackStage;
 }
 
 hipError_t launch_pack_weights(const Dims& d, bool gateup, const uint16_t* w0, const uint16_t* w1,
-                               uint16_t* out, hipStream_t s) {
-  const int Nout = gateup ? d.F : d.D, Kd = gateup ? d.D : d.F;
-  const int64_t chunks = (int64_t)(packed_weight_bytes(d, gateup) / 16);
+                               uint16_t* out, hipStream_t s, bool fp8) {
+  // FP8 codes are packed as pairs: a 128-code stage is 64 two-byte units
+  const int Nout = gateup ? d.F : d.D, Kd = (gateup ? d.D : d.F) / (fp8 ? 2 : 1);
+  const int64_t chunks = (int64_t)(packed_weight_bytes(d, gateup, fp8) / 16);
   const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, (int64_t)device_cu_count() * 8);
   if (gateup)
     hipLaunchKernelGGL(pack_weights_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, w0, w1,
@@ -1946,33 +1977,39 @@ hipError_t launch_pack_weights(const Dims& d, bool gateup, const uint16_t* w0, c
 
 hipError_t launch_expert_gateup_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                     const Fp8Weight& wg, const Fp8Weight& wu, uint16_t* h,
-                                    hipStream_t s) {
-  return launch_gemm<kEpiSwiglu, true>(d, GemmArgs{x_perm, wg.codes, wu.codes, h, offsets, d.E, d.D, d.F,
-                                  0, wg.scales, wu.scales}, s);
+                                    hipStream_t s, bool packed) {
+  GemmArgs a{x_perm, wg.codes, wu.codes, h, offsets, d.E, d.D, d.F, 0, wg.scales, wu.scales};
+  a.wpack = packed;
+  return launch_gemm<kEpiSwiglu, true>(d, a, s);
 }
 
 hipError_t launch_expert_gateup_fp8_gathered(const Dims& d, const uint16_t* x,
                                              const int32_t* row_token, const int32_t* offsets,
                                              const Fp8Weight& wg, const Fp8Weight& wu,
-                                             uint16_t* h, hipStream_t s) {
-  if (!gateup_gather_supported(d, true)) return hipErrorNotSupported;
-  return launch_gemm<kEpiSwiglu, true>(d, GemmArgs{x, wg.codes, wu.codes, h, offsets, d.E, d.D,
-                                  d.F, 0, wg.scales, wu.scales, nullptr, row_token}, s);
+                                             uint16_t* h, hipStream_t s, bool packed) {
+  if (!gateup_gather_supported(d, true, packed)) return hipErrorNotSupported;
+  GemmArgs a{x, wg.codes, wu.codes, h, offsets, d.E, d.D, d.F, 0, wg.scales, wu.scales, nullptr,
+             row_token};
+  a.wpack = packed;
+  return launch_gemm<kEpiSwiglu, true>(d, a, s);
 }
 
 hipError_t launch_expert_down_fp8(const Dims& d, const uint16_t* h, const int32_t* offsets,
-                                  const Fp8Weight& wd, uint16_t* out_perm, hipStream_t s) {
-  return launch_gemm<kEpiStore, true>(d, GemmArgs{h, wd.codes, nullptr, out_perm, offsets, d.E, d.F, d.D,
-                                0, wd.scales, nullptr}, s);
+                                  const Fp8Weight& wd, uint16_t* out_perm, hipStream_t s,
+                                  bool packed) {
+  GemmArgs a{h, wd.codes, nullptr, out_perm, offsets, d.E, d.F, d.D, 0, wd.scales, nullptr};
+  a.wpack = packed;
+  return launch_gemm<kEpiStore, true>(d, a, s);
 }
 
 hipError_t launch_grouped_ffn_fp8(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,
                                   const Fp8Weight& wg, const Fp8Weight& wu, const Fp8Weight& wd,
-                                  uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s) {
+                                  uint16_t* out_perm, uint16_t* h, void* ws, hipStream_t s,
+                                  bool packed) {
   if (!h) h = static_cast<uint16_t*>(ws);
-  hipError_t e = launch_expert_gateup_fp8(d, x_perm, offsets, wg, wu, h, s);
+  hipError_t e = launch_expert_gateup_fp8(d, x_perm, offsets, wg, wu, h, s, packed);
   if (e != hipSuccess) return e;
-  return launch_expert_down_fp8(d, h, offsets, wd, out_perm, s);
+  return launch_expert_down_fp8(d, h, offsets, wd, out_perm, s, packed);
 }
 
 hipError_t launch_expert_up_gelu(const Dims& d, const uint16_t* x_perm, const int32_t* offsets,

@@ -117,7 +117,7 @@ inline moe_status hip_status(hipError_t e) {
 // through row_token (kGatherBf16 / kGatherFp8: with bf16 or FP8 weight
 // tiles); where the tiles allow it, the permuted copy of x is then not
 // written and `ffn` gets x and row_token (else x_perm and NULL).
-enum GatherKind { kNoGather, kGatherBf16, kGatherFp8 };
+enum GatherKind { kNoGather, kGatherBf16, kGatherFp8, kGatherFp8Packed };
 
 template <class Route, class Ffn>
 moe_status forward_impl(const moe_problem* p, const uint16_t* x, bool weights_present,
@@ -150,7 +150,8 @@ moe_status forward_impl(const moe_problem* p, const uint16_t* x, bool weights_pr
   if (st != MOE_OK) return st;
   const bool gather = can_gather != kNoGather && !d.padded &&
                       (uint64_t)d.N * d.D * 2 < (1ull << 32) &&
-                      gateup_gather_supported(d, can_gather == kGatherFp8);
+                      gateup_gather_supported(d, can_gather >= kGatherFp8,
+                                              can_gather == kGatherFp8Packed);
   st = hip_status(launch_permute(d, x, topk_ids, expert_counts, expert_offsets, row_token,
                                  slot_row, gather ? nullptr : x_perm, base + L.perm, s));
   if (st != MOE_OK) return st;
@@ -585,13 +586,150 @@ moe_status moe_forward_fp8(const moe_problem* p, const uint16_t* x, const float*
                       });
 }
 
+// The contraction length of an FP8 stack packed by 128-code stages must be a
+// multiple of 128: D for gate/up, F for down.
+inline bool fp8_pack_fits(const Dims& d, bool gateup) {
+  return (gateup ? d.D : d.F) % 128 == 0;
+}
+
 moe_status moe_packed_weight_size(const moe_problem* p, int32_t kind, size_t* bytes) {
   Dims d;
   const moe_status st = check_problem(p, &d);
   if (st != MOE_OK) return st;
-  if (!bytes || (kind != MOE_PACK_GATEUP && kind != MOE_PACK_DOWN)) return MOE_ERR_INVALID_ARG;
-  *bytes = packed_weight_bytes(d, kind == MOE_PACK_GATEUP);
+  if (!bytes || kind < MOE_PACK_GATEUP || kind > MOE_PACK_DOWN_FP8) return MOE_ERR_INVALID_ARG;
+  const bool gateup = kind == MOE_PACK_GATEUP || kind == MOE_PACK_GATEUP_FP8;
+  const bool fp8 = kind == MOE_PACK_GATEUP_FP8 || kind == MOE_PACK_DOWN_FP8;
+  if (fp8 && !fp8_pack_fits(d, gateup)) return MOE_ERR_UNSUPPORTED;
+  *bytes = packed_weight_bytes(d, gateup, fp8);
   return MOE_OK;
+}
+
+moe_status moe_pack_weights_fp8(const moe_problem* p, int32_t kind, const uint8_t* c0,
+                                const uint8_t* c1, uint8_t* packed, void* stream) {
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  const bool gateup = kind == MOE_PACK_GATEUP_FP8;
+  if ((!gateup && kind != MOE_PACK_DOWN_FP8) || !c0 || (gateup && !c1) || !packed)
+    return MOE_ERR_INVALID_ARG;
+  if (!fp8_pack_fits(d, gateup)) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(c0) || (gateup && !aligned16(c1)) || !aligned16(packed))
+    return MOE_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_pack_weights(d, gateup, reinterpret_cast<const uint16_t*>(c0),
+                                        reinterpret_cast<const uint16_t*>(gateup ? c1 : c0),
+                                        reinterpret_cast<uint16_t*>(packed),
+                                        static_cast<hipStream_t>(stream), true));
+}
+
+moe_status moe_expert_gateup_fp8_packed(const moe_problem* p, const uint16_t* x_perm,
+                                        const int32_t* expert_offsets,
+                                        const uint8_t* w_gateup_packed,
+                                        const uint8_t* w_gate_scales, const uint8_t* w_up_scales,
+                                        uint16_t* h, void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !h) return MOE_ERR_INVALID_ARG;
+  if ((st = check_fp8(w_gateup_packed, w_gate_scales)) != MOE_OK) return st;
+  if ((st = check_fp8(w_gateup_packed, w_up_scales)) != MOE_OK) return st;
+  if (!fp8_pack_fits(d, true) || !aligned16(x_perm) || !aligned16(h)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_gateup_fp8(d, x_perm, expert_offsets,
+                                             Fp8Weight{w_gateup_packed, w_gate_scales},
+                                             Fp8Weight{nullptr, w_up_scales}, h,
+                                             static_cast<hipStream_t>(stream), true));
+}
+
+moe_status moe_expert_gateup_fp8_packed_gathered(const moe_problem* p, const uint16_t* x,
+                                                 const int32_t* row_token,
+                                                 const int32_t* expert_offsets,
+                                                 const uint8_t* w_gateup_packed,
+                                                 const uint8_t* w_gate_scales,
+                                                 const uint8_t* w_up_scales, uint16_t* h,
+                                                 void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!x || !row_token || !expert_offsets || !h) return MOE_ERR_INVALID_ARG;
+  if ((st = check_fp8(w_gateup_packed, w_gate_scales)) != MOE_OK) return st;
+  if ((st = check_fp8(w_gateup_packed, w_up_scales)) != MOE_OK) return st;
+  if (!fp8_pack_fits(d, true)) return MOE_ERR_UNSUPPORTED;
+  if (d.padded || (uint64_t)d.N * d.D * 2 >= (1ull << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(h)) return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  if (!gateup_gather_supported(d, true, true)) return MOE_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_gateup_fp8_gathered(
+      d, x, row_token, expert_offsets, Fp8Weight{w_gateup_packed, w_gate_scales},
+      Fp8Weight{nullptr, w_up_scales}, h, static_cast<hipStream_t>(stream), true));
+}
+
+moe_status moe_expert_down_fp8_packed(const moe_problem* p, const uint16_t* h,
+                                      const int32_t* expert_offsets,
+                                      const uint8_t* w_down_packed,
+                                      const uint8_t* w_down_scales, uint16_t* out_perm,
+                                      void* stream) {
+  Dims d;
+  moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (!h || !expert_offsets || !out_perm) return MOE_ERR_INVALID_ARG;
+  if ((st = check_fp8(w_down_packed, w_down_scales)) != MOE_OK) return st;
+  if (!fp8_pack_fits(d, false) || !aligned16(h) || !aligned16(out_perm))
+    return MOE_ERR_UNSUPPORTED;
+  if (d.N == 0) return MOE_OK;
+  (void)hipGetLastError();  // report only this call's launch errors
+  return hip_status(launch_expert_down_fp8(d, h, expert_offsets,
+                                           Fp8Weight{w_down_packed, w_down_scales}, out_perm,
+                                           static_cast<hipStream_t>(stream), true));
+}
+
+moe_status moe_forward_fp8_packed(const moe_problem* p, const uint16_t* x, const float* w_router,
+                                  const float* expert_bias, const uint8_t* w_gateup_packed,
+                                  const uint8_t* w_gate_scales, const uint8_t* w_up_scales,
+                                  const uint8_t* w_down_packed, const uint8_t* w_down_scales,
+                                  uint16_t* y, float* logits, int32_t* topk_ids,
+                                  float* topk_weights, int32_t* expert_counts,
+                                  int32_t* expert_offsets, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  const bool present = w_router && fp8_present(w_gateup_packed, w_gate_scales) &&
+                       fp8_present(w_gateup_packed, w_up_scales) &&
+                       fp8_present(w_down_packed, w_down_scales);
+  const bool aligned = aligned16(w_router) && fp8_aligned(w_gateup_packed, w_gate_scales) &&
+                       fp8_aligned(w_gateup_packed, w_up_scales) &&
+                       fp8_aligned(w_down_packed, w_down_scales);
+  Dims d;
+  const moe_status st = check_problem(p, &d);
+  if (st != MOE_OK) return st;
+  if (present && x && y && (!fp8_pack_fits(d, true) || !fp8_pack_fits(d, false)))
+    return MOE_ERR_UNSUPPORTED;
+  const Fp8Weight wg{w_gateup_packed, w_gate_scales}, wu{nullptr, w_up_scales},
+      wd{w_down_packed, w_down_scales};
+  return forward_impl(p, x, present, aligned, y, logits, topk_ids, topk_weights, expert_counts,
+                      expert_offsets, ws, ws_bytes, stream, kGatherFp8Packed,
+                      [&](const Dims& dd, float* lg, int32_t* ids, float* w, char* base,
+                          const ForwardWs& L, hipStream_t s) {
+                        float* parts = router_ws_bytes(dd) > 0
+                                           ? reinterpret_cast<float*>(base + L.rpart)
+                                           : nullptr;
+                        const hipError_t e = launch_router_gemm(dd, x, w_router, lg, parts, s);
+                        return e != hipSuccess ? e
+                                               : launch_topk(dd, lg, expert_bias, ids, w, parts, s);
+                      },
+                      [&](const Dims& dd, const uint16_t* xp, const int32_t* rt,
+                          const int32_t* offs, uint16_t* op, void* fws, hipStream_t s) {
+                        if (rt) {
+                          uint16_t* h = static_cast<uint16_t*>(fws);
+                          const hipError_t e = launch_expert_gateup_fp8_gathered(
+                              dd, xp, rt, offs, wg, wu, h, s, true);
+                          return e != hipSuccess
+                                     ? e
+                                     : launch_expert_down_fp8(dd, h, offs, wd, op, s, true);
+                        }
+                        return launch_grouped_ffn_fp8(dd, xp, offs, wg, wu, wd, op, nullptr, fws,
+                                                      s, true);
+                      });
 }
 
 moe_status moe_pack_weights(const moe_problem* p, int32_t kind, const uint16_t* w0,

@@ -226,11 +226,12 @@ def test_packed_weight_argument_checks():
         assert L.moe_packed_weight_size(bp, 1, ctypes.byref(n)) == OK
         assert n.value == 8 * math.ceil(D / 256) * (F // 64) * 32768
     bp = ctypes.byref(P())
-    assert L.moe_packed_weight_size(bp, 2, ctypes.byref(n)) == INVALID
+    assert L.moe_packed_weight_size(bp, 4, ctypes.byref(n)) == INVALID     # no such kind
+    assert L.moe_packed_weight_size(bp, -1, ctypes.byref(n)) == INVALID
     assert L.moe_packed_weight_size(bp, 0, None) == INVALID
     assert L.moe_packed_weight_size(ctypes.byref(P(D=100)), 0, ctypes.byref(n)) == UNSUPPORTED
     pk = L.moe_pack_weights
-    assert pk(bp, 2, FAKE, FAKE, FAKE, None) == INVALID          # no such kind
+    assert pk(bp, 2, FAKE, FAKE, FAKE, None) == INVALID          # FP8 kinds: moe_pack_weights_fp8
     assert pk(bp, 0, FAKE, None, FAKE, None) == INVALID          # gate/up needs both stacks
     assert pk(bp, 1, None, None, FAKE, None) == INVALID
     assert pk(bp, 1, FAKE, None, None, None) == INVALID
@@ -261,6 +262,57 @@ def test_packed_weight_argument_checks():
     assert fw(*bad, FAKE, need, None) == UNSUPPORTED
     assert fw(*args, FAKE, need - 1, None) == WORKSPACE
     assert fw(ctypes.byref(P(N=0)), *args[1:], None, 0, None) == OK
+
+
+def test_packed_fp8_argument_checks():
+    L = moe.lib
+    n = ctypes.c_size_t()
+    by = ctypes.byref
+    # sizes: E * ceil(F / 128) * (D / 128) * 32 KB (gate/up), E * ceil(D / 256) * (F / 128) * 32 KB
+    for D, F in ((256, 512), (384, 640), (7168, 2048)):
+        bp = by(P(D=D, F=F))
+        assert L.moe_packed_weight_size(bp, 2, by(n)) == OK
+        assert n.value == 8 * math.ceil(F / 128) * (D // 128) * 32768
+        assert L.moe_packed_weight_size(bp, 3, by(n)) == OK
+        assert n.value == 8 * math.ceil(D / 256) * (F // 128) * 32768
+    # the contraction length (D for gate/up, F for down) must be a multiple of 128
+    odd = by(P(D=320, F=192))
+    assert L.moe_packed_weight_size(odd, 2, by(n)) == UNSUPPORTED
+    assert L.moe_packed_weight_size(odd, 3, by(n)) == UNSUPPORTED
+    assert L.moe_packed_weight_size(by(P(D=320, F=256)), 3, by(n)) == OK
+    bp = by(P())
+    pk = L.moe_pack_weights_fp8
+    assert pk(bp, 0, FAKE, FAKE, FAKE, None) == INVALID          # a bf16 kind
+    assert pk(bp, 2, FAKE, None, FAKE, None) == INVALID          # gate/up needs both stacks
+    assert pk(bp, 3, None, None, FAKE, None) == INVALID
+    assert pk(bp, 3, FAKE, None, None, None) == INVALID
+    assert pk(odd, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert pk(bp, 2, FAKE, FAKE + 2, FAKE, None) == UNSUPPORTED
+    g = L.moe_expert_gateup_fp8_packed       # p, x_perm, offsets, packed, gate scales, up scales, h
+    assert g(bp, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == INVALID
+    assert g(bp, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == INVALID
+    assert g(odd, *([FAKE] * 6), None) == UNSUPPORTED
+    assert g(bp, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert g(by(P(N=0)), *([FAKE] * 6), None) == OK
+    gg = L.moe_expert_gateup_fp8_packed_gathered   # p, x, row_token, offsets, packed, gs, us, h
+    assert gg(bp, FAKE, None, *([FAKE] * 5), None) == INVALID
+    assert gg(by(P(cn=5, cd=4)), *([FAKE] * 7), None) == UNSUPPORTED    # padded layout
+    assert gg(odd, *([FAKE] * 7), None) == UNSUPPORTED
+    assert gg(by(P(N=0)), *([FAKE] * 7), None) == OK
+    d = L.moe_expert_down_fp8_packed         # p, h, offsets, packed, down scales, out_perm
+    assert d(bp, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
+    assert d(by(P(F=192)), *([FAKE] * 5), None) == UNSUPPORTED
+    assert d(by(P(N=0)), *([FAKE] * 5), None) == OK
+    fw = L.moe_forward_fp8_packed
+    need = moe.workspace_size(P())
+    args = [bp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE] + [None] * 5
+    bad = list(args)
+    bad[8] = None                                                 # down scales missing
+    assert fw(*bad, FAKE, need, None) == INVALID
+    p320 = P(D=320)
+    assert fw(by(p320), *args[1:], FAKE, moe.workspace_size(p320), None) == UNSUPPORTED
+    assert fw(*args, FAKE, need - 1, None) == WORKSPACE
+    assert fw(by(P(N=0)), *args[1:], None, 0, None) == OK
 
 
 def test_gelu_layer_argument_checks():

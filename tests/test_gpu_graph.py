@@ -98,11 +98,13 @@ def _pack(p, kind, w0, w1=None):
     return buf
 
 
-@pytest.mark.parametrize("kind", ["fp8", "fused", "gelu", "packed", "packed_decode"])
+@pytest.mark.parametrize("kind", ["fp8", "fused", "gelu", "packed", "packed_decode",
+                                  "fp8_packed_decode"])
 def test_forward_variants_graph_replays_match_eager(kind):
     """moe_forward_fp8 (split-ring-sized rows), moe_forward_fused,
-    moe_forward_gelu and moe_forward_packed (split-ring and decode-sized rows)
-    captured once and replayed with eager calls between."""
+    moe_forward_gelu, moe_forward_packed (split-ring and decode-sized rows)
+    and moe_forward_fp8_packed (decode-sized rows) captured once and replayed
+    with eager calls between."""
     if kind == "gelu":
         from gpu_layer import GeluLayer
         L = GeluLayer(ms.CONFIGS["gelu_tiny"])
@@ -111,6 +113,20 @@ def test_forward_variants_graph_replays_match_eager(kind):
         def call(out):
             moe.forward_gelu(L.p, i["x"], i["w_proj"], i["b_proj"], i["w_out"], i["b_out"],
                              i["w1"], i["b1"], i["w2"], i["b2"], out, L.ws)
+        N, D = L.cfg.N, L.cfg.D
+    elif kind == "fp8_packed_decode":
+        L = Layer(ms.CONFIGS["qwen3_decode"])
+        q = [_quantize(w) for w in (L.w_gate, L.w_up, L.w_down)]
+        gu8 = torch.empty(moe.packed_weight_size(L.p, moe.PACK_GATEUP_FP8), dtype=torch.uint8,
+                          device=DEV)
+        moe.pack_weights_fp8(L.p, moe.PACK_GATEUP_FP8, q[0][0], q[1][0], gu8)
+        dn8 = torch.empty(moe.packed_weight_size(L.p, moe.PACK_DOWN_FP8), dtype=torch.uint8,
+                          device=DEV)
+        moe.pack_weights_fp8(L.p, moe.PACK_DOWN_FP8, q[2][0], None, dn8)
+
+        def call(out):
+            moe.forward_fp8_packed(L.p, L.x, L.w_router, L.bias, gu8, q[0][1], q[1][1], dn8,
+                                   q[2][1], out, L.ws)
         N, D = L.cfg.N, L.cfg.D
     elif kind.startswith("packed"):
         L = Layer(ms.CONFIGS["qwen3_decode"] if kind == "packed_decode" else SMALL["large_tiles"])

@@ -94,7 +94,9 @@ def test_forward_independent_of_workspace_contents(name, padded):
             assert np.array_equal(got, ref), f"moe_forward_packed run {i} differs"
 
 
-@pytest.mark.parametrize("name,padded", [("large_tiles", False), ("padded", True)])
+@pytest.mark.parametrize("name,padded", [("large_tiles", False), ("padded", True),
+                                         ("two_big_experts", False),
+                                         ("padded_small_rows", True)])
 def test_fp8_forward_independent_of_workspace_contents(name, padded):
     L = Layer(SMALL[name], padded=padded)
     q = [_quantize(w) for w in (L.w_gate, L.w_up, L.w_down)]
@@ -110,6 +112,20 @@ def test_fp8_forward_independent_of_workspace_contents(name, padded):
     runs = _runs(fwd8, L.ws, fwd)
     for i, got in enumerate(runs[1:], 1):
         assert np.array_equal(got, runs[0]), f"moe_forward_fp8 run {i} differs from run 0"
+    if L.cfg.D % 128 == 0 and L.cfg.F % 128 == 0:
+        gu8 = torch.empty(moe.packed_weight_size(L.p, moe.PACK_GATEUP_FP8), dtype=torch.uint8,
+                          device=DEV)
+        moe.pack_weights_fp8(L.p, moe.PACK_GATEUP_FP8, q[0][0], q[1][0], gu8)
+        dn8 = torch.empty(moe.packed_weight_size(L.p, moe.PACK_DOWN_FP8), dtype=torch.uint8,
+                          device=DEV)
+        moe.pack_weights_fp8(L.p, moe.PACK_DOWN_FP8, q[2][0], None, dn8)
+
+        def fwd8p():
+            moe.forward_fp8_packed(L.p, L.x, L.w_router, L.bias, gu8, q[0][1], q[1][1], dn8,
+                                   q[2][1], y, L.ws)
+            return y
+        for i, got in enumerate(_runs(fwd8p, L.ws, fwd)):
+            assert np.array_equal(got, runs[0]), f"moe_forward_fp8_packed run {i} differs"
 
 
 @pytest.mark.parametrize("padded", [False, True])
